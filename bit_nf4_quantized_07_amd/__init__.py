@@ -1,0 +1,270 @@
+"""Python binding of libqlora.so, the gfx950 QLoRA NF4 linear-layer library.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in include/qlora.h.  PyTorch supplies device memory
+and the current stream.  There is no CPU fallback: if the library is missing
+or no GPU is visible, the compute calls raise.
+
+    qw = quantize(W_fp32_cuda)                       # NF4 + double quant
+    Y, T = linear_fwd(X, qw, A, B, alpha)            # bf16 tensors on cuda
+    dX, dA, dB = linear_bwd(dY, X, qw, A, B, alpha, T)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+BWD_ACCUMULATE_DX = 1
+BLOCKSIZE = 64
+DQ_BLOCKSIZE = 256
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+# name -> (restype, argtypes), mirroring include/qlora.h
+SIGNATURES = {
+    "nf4_quantize": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "double_quant": (_I, [_P, _I64, _I, _P, _P, _P, _P]),
+    "nf4_dequant": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P]),
+    "qlora_linear_fwd": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F, _P, _P,
+                              _P, ctypes.c_size_t, _P]),
+    "qlora_linear_bwd": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F, _P,
+                              _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
+    "qlora_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I, _I]),
+    "silu_mul_fwd": (_I, [_P, _P, _I64, _P, _P]),
+    "silu_mul_bwd": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
+    "nf4_codebook": (_I, [_P]),
+    "dq_codebook": (_I, [_P, ctypes.POINTER(_I)]),
+    "qlora_strerror": (ctypes.c_char_p, [_I]),
+    "qlora_version": (_I, []),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libqlora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m bit_nf4_quantized_07_amd.build`")
+    try:  # make sure torch's HIP runtime is the one in the process
+        import torch  # noqa: F401
+    except Exception:
+        pass
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+class QLoRAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load_library().qlora_strerror(status).decode()
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise QLoRAError(fn, status)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+
+
+class QuantizedWeight(NamedTuple):
+    """NF4 base weight [N, K] with double-quantised block constants."""
+    packed: "object"   # uint8 [N*K/2]
+    codes: "object"    # uint8 [N*K/64]
+    scales: "object"   # fp32  [ceil(N*K/64/256)]
+    mean: "object"     # fp32  [1]
+    N: int
+    K: int
+
+    def nbytes(self) -> int:
+        return (self.packed.numel() + self.codes.numel() + 4 * self.scales.numel()
+                + 4 * self.mean.numel())
+
+
+def nf4_quantize(W):
+    """W fp32 [N, K] (cuda) -> (packed uint8 [N*K/2], absmax fp32 [N*K/64])."""
+    torch = _torch()
+    _need_cuda(W)
+    N, K = W.shape
+    packed = torch.empty(N * K // 2, dtype=torch.uint8, device=W.device)
+    absmax = torch.empty(max(N * K // BLOCKSIZE, 1), dtype=torch.float32, device=W.device)
+    _check("nf4_quantize", load_library().nf4_quantize(
+        _ptr(W), N, K, BLOCKSIZE, _ptr(packed), _ptr(absmax), _stream(W.device)))
+    return packed, absmax
+
+
+def double_quant(absmax):
+    """absmax fp32 [nb] -> (codes uint8 [nb], scales fp32 [ceil(nb/256)], mean fp32 [1])."""
+    torch = _torch()
+    _need_cuda(absmax)
+    nb = absmax.numel()
+    codes = torch.empty(nb, dtype=torch.uint8, device=absmax.device)
+    scales = torch.empty((nb + DQ_BLOCKSIZE - 1) // DQ_BLOCKSIZE, dtype=torch.float32,
+                         device=absmax.device)
+    mean = torch.empty(4, dtype=torch.float32, device=absmax.device)[:1]
+    _check("double_quant", load_library().double_quant(
+        _ptr(absmax), nb, DQ_BLOCKSIZE, _ptr(codes), _ptr(scales), _ptr(mean),
+        _stream(absmax.device)))
+    return codes, scales, mean
+
+
+def quantize(W) -> QuantizedWeight:
+    """NF4 quantisation followed by double quantisation of the constants."""
+    packed, absmax = nf4_quantize(W)
+    codes, scales, mean = double_quant(absmax)
+    return QuantizedWeight(packed, codes, scales, mean, W.shape[0], W.shape[1])
+
+
+def nf4_dequant(qw: QuantizedWeight):
+    """-> bf16 [N, K] dequantised weight."""
+    torch = _torch()
+    out = torch.empty(qw.N, qw.K, dtype=torch.bfloat16, device=qw.packed.device)
+    _check("nf4_dequant", load_library().nf4_dequant(
+        _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean), qw.N, qw.K,
+        BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out), _stream(out.device)))
+    return out
+
+
+def workspace_bytes(M: int, K: int, N: int, r: int, backward: bool) -> int:
+    return int(load_library().qlora_workspace_bytes(M, K, N, r, 1 if backward else 0))
+
+
+class Workspace:
+    """A reusable device workspace that grows on demand."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf, self.buf.numel()
+
+
+_default_ws = {}
+
+
+def _ws(device, nbytes):
+    key = str(device)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key].get(nbytes)
+
+
+def linear_fwd(X, qw: QuantizedWeight, A, B, alpha: float, save_T: bool = True,
+               out=None, T_out=None, workspace=None):
+    """Y = X W_hat^T + (alpha/r) (X A^T) B^T.  Returns (Y, T or None)."""
+    torch = _torch()
+    M, K = X.shape
+    r = A.shape[0]
+    _need_cuda(X, A, B)
+    Y = out if out is not None else torch.empty(M, qw.N, dtype=torch.bfloat16, device=X.device)
+    T = T_out if T_out is not None else (
+        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if save_T else None)
+    nb = workspace_bytes(M, K, qw.N, r, False)
+    ws, wsb = (workspace.get(nb) if workspace is not None else _ws(X.device, nb))
+    _check("qlora_linear_fwd", load_library().qlora_linear_fwd(
+        _ptr(X), M, K, qw.N, _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean),
+        _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(T), _ptr(ws), wsb, _stream(X.device)))
+    return Y, T
+
+
+def linear_bwd(dY, X, qw: QuantizedWeight, A, B, alpha: float, T=None, need_dX: bool = True,
+               accumulate_into=None, dA_out=None, dB_out=None, workspace=None):
+    """Returns (dX bf16 [M,K] or None, dA fp32 [r,K], dB fp32 [N,r])."""
+    torch = _torch()
+    M, K = X.shape
+    r = A.shape[0]
+    _need_cuda(dY, X, A, B, T)
+    flags = 0
+    if accumulate_into is not None:
+        dX = accumulate_into
+        flags |= BWD_ACCUMULATE_DX
+    else:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device) if need_dX else None
+    dA = dA_out if dA_out is not None else torch.empty(r, K, dtype=torch.float32, device=X.device)
+    dB = dB_out if dB_out is not None else torch.empty(qw.N, r, dtype=torch.float32,
+                                                       device=X.device)
+    nb = workspace_bytes(M, K, qw.N, r, True)
+    ws, wsb = (workspace.get(nb) if workspace is not None else _ws(X.device, nb))
+    _check("qlora_linear_bwd", load_library().qlora_linear_bwd(
+        _ptr(dY), _ptr(X), M, K, qw.N, _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales),
+        _ptr(qw.mean), _ptr(A), _ptr(B), r, float(alpha), _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB),
+        flags, _ptr(ws), wsb, _stream(X.device)))
+    return dX, dA, dB
+
+
+def silu_mul_fwd(G, Up, out=None):
+    torch = _torch()
+    _need_cuda(G, Up)
+    H = out if out is not None else torch.empty_like(G)
+    _check("silu_mul_fwd", load_library().silu_mul_fwd(
+        _ptr(G), _ptr(Up), G.numel(), _ptr(H), _stream(G.device)))
+    return H
+
+
+def silu_mul_bwd(dH, G, Up):
+    torch = _torch()
+    _need_cuda(dH, G, Up)
+    dG, dU = torch.empty_like(G), torch.empty_like(Up)
+    _check("silu_mul_bwd", load_library().silu_mul_bwd(
+        _ptr(dH), _ptr(G), _ptr(Up), G.numel(), _ptr(dG), _ptr(dU), _stream(G.device)))
+    return dG, dU
+
+
+def codebook():
+    """The 16 NF4 levels the kernels embed (host copy)."""
+    buf = (ctypes.c_float * 16)()
+    _check("nf4_codebook", load_library().nf4_codebook(ctypes.cast(buf, _P)))
+    return list(buf)
+
+
+def dq_levels():
+    buf = (ctypes.c_float * 256)()
+    n = _I(0)
+    _check("dq_codebook", load_library().dq_codebook(ctypes.cast(buf, _P), ctypes.byref(n)))
+    return list(buf)[: n.value]

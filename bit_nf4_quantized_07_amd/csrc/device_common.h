@@ -1,0 +1,111 @@
+// Device-side helpers shared by the gfx950 kernels of the QLoRA NF4 library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+namespace qlk {
+
+// The 16 NF4 levels as fp32 bit patterns, ascending.  They are the standard
+// normal quantiles that give every bin the same probability mass (8 on the
+// positive side, 7 on the negative side, plus an exact zero), divided by the
+// outermost quantile so that the range is exactly [-1, 1]; the outermost
+// probability is 1 - (1/30 + 1/32)/2.  (auryth.ai "QLoRA", NF4 box;
+// llm-compass "QLoRA", 方法与公式 item 1.)  Each value was evaluated in high
+// precision and rounded once to fp32.
+constexpr uint32_t kNF4Bits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu,
+    0xbe91a24bu, 0xbe3d353du, 0xbdba7869u, 0x00000000u,
+    0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+constexpr int kBlock = 64;      // weights per absmax constant
+constexpr int kDQBlock = 256;   // constants per second-level scale
+constexpr int kZeroCode4 = 7;   // index of the exact zero level
+constexpr int kZeroCode8 = 127;
+
+__device__ __forceinline__ float nf4_level(int i) { return __uint_as_float(kNF4Bits[i]); }
+
+// 8-bit level i of the symmetric linear code: the correctly rounded fp32
+// quotient (i - 127) / 127.
+__device__ __forceinline__ float dq_level(int i) {
+  return (float)(i - 127) / 127.0f;
+}
+
+// Decision threshold between NF4 levels i and i+1: their exact midpoint
+// (exact in fp64) rounded toward -inf, so that for any fp32 n
+// "n > threshold" <=> "n is strictly above the midpoint".  Ties (n equal to
+// a representable midpoint) therefore go to the lower index.
+__device__ __forceinline__ float nf4_threshold(int i) {
+  double m = ((double)nf4_level(i) + (double)nf4_level(i + 1)) * 0.5;
+  return __double2float_rd(m);
+}
+__device__ __forceinline__ float dq_threshold(int i) {
+  double m = ((double)dq_level(i) + (double)dq_level(i + 1)) * 0.5;
+  return __double2float_rd(m);
+}
+
+// a_hat = fp32(fp32(Q8[code] * scale) + mean): two separately rounded ops.
+__device__ __forceinline__ float absmax_decode(int code, float scale, float mean) {
+#pragma clang fp contract(off)
+  float q = dq_level(code);
+  float p = q * scale;
+  return p + mean;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round two fp32 values to bf16 (round-to-nearest-even, hardware convert) and
+// pack them, `lo` in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Select two 16-bit halves: result = (lo half of x, lo half of y) or the
+// high halves, via the byte permute unit.
+__device__ __forceinline__ uint32_t lo16x2(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi16x2(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
+// Transpose an 8x8 tile of 16-bit values held as 8 rows of 4 packed words:
+// in[i].w[j] = (e[i][2j], e[i][2j+1]);  out[j].w[k] = (e[2k][j], e[2k+1][j]).
+__device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&out)[8]) {
+  const uint32_t* r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = reinterpret_cast<const uint32_t*>(&in[i]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t x = r[2 * k][j >> 1], y = r[2 * k + 1][j >> 1];
+      w[k] = (j & 1) ? hi16x2(x, y) : lo16x2(x, y);
+    }
+    out[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace qlk

@@ -1,0 +1,51 @@
+// Internal launcher declarations (host side) of the QLoRA NF4 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlk {
+
+hipError_t launch_nf4_quantize(const float* W, int64_t numel, uint8_t* packed, float* absmax,
+                               hipStream_t st);
+hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, float* scales,
+                               float* mean, hipStream_t st);
+hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                              const float* mean, int64_t numel, uint16_t* out, hipStream_t st);
+
+// Quantised base weight, as stored.
+struct NF4Weight {
+  const uint8_t* packed;
+  const uint8_t* codes;
+  const float* scales;
+  const float* mean;
+  int64_t N, K;
+};
+
+// Workspace layout shared by the planner (qlora_workspace_bytes) and the
+// launchers, so that both always agree.
+struct FwdPlan {
+  bool gemv;          // small-M path
+  int t_splits;       // contraction splits for T = X A^T
+  size_t off_T, off_part, bytes;
+};
+struct BwdPlan {
+  int u_splits, t_splits, m_splits_a, m_splits_b;
+  size_t off_U, off_T, off_part, bytes;
+};
+FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r);
+BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r);
+
+hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
+                            const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
+                            void* ws, const FwdPlan& plan, hipStream_t st);
+hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
+                            const uint16_t* A, const uint16_t* B, int r, float s,
+                            const uint16_t* T, uint16_t* dX, float* dA, float* dB,
+                            bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st);
+
+hipError_t launch_silu_mul_fwd(const uint16_t* G, const uint16_t* U, int64_t n, uint16_t* H,
+                               hipStream_t st);
+hipError_t launch_silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* U,
+                               int64_t n, uint16_t* dG, uint16_t* dU, hipStream_t st);
+
+}  // namespace qlk

@@ -1,0 +1,178 @@
+// Bit-exact storage kernels: NF4 blockwise quantisation, double quantisation
+// of the block constants, and dequantisation to bf16.
+//
+// Format (aigrafen.se "QLoRA", list "Tre tekniska bitar" items 1-2;
+// llm-compass "QLoRA", 方法与公式 items 1-2): 4-bit NormalFloat codes in
+// blocks of 64 consecutive weights with one absmax constant each; the
+// constants are quantised again to 8 bits around their mean with one fp32
+// scale per 256 constants.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qlk {
+
+// ---------------------------------------------------------------------------
+// nf4_quantize: 8 lanes per block of 64, each lane 8 consecutive weights.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_nf4_quantize(const float* __restrict__ W, int64_t nblocks,
+               uint8_t* __restrict__ packed, float* __restrict__ absmax) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = gid >> 3;
+  const int sub = (int)(gid & 7);
+  // Whole groups of 8 lanes are in or out together (nblocks*8 threads).
+  if (blk >= nblocks) return;
+
+  float thr[15];
+#pragma unroll
+  for (int i = 0; i < 15; ++i) thr[i] = nf4_threshold(i);
+
+  const float4* src = reinterpret_cast<const float4*>(W + blk * kBlock + sub * 8);
+  const float4 a = src[0], b = src[1];
+  float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(w[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 8));
+  m = fmaxf(m, __shfl_xor(m, 2, 8));
+  m = fmaxf(m, __shfl_xor(m, 4, 8));
+
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // IEEE division (correctly rounded); an all-zero block maps to level 7.
+    const float n = (m > 0.0f) ? w[i] / m : 0.0f;
+    uint32_t c = 0;
+#pragma unroll
+    for (int t = 0; t < 15; ++t) c += (n > thr[t]) ? 1u : 0u;
+    // element 2j -> high nibble of byte j; bytes little-endian in the word
+    const int byte = i >> 1;
+    const int shift = byte * 8 + ((i & 1) ? 0 : 4);
+    word |= c << shift;
+  }
+  reinterpret_cast<uint32_t*>(packed + blk * (kBlock / 2))[sub] = word;
+  if (sub == 0) absmax[blk] = m;
+}
+
+// ---------------------------------------------------------------------------
+// double_quant, step 1: the per-tensor mean in a fixed summation order.
+// One workgroup of 1024 lanes.  Lane t sums constant-group (base + t)
+// sequentially in fp64; lane 0 then adds the group sums sequentially.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024)
+k_dq_mean(const float* __restrict__ absmax, int64_t nb, float* __restrict__ mean) {
+  __shared__ double part[1024];
+  const int64_t ngroups = (nb + kDQBlock - 1) / kDQBlock;
+  double total = 0.0;
+  for (int64_t base = 0; base < ngroups; base += 1024) {
+    const int64_t g = base + threadIdx.x;
+    if (g < ngroups) {
+      const int64_t lo = g * kDQBlock;
+      const int64_t hi = (lo + kDQBlock < nb) ? lo + kDQBlock : nb;
+      double s = 0.0;
+      for (int64_t i = lo; i < hi; ++i) s += (double)absmax[i];
+      part[threadIdx.x] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int64_t lim = (ngroups - base < 1024) ? ngroups - base : 1024;
+      for (int64_t j = 0; j < lim; ++j) total += part[j];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mean[0] = (float)(total / (double)nb);
+}
+
+// ---------------------------------------------------------------------------
+// double_quant, step 2: one workgroup per group of 256 constants.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_dq_codes(const float* __restrict__ absmax, int64_t nb, const float* __restrict__ mean,
+           uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ float thr[254];
+  __shared__ float wmax[4];
+  for (int i = threadIdx.x; i < 254; i += blockDim.x) thr[i] = dq_threshold(i);
+
+  const int64_t i = (int64_t)blockIdx.x * kDQBlock + threadIdx.x;
+  const bool valid = i < nb;
+  const float mu = mean[0];
+  const float c = valid ? absmax[i] - mu : 0.0f;
+  float m = fabsf(c);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float s = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+  const float n2 = (s > 0.0f) ? c / s : 0.0f;
+  // code = number of thresholds strictly below n2 (binary search).
+  int lo = 0, hi = 254;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (n2 > thr[mid]) lo = mid + 1; else hi = mid;
+  }
+  if (valid) codes[i] = (uint8_t)lo;
+  if (threadIdx.x == 0) scales[blockIdx.x] = s;
+}
+
+// ---------------------------------------------------------------------------
+// nf4_dequant: each lane expands 16 packed bytes (32 weights, half a block).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_nf4_dequant(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
+              const float* __restrict__ scales, const float* __restrict__ mean,
+              int64_t nchunks, uint16_t* __restrict__ out) {
+  __shared__ float q4[16];
+  if (threadIdx.x < 16) q4[threadIdx.x] = nf4_level(threadIdx.x);
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nchunks) return;
+  const int64_t blk = c >> 1;
+  const uint4 p = reinterpret_cast<const uint4*>(packed)[c];
+  const float ah = absmax_decode(codes[blk], scales[blk / kDQBlock], mean[0]);
+  const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+  uint32_t o[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t byte = (pw[j >> 2] >> ((j & 3) * 8)) & 0xffu;
+    const float w0 = q4[byte >> 4] * ah;     // element 2j: high nibble
+    const float w1 = q4[byte & 15u] * ah;
+    o[j] = pack_bf16x2(w0, w1);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + c * 32);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_nf4_quantize(const float* W, int64_t numel, uint8_t* packed, float* absmax,
+                               hipStream_t st) {
+  const int64_t nb = numel / kBlock;
+  const int64_t threads = nb * 8;
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)grid), dim3(256), 0, st, W, nb, packed, absmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, float* scales,
+                               float* mean, hipStream_t st) {
+  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(1024), 0, st, absmax, nb, mean);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ng = (nb + kDQBlock - 1) / kDQBlock;
+  hipLaunchKernelGGL(k_dq_codes, dim3((unsigned)ng), dim3(256), 0, st, absmax, nb, mean, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                              const float* mean, int64_t numel, uint16_t* out, hipStream_t st) {
+  const int64_t nchunks = numel / 32;
+  const int64_t grid = (nchunks + 255) / 256;
+  hipLaunchKernelGGL(k_nf4_dequant, dim3((unsigned)grid), dim3(256), 0, st, packed, codes, scales,
+                     mean, nchunks, out);
+  return hipGetLastError();
+}
+
+}  // namespace qlk

@@ -1,0 +1,169 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) QLoRA NF4 linear-layer library.
+ *
+ * The library implements the QLoRA linear layer of
+ *     h = dequant(W0_NF4) x + (alpha / r) B A x
+ * (llm-compass "QLoRA", section 方法与公式, the displayed equation), forward and
+ * backward, with the frozen base weight stored as 4-bit NormalFloat codes in
+ * blocks of 64 and double-quantised block constants (aigrafen.se "QLoRA",
+ * list "Tre tekniska bitar" items 1-2; auryth.ai "QLoRA", "Hoe het werkt"
+ * NF4 and Dubbele Quantisatie boxes; llm-compass 方法与公式 items 1-2).
+ *
+ * Conventions for every call
+ *   - Array pointers are DEVICE pointers into caller-owned, contiguous,
+ *     row-major buffers, each 16-byte aligned (the kernels use 128-bit loads).
+ *   - bf16 values travel as their uint16_t bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on that stream and returns immediately.
+ *   - Outputs are overwritten (never accumulated) unless a flag says
+ *     otherwise.  The library allocates no device memory and keeps no mutable
+ *     global state: scratch space comes from the caller's `workspace`.
+ *   - Calls return a status code (QLORA_* below).  All argument checks run on
+ *     the host before any launch, so a non-zero status means nothing was
+ *     enqueued.  Faults inside a kernel surface at the next stream
+ *     synchronisation, as in any HIP program.  No C++ exception crosses this
+ *     interface and the library prints nothing.
+ *
+ * Storage format (all produced by nf4_quantize + double_quant):
+ *   W0       [N, K] fp32, row-major (out x in), K % 64 == 0
+ *   packed   [N*K/2] uint8: element 2j in the HIGH nibble of byte j
+ *   absmax   [N*K/64] fp32: max |w| of each run of 64 consecutive elements
+ *   codes    [N*K/64] uint8: 8-bit code of each centred constant
+ *   scales   [ceil(N*K/64/256)] fp32: one second-level scale per 256 constants
+ *   mean     [1] fp32 (device): mean of all absmax values of the tensor
+ * Dequantised weight: w_hat = fp32(Q4[nibble] * a_hat),
+ *   a_hat = fp32(fp32(Q8[code] * scale) + mean),  Q8[i] = fp32(i-127)/127.
+ */
+#ifndef QLORA_H_
+#define QLORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define QLORA_OK                 0
+#define QLORA_ERR_NULL          -1  /* a required pointer is NULL                   */
+#define QLORA_ERR_SHAPE         -2  /* M,N,K <= 0; K % 64; N % 8; r % 8 or r > 256;
+                                       N*K odd or too large                           */
+#define QLORA_ERR_UNSUPPORTED   -3  /* blocksize != 64 or dq_blocksize != 256       */
+#define QLORA_ERR_ALIGN         -4  /* a pointer is not 16-byte aligned             */
+#define QLORA_ERR_WORKSPACE     -5  /* workspace NULL or smaller than required      */
+#define QLORA_ERR_LAUNCH        -6  /* the HIP runtime refused a launch             */
+#define QLORA_ERR_ARG           -7  /* other invalid argument (alpha not finite,
+                                       unknown flag bits)                            */
+
+/* qlora_linear_bwd flag: add the computed dX into the bf16 values already in
+ * dX instead of overwriting them (used when two linears share an input, as
+ * the gate and up projections of a gated MLP do). */
+#define QLORA_BWD_ACCUMULATE_DX  1
+
+/* ---- quantisation (run once, when the base weight is loaded) ------------ */
+
+/* Blockwise NF4 quantisation of W0 [N, K].
+ * llm-compass "QLoRA", 方法与公式 item 1: blocks of 64 weights, one absmax
+ * constant each; auryth.ai "QLoRA", NF4 box: 16 levels at normal quantiles.
+ * For each block: absmax = max |w|; n = w / absmax (IEEE fp32 division);
+ * code = index of the nearest NF4 level, ties to the lower index; a block of
+ * zeros gets the zero level (index 7).  Non-finite inputs give unspecified
+ * codes.  Bit-exact: same bytes on every run.
+ * In:  W0 fp32 [N*K].   Out: packed uint8 [N*K/2], absmax fp32 [N*K/64].
+ * Requires K % 64 == 0, blocksize == 64. */
+int nf4_quantize(const float* W0, int64_t N, int64_t K, int blocksize,
+                 uint8_t* packed, float* absmax, void* stream);
+
+/* Double quantisation of the block constants.
+ * aigrafen.se "QLoRA" item 2 and llm-compass 方法与公式 item 2: the fp32
+ * constants are quantised again, to 8 bits.  mean = fp32(S / nblocks) with S
+ * the fp64 sum taken sequentially inside each run of 256 constants and then
+ * sequentially over those partial sums; c = fp32(absmax - mean); per run of
+ * 256: scale = max |c|; code = nearest level of Q8 to fp32(c / scale), ties
+ * to the lower index (scale == 0 gives code 127).
+ * In:  absmax fp32 [nblocks].
+ * Out: codes uint8 [nblocks], scales fp32 [ceil(nblocks/256)], mean fp32 [1].
+ * Requires dq_blocksize == 256.  Bit-exact. */
+int double_quant(const float* absmax, int64_t nblocks, int dq_blocksize,
+                 uint8_t* codes, float* scales, float* mean, void* stream);
+
+/* Dequantise to the bf16 compute type (auryth.ai "QLoRA", DATASTROOM box;
+ * llm-compass 直觉与动机).  W_bf16[i] = RNE_bf16(w_hat[i]).  Bit-exact.
+ * Out: W_bf16 uint16 [N*K]. */
+int nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                const float* mean, int64_t N, int64_t K, int blocksize,
+                int dq_blocksize, uint16_t* W_bf16, void* stream);
+
+/* ---- the linear layer --------------------------------------------------- */
+
+/* Forward  Y = X W_hat^T + s (X A^T) B^T,  s = fp32(alpha / r)
+ * (llm-compass 方法与公式, the equation, for a batch of rows).
+ *   X  bf16 [M, K]     activations
+ *   A  bf16 [r, K]     adapter down-projection
+ *   B  bf16 [N, r]     adapter up-projection
+ *   Y  bf16 [M, N]     output
+ *   T_out bf16 [M, r]  optional: X A^T for the backward (NULL = not stored)
+ * W_hat is never written to memory: tiles are dequantised on the fly.
+ * Accumulation is fp32; Y is rounded to bf16 once.  Results meet
+ * |err|_F / |ref|_F <= 1e-2 and max|err| <= 3e-2 max|ref| against an exact
+ * evaluation of the same bf16 inputs.
+ * Requires 1 <= M, K % 64 == 0, N % 8 == 0, r % 8 == 0, 8 <= r <= 256, and
+ * workspace_bytes >= qlora_workspace_bytes(M, K, N, r, 0). */
+int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                     const uint8_t* packed, const uint8_t* codes, const float* scales,
+                     const float* mean, const uint16_t* A, const uint16_t* B,
+                     int r, float alpha, uint16_t* Y, uint16_t* T_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of the forward above.  Gradients reach the adapters only; the
+ * frozen base weight gets none (aigrafen.se "QLoRA", opening paragraph;
+ * llm-compass 方法与公式, text under the equation; skillbyai "Quantized base
+ * plus LoRA").  With U = dY B:
+ *   dX = dY W_hat + s U A      bf16 [M, K]  (NULL = skip)
+ *   dA = s U^T X               fp32 [r, K]
+ *   dB = s dY^T (X A^T)        fp32 [N, r]
+ * T is the X A^T saved by the forward (bf16 [M, r]); NULL = recompute it.
+ * flags: 0 or QLORA_BWD_ACCUMULATE_DX.  The reductions over M run in a fixed
+ * order, so repeated calls give identical bits.  Same shape rules and
+ * tolerances as the forward; workspace >= qlora_workspace_bytes(..., 1). */
+int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                     const uint8_t* packed, const uint8_t* codes, const float* scales,
+                     const float* mean, const uint16_t* A, const uint16_t* B,
+                     int r, float alpha, const uint16_t* T,
+                     uint16_t* dX, float* dA, float* dB, int flags,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace the forward (is_bwd = 0) or backward (is_bwd = 1)
+ * needs for these sizes; 0 means none.  Returns 0 for invalid sizes too. */
+size_t qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int r, int is_bwd);
+
+/* ---- gated-MLP glue (not a QLoRA step; used by MLP workloads) ----------- */
+
+/* H = silu(G) * Up, silu(g) = g / (1 + exp(-g)); bf16 [n] each, n % 8 == 0. */
+int silu_mul_fwd(const uint16_t* G, const uint16_t* Up, int64_t n, uint16_t* H,
+                 void* stream);
+
+/* dG = dH * Up * sig(G) * (1 + G (1 - sig(G))),  dUp = dH * silu(G). */
+int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int64_t n,
+                 uint16_t* dG, uint16_t* dUp, void* stream);
+
+/* ---- host-side helpers --------------------------------------------------- */
+
+/* The 16 NF4 levels the kernels use (HOST memory, 16 floats). */
+int nf4_codebook(float* out16);
+
+/* The 8-bit levels the kernels use (HOST memory, 256 floats; *n = 255). */
+int dq_codebook(float* out256, int* n);
+
+/* Static text for a status code. */
+const char* qlora_strerror(int status);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int qlora_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H_ */

@@ -31,7 +31,7 @@ No function is "parity unpinned".
 from .nf4 import (  # noqa: F401
     NF4_DELTA, nf4_codebook, dq_codebook, nearest_index, absmax_blocks,
     quantize_nf4, pack_nibbles, unpack_nibbles, double_quant, dequant_absmax,
-    dequant_nf4, f32_to_bf16_bits, bf16_bits_to_f64, bits_per_param,
+    dequant_nf4, dequant_codes, f32_to_bf16_bits, bf16_bits_to_f64, bits_per_param,
 )
 from .qlora import (  # noqa: F401
     lora_scale, forward, backward, silu_mul_forward, silu_mul_backward,

@@ -242,8 +242,18 @@ def dequant_nf4(packed: np.ndarray, codes: np.ndarray, scales: np.ndarray, mean,
     """
     nib = unpack_nibbles(packed)[:N * K]
     a_hat = dequant_absmax(codes, scales, mean, dq_blocksize)
-    per_elem = np.repeat(a_hat, blocksize)[:N * K]
-    w_hat = (nf4_codebook()[nib] * per_elem).astype(np.float32).reshape(N, K)
+    w_hat, wb = dequant_codes(nib, a_hat, blocksize)
+    return w_hat.reshape(N, K), wb.reshape(N, K)
+
+
+def dequant_codes(codes4: np.ndarray, a_hat: np.ndarray, blocksize: int = 64):
+    """4-bit codes [nblk*blocksize] and the decoded constant of each of their
+    blocks [nblk] -> (w_hat fp32, bf16 bits), w_hat = fp32(Q4[code] * a_hat).
+
+    Works on any whole-block subset of a weight (blocks are independent)."""
+    c = np.asarray(codes4, dtype=np.uint8).reshape(-1)
+    per_elem = np.repeat(np.asarray(a_hat, dtype=np.float32), blocksize)[:c.size]
+    w_hat = (nf4_codebook()[c] * per_elem).astype(np.float32)
     return w_hat, f32_to_bf16_bits(w_hat)
 
 
