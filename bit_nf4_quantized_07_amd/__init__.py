@@ -45,7 +45,10 @@ SIGNATURES = {
     "dq_codebook": (_I, [_P, ctypes.POINTER(_I)]),
     "qlora_strerror": (ctypes.c_char_p, [_I]),
     "qlora_version": (_I, []),
+    "qlora_set_kernel_timer": (_I, [_I, _P, _P]),
 }
+
+KERNEL_FWD_GEMM, KERNEL_DX_GEMM, KERNEL_GEMV = 1, 2, 3
 
 _lib = None
 
@@ -214,7 +217,7 @@ def linear_fwd(X, qw: QuantizedWeight, A, B, alpha: float, save_T: bool = True,
 
 
 def linear_bwd(dY, X, qw: QuantizedWeight, A, B, alpha: float, T=None, need_dX: bool = True,
-               accumulate_into=None, dA_out=None, dB_out=None, workspace=None):
+               accumulate_into=None, dX_out=None, dA_out=None, dB_out=None, workspace=None):
     """Returns (dX bf16 [M,K] or None, dA fp32 [r,K], dB fp32 [N,r])."""
     torch = _torch()
     M, K = X.shape
@@ -224,6 +227,8 @@ def linear_bwd(dY, X, qw: QuantizedWeight, A, B, alpha: float, T=None, need_dX: 
     if accumulate_into is not None:
         dX = accumulate_into
         flags |= BWD_ACCUMULATE_DX
+    elif dX_out is not None:
+        dX = dX_out
     else:
         dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device) if need_dX else None
     dA = dA_out if dA_out is not None else torch.empty(r, K, dtype=torch.float32, device=X.device)

@@ -500,6 +500,24 @@ k_lora_down_small(const uint16_t* __restrict__ X, int M, int64_t K, const uint16
   }
 }
 
+// ---------------------------- measurement hook ------------------------------
+
+namespace {
+hipEvent_t g_timer_start[TK_COUNT] = {};
+hipEvent_t g_timer_stop[TK_COUNT] = {};
+}  // namespace
+
+void set_kernel_timer(int kernel, hipEvent_t start, hipEvent_t stop) {
+  g_timer_start[kernel] = start;
+  g_timer_stop[kernel] = stop;
+}
+void timer_begin(int kernel, hipStream_t st) {
+  if (g_timer_start[kernel]) (void)hipEventRecord(g_timer_start[kernel], st);
+}
+void timer_end(int kernel, hipStream_t st) {
+  if (g_timer_stop[kernel]) (void)hipEventRecord(g_timer_stop[kernel], st);
+}
+
 // ------------------------------- planning ----------------------------------
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -639,7 +657,9 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
     hipLaunchKernelGGL(k_lora_down_small, dim3(r), dim3(256), 0, st, X, (int)M, K, A, r, T);
     QLK_TRY(hipGetLastError());
     const unsigned grid = (unsigned)((N + 63) / 64);
+    timer_begin(TK_GEMV, st);
     hipLaunchKernelGGL(k_gemv_nf4, dim3(grid), dim3(256), 0, st, X, (int)M, w, T, B, r, s, Y);
+    timer_end(TK_GEMV, st);
     return hipGetLastError();
   }
   float* part = reinterpret_cast<float*>(base + plan.off_part);
@@ -653,8 +673,11 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   g.P = (int)M; g.Q = (int)N;
   g.c1_len = (int)K; g.c1_split = (int)K; g.c2_len = r;
   g.out = Y; g.ldo = N; g.accumulate = 0;
-  return launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdNF4K<128>, LdBF16K<128, kBK, false>,
-                     LdBF16K<128, kBK, true>, EPI_BF16>(g, 1, st);
+  timer_begin(TK_FWD_GEMM, st);
+  const hipError_t e = launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdNF4K<128>,
+                                   LdBF16K<128, kBK, false>, LdBF16K<128, kBK, true>, EPI_BF16>(g, 1, st);
+  timer_end(TK_FWD_GEMM, st);
+  return e;
 }
 
 hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
@@ -686,8 +709,11 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     g.P = (int)M; g.Q = (int)K;
     g.c1_len = (int)N; g.c1_split = (int)N; g.c2_len = r;
     g.out = dX; g.ldo = K; g.accumulate = accumulate_dx ? 1 : 0;
-    QLK_TRY((launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdNF4MN<128, kBK, 4>,
-                         LdBF16K<128, kBK, false>, LdBF16MN<128, kBK, true>, EPI_BF16>(g, 1, st)));
+    timer_begin(TK_DX_GEMM, st);
+    const hipError_t e = launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdNF4MN<128, kBK, 4>,
+                                     LdBF16K<128, kBK, false>, LdBF16MN<128, kBK, true>, EPI_BF16>(g, 1, st);
+    timer_end(TK_DX_GEMM, st);
+    QLK_TRY(e);
   }
   // dA = s U^T X: rows j (U^T, transposed), cols k (X^T, transposed), contraction m.
   QLK_TRY((skinny<1, 1, true>(rt, opnd(U, r, r), opnd(X, K, (int)K), r, (int)K, M, plan.m_splits_a,

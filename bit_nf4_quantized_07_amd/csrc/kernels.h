@@ -43,6 +43,12 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,
                             bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st);
 
+// Measurement hook: events recorded around individual launches.
+enum TimedKernel { TK_NONE = 0, TK_FWD_GEMM = 1, TK_DX_GEMM = 2, TK_GEMV = 3, TK_COUNT = 4 };
+void set_kernel_timer(int kernel, hipEvent_t start, hipEvent_t stop);
+void timer_begin(int kernel, hipStream_t st);
+void timer_end(int kernel, hipStream_t st);
+
 hipError_t launch_silu_mul_fwd(const uint16_t* G, const uint16_t* U, int64_t n, uint16_t* H,
                                hipStream_t st);
 hipError_t launch_silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* U,

@@ -181,6 +181,13 @@ const char* qlora_strerror(int status) {
   }
 }
 
+int qlora_set_kernel_timer(int kernel, void* ev_start, void* ev_stop) {
+  if (kernel <= 0 || kernel >= QLORA_KERNEL_COUNT) return QLORA_ERR_ARG;
+  qlk::set_kernel_timer(kernel, reinterpret_cast<hipEvent_t>(ev_start),
+                        reinterpret_cast<hipEvent_t>(ev_stop));
+  return QLORA_OK;
+}
+
 int qlora_version(void) { return 100; }
 
 }  // extern "C"

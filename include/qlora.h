@@ -16,8 +16,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call only enqueues work on that stream and returns immediately.
  *   - Outputs are overwritten (never accumulated) unless a flag says
- *     otherwise.  The library allocates no device memory and keeps no mutable
- *     global state: scratch space comes from the caller's `workspace`.
+ *     otherwise.  The library allocates no device memory: scratch space comes
+ *     from the caller's `workspace`.  Its only mutable global state is the
+ *     optional measurement hook (qlora_set_kernel_timer).
  *   - Calls return a status code (QLORA_* below).  All argument checks run on
  *     the host before any launch, so a non-zero status means nothing was
  *     enqueued.  Faults inside a kernel surface at the next stream
@@ -147,6 +148,22 @@ int silu_mul_fwd(const uint16_t* G, const uint16_t* Up, int64_t n, uint16_t* H,
 /* dG = dH * Up * sig(G) * (1 + G (1 - sig(G))),  dUp = dH * silu(G). */
 int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int64_t n,
                  uint16_t* dG, uint16_t* dUp, void* stream);
+
+/* ---- measurement hook ---------------------------------------------------- */
+
+/* Internal kernels that can be timed individually. */
+#define QLORA_KERNEL_FWD_GEMM   1  /* fused dequant GEMM  Y = X W_hat^T + s T B^T     */
+#define QLORA_KERNEL_DX_GEMM    2  /* fused dequant GEMM  dX = dY W_hat + s U A       */
+#define QLORA_KERNEL_GEMV       3  /* small-M dequant GEMV forward                    */
+#define QLORA_KERNEL_COUNT      4
+
+/* While set, each launch of `kernel` is bracketed by hipEventRecord(ev_start)
+ * and hipEventRecord(ev_stop) on the stream of the call that launches it
+ * (events are hipEvent_t passed as void*, created by the caller).  Passing
+ * NULL events clears the slot.  The slots are process-wide and not
+ * thread-safe: this is for benchmarks, not for production use.  Returns
+ * QLORA_ERR_ARG for an unknown kernel id. */
+int qlora_set_kernel_timer(int kernel, void* ev_start, void* ev_stop);
 
 /* ---- host-side helpers --------------------------------------------------- */
 

@@ -136,6 +136,13 @@ def test_workspace_sizes():
     assert lib.qlora_workspace_bytes(2048, 4096, 4096, 16, 1) >= 2 * 2048 * 16 * 2
 
 
+def test_kernel_timer_validation():
+    assert lib.qlora_set_kernel_timer(0, None, None) == q.ERR_ARG
+    assert lib.qlora_set_kernel_timer(4, None, None) == q.ERR_ARG
+    for k in (1, 2, 3):
+        assert lib.qlora_set_kernel_timer(k, None, None) == q.OK
+
+
 def test_silu_validation():
     assert lib.silu_mul_fwd(D, None, 64, D, None) == q.ERR_NULL
     assert lib.silu_mul_fwd(D, D, 60, D, None) == q.ERR_SHAPE
