@@ -57,6 +57,23 @@ __device__ __forceinline__ float absmax_decode(int code, float scale, float mean
   return p + mean;
 }
 
+// Same decode with the 8-bit levels read from a table (e.g. in LDS) that
+// holds dq_level(i) at index i.
+__device__ __forceinline__ float absmax_decode_tab(int code, float scale, float mean,
+                                                   const float* q8) {
+#pragma clang fp contract(off)
+  float p = q8[code] * scale;
+  return p + mean;
+}
+
+// Decode context handed to the NF4 tile loaders: the 16 NF4 levels and the
+// 256 8-bit levels (both in LDS) and the tensor's mean constant.
+struct Dec {
+  const float* q4;
+  const float* q8;
+  float mean;
+};
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -99,6 +116,18 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&o
     }
     out[j] = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t* lds_v4s_ptr;
+
+// LDS transpose read of 16-bit elements (gfx950 ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane t receives element (t % 4) of the 8-byte pieces
+// that source lanes 4s + t/4 point at, for s = 0..3.  If source lane 4s + u of
+// a group points at row r0 + s, column c0 + 4u of a row-major tile, lane t
+// receives column c0 + t of rows r0 .. r0+3.
+__device__ __forceinline__ v4s_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p));
 }
 
 __device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {

@@ -1,0 +1,75 @@
+// Gated-MLP glue used by the MLP workloads: H = silu(G) * Up and its
+// derivative, bf16 in and out, fp32 inside.  Not a QLoRA step; the pages only
+// name gate/up/down projections as adapter targets.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qlk {
+
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+__global__ void __launch_bounds__(256)
+k_silu_mul_fwd(const uint16_t* __restrict__ G, const uint16_t* __restrict__ U, int64_t n8,
+               uint16_t* __restrict__ H) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 gv = reinterpret_cast<const uint4*>(G)[i];
+  const uint4 uv = reinterpret_cast<const uint4*>(U)[i];
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float g0 = bf16_to_f32(gw[q] & 0xffffu), g1 = bf16_to_f32(gw[q] >> 16);
+    const float u0 = bf16_to_f32(uw[q] & 0xffffu), u1 = bf16_to_f32(uw[q] >> 16);
+    o[q] = pack_bf16x2(g0 * sigmoidf_(g0) * u0, g1 * sigmoidf_(g1) * u1);
+  }
+  reinterpret_cast<uint4*>(H)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__global__ void __launch_bounds__(256)
+k_silu_mul_bwd(const uint16_t* __restrict__ dH, const uint16_t* __restrict__ G,
+               const uint16_t* __restrict__ U, int64_t n8, uint16_t* __restrict__ dG,
+               uint16_t* __restrict__ dU) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 hv = reinterpret_cast<const uint4*>(dH)[i];
+  const uint4 gv = reinterpret_cast<const uint4*>(G)[i];
+  const uint4 uv = reinterpret_cast<const uint4*>(U)[i];
+  const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w},
+                 uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  uint32_t og[4], ou[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float rg[2], ru[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float d = bf16_to_f32(h ? hw[q] >> 16 : hw[q] & 0xffffu);
+      const float g = bf16_to_f32(h ? gw[q] >> 16 : gw[q] & 0xffffu);
+      const float u = bf16_to_f32(h ? uw[q] >> 16 : uw[q] & 0xffffu);
+      const float sg = sigmoidf_(g);
+      rg[h] = d * u * sg * (1.0f + g * (1.0f - sg));
+      ru[h] = d * g * sg;
+    }
+    og[q] = pack_bf16x2(rg[0], rg[1]);
+    ou[q] = pack_bf16x2(ru[0], ru[1]);
+  }
+  reinterpret_cast<uint4*>(dG)[i] = make_uint4(og[0], og[1], og[2], og[3]);
+  reinterpret_cast<uint4*>(dU)[i] = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+}
+
+hipError_t launch_silu_mul_fwd(const uint16_t* G, const uint16_t* U, int64_t n, uint16_t* H,
+                               hipStream_t st) {
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_silu_mul_fwd, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, G, U, n8, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* U,
+                               int64_t n, uint16_t* dG, uint16_t* dU, hipStream_t st) {
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_silu_mul_bwd, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dH, G, U,
+                     n8, dG, dU);
+  return hipGetLastError();
+}
+
+}  // namespace qlk

@@ -21,6 +21,9 @@ struct NF4Weight {
   int64_t N, K;
 };
 
+// Token counts up to this take the small-M (GEMV) forward.
+constexpr int kGemvMaxM = 16;
+
 // Workspace layout shared by the planner (qlora_workspace_bytes) and the
 // launchers, so that both always agree.
 struct FwdPlan {
@@ -38,6 +41,8 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r);
 hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                             const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
                             void* ws, const FwdPlan& plan, hipStream_t st);
+hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
+                       const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, hipStream_t st);
 hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
                             const uint16_t* A, const uint16_t* B, int r, float s,
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,
