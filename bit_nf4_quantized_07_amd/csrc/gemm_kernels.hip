@@ -646,7 +646,8 @@ FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r) {
     p.t_splits = actual_splits(K, choose_splits(blocks, K));
     off += align256((size_t)p.t_splits * M * r * 4);
   } else {
-    p.t_splits = 0;
+    p.t_splits = kTSplits;
+    off += align256((size_t)kTSplits * M * r * 4);
   }
   p.bytes = off;
   return p;
@@ -760,8 +761,8 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   const int64_t K = w.K, N = w.N;
   char* base = reinterpret_cast<char*>(ws);
   uint16_t* T = T_out ? T_out : reinterpret_cast<uint16_t*>(base + plan.off_T);
-  if (plan.gemv) return launch_gemv(X, M, w, A, B, r, s, Y, T, st);
   float* part = reinterpret_cast<float*>(base + plan.off_part);
+  if (plan.gemv) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st);
   QLK_TRY(compute_T(X, M, K, A, r, plan.t_splits, part, T, st));
   GemmArgs g{};
   g.a1 = opnd(X, K, (int)M, M);

@@ -23,6 +23,8 @@ struct NF4Weight {
 
 // Token counts up to this take the small-M (GEMV) forward.
 constexpr int kGemvMaxM = 16;
+// K slices of the small-M T = X A^T partial sums.
+constexpr int kTSplits = 16;
 
 // Workspace layout shared by the planner (qlora_workspace_bytes) and the
 // launchers, so that both always agree.
@@ -42,7 +44,8 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
                             const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
                             void* ws, const FwdPlan& plan, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
-                       const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, hipStream_t st);
+                       const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
+                       hipStream_t st);
 hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
                             const uint16_t* A, const uint16_t* B, int r, float s,
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,
