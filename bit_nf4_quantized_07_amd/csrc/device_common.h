@@ -137,4 +137,62 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+
+// ----------------------------- buffer loads ---------------------------------
+//
+// Loads go through raw buffer resources.  Each loader fixes its per-lane byte
+// offsets once per phase (init); every K-step only moves the resource base by
+// a scalar amount, so the loads cost no vector address arithmetic.  A lane
+// whose element lies outside the operand uses an offset past the end of the
+// buffer and the hardware returns zero.
+
+constexpr uint32_t kOOB = 0x80000000u;       // offset beyond any accepted buffer
+constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
+
+// All arguments are wave-uniform.  The remaining size is a saturating
+// subtraction, which exists only as a vector instruction; readfirstlane brings
+// it back to a scalar register, so the resource stays in scalar registers and
+// the load needs no per-lane resource loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint32_t bytes,
+                                                          uint32_t shift) {
+  shift = __builtin_amdgcn_readfirstlane(shift);
+  const uint32_t rem = __builtin_amdgcn_readfirstlane(shift < bytes ? bytes - shift : 0u);
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(reinterpret_cast<const char*>(base) + shift), (short)0, (int)rem,
+      kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
+}
+
+
+// ------------------------- workgroup -> tile order ---------------------------
+
+constexpr int kXCDs = 8;   // the hardware deals workgroup ids round-robin over 8 XCDs
+
+// Tile coordinates of workgroup `bid`: ids are first regrouped so that the
+// workgroups one XCD receives (bid = x, x+8, x+16, ...) get consecutive
+// positions, then walked in groups of `group_p` tile rows across all tile
+// columns.  Both steps are bijections on [0, tiles).
+__device__ __forceinline__ void tile_coords(int bid, int tiles_p, int tiles_q, int group_p, int& tp,
+                                            int& tq) {
+  const int total = tiles_p * tiles_q;
+  const int full = (total / kXCDs) * kXCDs;
+  int t = bid;
+  if (bid < full) t = (bid % kXCDs) * (full / kXCDs) + bid / kXCDs;
+  const int per_group = group_p * tiles_q;
+  const int gi = t / per_group;
+  const int first = gi * group_p;
+  const int gp = min(group_p, tiles_p - first);
+  const int rem = t - gi * per_group;
+  tp = first + rem % gp;
+  tq = rem / gp;
+}
+
 }  // namespace qlk

@@ -1,0 +1,306 @@
+// Forward of the QLoRA linear layer for more than 16 tokens, on gfx950:
+//
+//   Y = X W_hat^T + s T B^T,   T = X A^T,   s = alpha / r
+//                                   (llm-compass "QLoRA", 方法与公式, the equation)
+//
+// One workgroup computes a 256 x 128 tile of Y (tokens x weight rows) with
+// four waves; wave w owns weight rows 32w .. 32w+31 of the tile and all 256
+// tokens: eight accumulators of v_mfma_f32_32x32x16_bf16, each computing a
+// 32 (weight rows) x 32 (tokens) block of Y^T.
+//
+//  * X is staged through LDS, one 256 x 64 tile per K-step, in four
+//    buffers, by buffer loads that write LDS directly (no registers, no LDS
+//    store instructions): X(k+3) is in flight while X(k) is multiplied, and
+//    the first MFMA operands of step k+1 are read from the already complete
+//    X(k+1) before the barrier that ends step k, so no step starts by
+//    waiting on LDS.  Rows are 128 bytes; the 16-byte pieces of row r are
+//    stored XOR-swizzled by (r >> 1) & 7, which makes the operand reads
+//    (16 rows x 16 bytes per bank cycle) conflict-free.
+//  * The NF4 weight never goes through LDS: each lane loads the 16 packed
+//    bytes (32 weights) of its weight row that its half of the MFMA operand
+//    covers, plus the block's 8-bit code and second-level scale, and decodes
+//    them straight into the bf16 MFMA operand.  Every weight is decoded once.
+//    The decode is the standalone dequantiser's arithmetic:
+//      a_hat = fp32(fp32(Q8[code] * scale) + mean),
+//      w_hat = bf16(fp32(Q4[nibble] * a_hat)),
+//    with the 16 fp32 levels in LDS (a 64-byte table: lanes that read
+//    different levels always hit different banks).
+//  * Inside a 64-block the contraction order is permuted so that a lane's 32
+//    weights are contiguous in memory: at MFMA step t (0..3) lane half h
+//    covers k = 32h + 8t .. 32h + 8t + 7, for X and for the weight alike.
+//  * Each K-step is a fixed schedule of 32 MFMA slots; the LDS reads of the
+//    decode table are issued 16 slots before their values are used, and the
+//    operand reads of MFMA step t+1 during step t.  Global loads of X and of
+//    the weight run three K-steps ahead.
+//  * The adapter term s T B^T is a last contraction over r into the same
+//    accumulators (the up-projection fused into the base GEMM).
+//  * The accumulator layout gives each lane four consecutive weight rows of
+//    one token, so Y is written 8 bytes at a time.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qlk {
+
+constexpr int kFwdBM = 256;                    // tokens per tile
+constexpr int kFwdWaveN = 32;                  // weight rows per wave
+constexpr int kFwdBN = 4 * kFwdWaveN;          // weight rows per tile
+constexpr int kXRow = kBlock;                  // LDS row of the X tile (elements, swizzled)
+constexpr int kXTile = kFwdBM * kXRow;         // elements per X buffer
+constexpr int kXBufs = 4;
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= 11, expcnt and lgkmcnt not waited on.
+constexpr int kWaitVm11 = (11 & 0xF) | ((11 >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+constexpr int kFwdUnroll = 4;                  // K-steps per loop iteration (register sets)
+
+struct FwdArgs {
+  const uint16_t* X;
+  int M;
+  NF4Weight w;
+  const uint16_t* T;    // [M, r] bf16
+  const uint16_t* B;    // [N, r] bf16
+  int r;
+  float s;
+  uint16_t* Y;
+  int tiles_m, tiles_n, group_m;
+};
+
+struct FwdWRegs { uint4 p; uint32_t code; float sc; };
+struct FwdBFrag { uint32_t d[4][4]; };   // [MFMA step][dword]
+
+__device__ __forceinline__ bf16x8_t as_frag(const uint32_t (&d)[4]) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
+}
+
+__global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
+  // Tables first (low LDS addresses fit the instructions' offset field),
+  // then the X buffers as four separate objects, so that the compiler can
+  // tell that a load into one buffer does not alias reads of another.
+  __shared__ __attribute__((aligned(64))) float q4[16];
+  __shared__ __attribute__((aligned(64))) float q8[256];
+  __shared__ __attribute__((aligned(16))) uint16_t xs0[kXTile];
+  __shared__ __attribute__((aligned(16))) uint16_t xs1[kXTile];
+  __shared__ __attribute__((aligned(16))) uint16_t xs2[kXTile];
+  __shared__ __attribute__((aligned(16))) uint16_t xs3[kXTile];
+  uint16_t* const xbuf[kXBufs] = {xs0, xs1, xs2, xs3};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  if (tid < 16) q4[tid] = nf4_level(tid);
+  q8[tid] = dq_level(tid);
+
+  int tm, tn;
+  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int m0 = tm * kFwdBM;
+  const int64_t K = g.w.K, N = g.w.N, nkb = K / kBlock;
+  const int nk = (int)nkb;
+  const float mean = g.w.mean[0];
+
+  // X tile loads: wave w, load i fills rows 64 w + 8 i .. +7 (1 KB of LDS);
+  // lane L lands at LDS offset 16 L, i.e. row 64 w + 8 i + L / 8, physical
+  // piece L % 8, which holds logical piece (L % 8) ^ swz(row).
+  const uint32_t xbytes = (uint32_t)((int64_t)g.M * K * 2);
+  auto swz = [](int row) { return (row >> 1) & 7; };
+  uint32_t xoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + (lane >> 3);
+    const int piece = (lane & 7) ^ swz(row);
+    xoff[i] = m0 + row < g.M ? (uint32_t)(((int64_t)(m0 + row) * K + piece * 8) * 2) : kOOB;
+  }
+  // Operand reads: row 32 i + c, logical piece 4 h + t -> physical.
+  int xrd[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) xrd[t] = c * kXRow + (((4 * h + t) ^ swz(c)) * 8);
+  // Weight row of this lane.
+  const int64_t nrow = (int64_t)tn * kFwdBN + wave * kFwdWaveN + c;
+  const bool nvalid = nrow < N;
+  const uint32_t pbytes = (uint32_t)(N * (K / 2)), cbytes = (uint32_t)(N * nkb);
+  const uint32_t sbytes = (uint32_t)(((N * nkb + kDQBlock - 1) / kDQBlock) * 4);
+  const uint32_t poff = nvalid ? (uint32_t)(nrow * (K / 2) + 16 * h) : kOOB;
+  const uint32_t coff = nvalid ? (uint32_t)(nrow * nkb) : kOOB;
+
+  // kb is wave-uniform; readfirstlane keeps the buffer resources scalar.
+  // Eight buffer loads straight into LDS buffer `buf`.
+  auto load_x = [&](uint16_t* buf, int kb) {
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(g.X, xbytes, (uint32_t)kb * (kBlock * 2));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * i) * kXRow), 16,
+          xoff[i], 0, 0, 0);
+  };
+  auto load_w = [&](FwdWRegs& R, int kb) {
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    const __amdgpu_buffer_rsrc_t rp = rsrc_at(g.w.packed, pbytes, (uint32_t)kb * (kBlock / 2));
+    const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.w.codes, cbytes, (uint32_t)kb);
+    const __amdgpu_buffer_rsrc_t rsc = rsrc_at(g.w.scales, sbytes, 0u);
+    R.p = bload128(rp, poff);
+    R.code = bload8(rc, coff);
+    R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + (uint32_t)kb) / kDQBlock) * 4u));
+  };
+  auto word = [](const FwdWRegs& R, int t) -> uint32_t {
+    return t == 0 ? R.p.x : t == 1 ? R.p.y : t == 2 ? R.p.z : R.p.w;
+  };
+  // Operand of MFMA step t for token tile i: X row 32 i + c, k = 32 h + 8 t.
+  auto xfrag = [&](const uint16_t* buf, int i, int t) -> bf16x8_t {
+    return *reinterpret_cast<const bf16x8_t*>(buf + 32 * i * kXRow + xrd[t]);
+  };
+  // Level of a nibble: hi4 / lo4 hold 4 x (high / low nibble) of each byte
+  // of a packed word; the byte permute unit moves byte e to bits 0..7, which
+  // is the byte offset of the level in q4.
+  const char* q4b = reinterpret_cast<const char*>(q4);
+  auto level = [&](uint32_t nib4, int e) -> float {
+    return *reinterpret_cast<const float*>(q4b + __builtin_amdgcn_perm(0u, nib4, 0x0c0c0c00u | e));
+  };
+  auto hi4 = [](uint32_t w) { return (w >> 2) & 0x3C3C3C3Cu; };
+  auto lo4 = [](uint32_t w) { return (w << 2) & 0x3C3C3C3Cu; };
+  auto decode_all = [&](const FwdWRegs& R, FwdBFrag& F) {
+    const float ah = absmax_decode_tab((int)R.code, R.sc, mean, q8);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        F.d[t][e] = pack_bf16x2(level(hi4(word(R, t)), e) * ah, level(lo4(word(R, t)), e) * ah);
+  };
+
+  f32x16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+
+  // Register sets: W(j) in wr[j % 4] from its load (step j-3) to its decode
+  // (step j-1); the decoded W(j) in bf[j % 2] during step j.  X(j) is in LDS
+  // buffer j % 4 from its load (step j-3) to step j.
+  FwdWRegs wr[4];
+  FwdBFrag bf[2];
+  bf16x8_t a[2][8];
+  __syncthreads();   // tables
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    load_x(xbuf[j], min(j, nk - 1));
+    load_w(wr[j], min(j, nk - 1));
+  }
+  decode_all(wr[0], bf[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[0][i] = xfrag(xbuf[0], i, 0);
+
+  // One K-step; P = kb % kFwdUnroll selects the register sets.
+  auto step = [&](auto Pc, int kb) {
+    constexpr int P = decltype(Pc)::value;
+    const FwdWRegs& wdec = wr[(P + 1) % 4];
+    FwdWRegs& wload = wr[(P + 3) % 4];
+    const FwdBFrag& bc = bf[P % 2];
+    FwdBFrag& bn = bf[(P + 1) % 2];
+    // kb % 4 == P: the loop starts at 0 and steps by 4
+    const uint16_t* xcur = xbuf[P];
+    const uint16_t* xnext = xbuf[(P + 1) % kXBufs];
+
+    // 3 weight loads, then 8 X loads into the buffer of step kb-1 (its
+    // operand reads by this wave completed before the last barrier).
+    load_w(wload, min(kb + 3, nk - 1));
+    load_x(xbuf[(P + 3) % kXBufs], min(kb + 3, nk - 1));
+    const float q8v = q8[wdec.code];
+    float ah = 0.0f;
+    float lh[16], ll[16];
+    uint32_t nh[4], nl[4];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int t = u / 8, i = u % 8;
+      acc[i] = mfma_32x32x16(as_frag(bc.d[t]), a[t & 1][i], acc[i]);
+      if (t < 3) a[(t + 1) & 1][i] = xfrag(xcur, i, t + 1);
+      else a[0][i] = xfrag(xnext, i, 0);
+      if (u < 16) {
+        if (u % 4 == 0) {
+          nh[u / 4] = hi4(word(wdec, u / 4));
+          nl[u / 4] = lo4(word(wdec, u / 4));
+        }
+        lh[u] = level(nh[u / 4], u % 4);
+        ll[u] = level(nl[u / 4], u % 4);
+      }
+      if (u == 2) {
+#pragma clang fp contract(off)
+        const float p = q8v * wdec.sc;
+        ah = p + mean;
+      }
+      if (u >= 16) {
+        const int v = u - 16;
+        bn.d[v / 4][v % 4] = pack_bf16x2(lh[v] * ah, ll[v] * ah);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // X(kb+2) (loaded during step kb-1) must be in LDS, from every wave,
+    // before step kb+1 reads it: wait until at most this step's 11 loads
+    // are outstanding, then barrier.
+    __builtin_amdgcn_s_waitcnt(kWaitVm11);
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int kb = 0; kb < nk; kb += kFwdUnroll) {
+    step(std::integral_constant<int, 0>(), kb);
+    step(std::integral_constant<int, 1>(), kb + 1);
+    step(std::integral_constant<int, 2>(), kb + 2);
+    step(std::integral_constant<int, 3>(), kb + 3);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
+
+  // Adapter term: acc += (s B) T^T over r in steps of 16 (natural order).
+  for (int r0 = 0; r0 < g.r; r0 += 16) {
+    const int rr = r0 + 8 * h;
+    uint4 bv = make_uint4(0, 0, 0, 0);
+    if (nvalid && rr < g.r) {
+      bv = *reinterpret_cast<const uint4*>(g.B + nrow * g.r + rr);
+      uint32_t wv[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        wv[q] = pack_bf16x2(bf16_to_f32(wv[q] & 0xffffu) * g.s, bf16_to_f32(wv[q] >> 16) * g.s);
+      bv = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, bv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + 32 * i + c;
+      uint4 tv = make_uint4(0, 0, 0, 0);
+      if (m < g.M && rr < g.r) tv = *reinterpret_cast<const uint4*>(g.T + (int64_t)m * g.r + rr);
+      acc[i] = mfma_32x32x16(bfr, __builtin_bit_cast(bf16x8_t, tv), acc[i]);
+    }
+  }
+
+  // Accumulator i: lane holds token m = m0 + 32 i + c and weight rows
+  // 8 (v / 4) + 4 h + (v % 4) of the wave's 32; four consecutive rows are
+  // one 8-byte store.
+  const int64_t nw0 = (int64_t)tn * kFwdBN + wave * kFwdWaveN;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + 32 * i + c;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = nw0 + 8 * q + 4 * h;
+      if (n >= N) continue;   // N % 8 == 0: a group of four is all in or all out
+      uint2 o;
+      o.x = pack_bf16x2(acc[i][4 * q + 0], acc[i][4 * q + 1]);
+      o.y = pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3]);
+      *reinterpret_cast<uint2*>(g.Y + (int64_t)m * N + n) = o;
+    }
+  }
+}
+
+bool fwd_nf4_supported(int64_t K) { return (K / kBlock) % kFwdUnroll == 0; }
+
+hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
+                          const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
+  if (!fwd_nf4_supported(w.K)) return hipErrorInvalidValue;
+  FwdArgs g;
+  g.X = X; g.M = (int)M; g.w = w; g.T = T; g.B = B; g.r = r; g.s = s; g.Y = Y;
+  g.tiles_m = (int)((M + kFwdBM - 1) / kFwdBM);
+  g.tiles_n = (int)((w.N + kFwdBN - 1) / kFwdBN);
+  g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * w.K * 2, (double)kFwdBN * w.K * 0.52);
+  hipLaunchKernelGGL(k_fwd_nf4, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace qlk

@@ -40,7 +40,6 @@ constexpr int kThreads = 256;
 #define QLK_PREFETCH2 0
 #endif
 constexpr int kPad = 8;   // bf16 elements of padding per LDS row (bank spread)
-constexpr int kXCDs = 8;
 
 struct Operand {
   const uint16_t* p;   // bf16 source (unused by NF4 loaders)
@@ -63,31 +62,6 @@ struct GemmArgs {
 
 // ------------------------------- loaders -----------------------------------
 //
-// Loads go through raw buffer resources.  Each loader fixes its per-lane byte
-// offsets once per phase (init); every K-step only moves the resource base by
-// a scalar amount, so the loads cost no vector address arithmetic.  A lane
-// whose element lies outside the operand uses an offset past the end of the
-// buffer and the hardware returns zero.
-
-constexpr uint32_t kOOB = 0x80000000u;       // offset beyond any accepted buffer
-constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint32_t bytes,
-                                                          uint32_t shift) {
-  return __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(reinterpret_cast<const char*>(base) + shift), (short)0,
-      (int)(shift < bytes ? bytes - shift : 0u), kRsrcWord3);
-}
-__device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
-__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, 0, 0);
-}
-
 struct LdNone {
   static constexpr bool TR = false;
   struct Regs {};
@@ -486,25 +460,6 @@ struct Tile {
   }
 };
 
-// Tile coordinates of workgroup `bid`: ids are first regrouped so that the
-// workgroups one XCD receives (bid = x, x+8, x+16, ...) get consecutive
-// positions, then walked in groups of `group_p` tile rows across all tile
-// columns.  Both steps are bijections on [0, tiles).
-__device__ __forceinline__ void tile_coords(int bid, int tiles_p, int tiles_q, int group_p, int& tp,
-                                            int& tq) {
-  const int total = tiles_p * tiles_q;
-  const int full = (total / kXCDs) * kXCDs;
-  int t = bid;
-  if (bid < full) t = (bid % kXCDs) * (full / kXCDs) + bid / kXCDs;
-  const int per_group = group_p * tiles_q;
-  const int gi = t / per_group;
-  const int first = gi * group_p;
-  const int gp = min(group_p, tiles_p - first);
-  const int rem = t - gi * per_group;
-  tp = first + rem % gp;
-  tq = rem / gp;
-}
-
 template <int BM, int BN, int BK, int WGM, int WGN, class LA1, class LB1, class LA2, class LB2, int EPI>
 __global__ void __launch_bounds__(kThreads) k_gemm(GemmArgs g) {
   using T = Tile<BM, BN, BK, WGM, WGN>;
@@ -563,16 +518,37 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmArgs g) {
 }
 
 // Fixed-order reduction of split partials: out = scale * sum_z part[z].
+// n is a multiple of 4.  A workgroup covers 64 groups of four outputs; its
+// four waves sum the splits z = g, g+4, g+8, ... (wave g, increasing z) with
+// 16-byte loads, and the four wave sums are added in the order g = 0..3.
 __global__ void __launch_bounds__(256)
 k_reduce_splits(const float* __restrict__ part, int splits, int64_t n, float scale,
                 float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.0f;
-  for (int z = 0; z < splits; ++z) s += part[(int64_t)z * n + i];
-  s *= scale;
-  if (out_f32) out_f32[i] = s;
-  if (out_bf16) out_bf16[i] = f32_to_bf16(s);
+  __shared__ float4 red[4][64];
+  const int tid = threadIdx.x, col = tid & 63, g = tid >> 6;
+  const int64_t n4 = n / 4;
+  const int64_t i4 = (int64_t)blockIdx.x * 64 + col;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (i4 < n4) {
+    const float4* p = reinterpret_cast<const float4*>(part) + i4;
+#pragma unroll 8
+    for (int z = g; z < splits; z += 4) {
+      const float4 v = p[(int64_t)z * n4];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  }
+  red[g][col] = acc;
+  __syncthreads();
+  if (g != 0 || i4 >= n4) return;
+  float4 t = red[0][col];
+#pragma unroll
+  for (int q = 1; q < 4; ++q) {
+    const float4 v = red[q][col];
+    t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+  }
+  t.x *= scale; t.y *= scale; t.z *= scale; t.w *= scale;
+  if (out_f32) reinterpret_cast<float4*>(out_f32)[i4] = t;
+  if (out_bf16) reinterpret_cast<uint2*>(out_bf16)[i4] = make_uint2(pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w));
 }
 
 // ---------------------------- measurement hook ------------------------------
@@ -607,6 +583,12 @@ constexpr int kBK = 64;
 #endif
 #ifndef QLK_DX_BN
 #define QLK_DX_BN 128
+#endif
+
+// 1: the forward runs on the generic tile engine (NF4 tiles decoded into
+// LDS); 0: on the register-decode forward kernel.
+#ifndef QLK_FWD_TILE_ENGINE
+#define QLK_FWD_TILE_ENGINE 0
 #endif
 
 // Token counts at or above this use 256-row forward tiles (fewer decodes of
@@ -676,7 +658,7 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r) {
 // Number of tile rows walked together: the square root of (tiles per XCD x
 // the bytes of a B tile / the bytes of an A tile) balances the two operand
 // footprints each XCD keeps in its L2.
-static inline int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes) {
+int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes) {
   const double per_xcd = (double)tiles_p * tiles_q / kXCDs;
   int gsz = (int)(sqrt(per_xcd * b_tile_bytes / a_tile_bytes) + 0.5);
   if (gsz < 1) gsz = 1;
@@ -700,7 +682,7 @@ static hipError_t launch_gemm(GemmArgs g, int splits, double a_tile_bytes, doubl
 
 static hipError_t launch_reduce(const float* part, int splits, int64_t n, float scale, float* of,
                                 uint16_t* ob, hipStream_t st) {
-  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
+  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n / 4 + 63) / 64)), dim3(256), 0, st, part,
                      splits, n, scale, of, ob);
   return hipGetLastError();
 }
@@ -775,7 +757,9 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   g.out = Y; g.ldo = N; g.accumulate = 0;
   timer_begin(TK_FWD_GEMM, st);
   hipError_t e;
-  if (M >= QLK_FWD_TALL_MIN_M) {
+  if (!QLK_FWD_TILE_ENGINE && fwd_nf4_supported(K)) {
+    e = launch_fwd_nf4(X, M, w, T, B, r, s, Y, st);
+  } else if (M >= QLK_FWD_TALL_MIN_M) {
     e = launch_gemm<256, 128, kBK, LdBF16K<256, kBK, false>, LdNF4K<128>, LdBF16K<256, kBK, false>,
                     LdBF16K<128, kBK, true>, EPI_BF16>(g, 1, 256.0 * K * 2, 128.0 * K * 0.52, st);
   } else {

@@ -43,6 +43,14 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r);
 hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                             const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
                             void* ws, const FwdPlan& plan, hipStream_t st);
+// Workgroup tile rows walked together by tile_coords (balances the operand
+// footprints each XCD keeps in its L2).
+int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes);
+// Y = X W_hat^T + s T B^T for M > kGemvMaxM (T precomputed, bf16 [M, r]);
+// supported when K / 64 is a multiple of 4 (else the tile engine runs).
+bool fwd_nf4_supported(int64_t K);
+hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
+                          const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
                        hipStream_t st);
