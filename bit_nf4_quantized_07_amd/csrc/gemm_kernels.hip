@@ -518,21 +518,22 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmArgs g) {
 }
 
 // Fixed-order reduction of split partials: out = scale * sum_z part[z].
-// n is a multiple of 4.  A workgroup covers 64 groups of four outputs; its
-// four waves sum the splits z = g, g+4, g+8, ... (wave g, increasing z) with
-// 16-byte loads, and the four wave sums are added in the order g = 0..3.
+// n is a multiple of 4.  A workgroup covers 16 groups of four outputs with
+// 16 lanes per group: lane g sums the splits z = g, g+16, g+32, ... with
+// 16-byte loads, and the 16 lane sums are then added in the order g = 0..15.
+constexpr int kRedCols = 16, kRedLanes = 16;
 __global__ void __launch_bounds__(256)
 k_reduce_splits(const float* __restrict__ part, int splits, int64_t n, float scale,
                 float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16) {
-  __shared__ float4 red[4][64];
-  const int tid = threadIdx.x, col = tid & 63, g = tid >> 6;
+  __shared__ float4 red[kRedLanes][kRedCols];
+  const int tid = threadIdx.x, col = tid % kRedCols, g = tid / kRedCols;
   const int64_t n4 = n / 4;
-  const int64_t i4 = (int64_t)blockIdx.x * 64 + col;
+  const int64_t i4 = (int64_t)blockIdx.x * kRedCols + col;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (i4 < n4) {
     const float4* p = reinterpret_cast<const float4*>(part) + i4;
-#pragma unroll 8
-    for (int z = g; z < splits; z += 4) {
+#pragma unroll 2
+    for (int z = g; z < splits; z += kRedLanes) {
       const float4 v = p[(int64_t)z * n4];
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
@@ -542,7 +543,7 @@ k_reduce_splits(const float* __restrict__ part, int splits, int64_t n, float sca
   if (g != 0 || i4 >= n4) return;
   float4 t = red[0][col];
 #pragma unroll
-  for (int q = 1; q < 4; ++q) {
+  for (int q = 1; q < kRedLanes; ++q) {
     const float4 v = red[q][col];
     t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
   }
@@ -682,7 +683,7 @@ static hipError_t launch_gemm(GemmArgs g, int splits, double a_tile_bytes, doubl
 
 static hipError_t launch_reduce(const float* part, int splits, int64_t n, float scale, float* of,
                                 uint16_t* ob, hipStream_t st) {
-  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n / 4 + 63) / 64)), dim3(256), 0, st, part,
+  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n / 4 + kRedCols - 1) / kRedCols)), dim3(256), 0, st, part,
                      splits, n, scale, of, ob);
   return hipGetLastError();
 }
