@@ -1,0 +1,329 @@
+// Input gradient of the QLoRA linear layer on gfx950:
+//
+//   dX = dY W_hat + s U A,   U = dY B,   s = alpha / r
+//                                   (llm-compass "QLoRA", 方法与公式, the equation,
+//                                    differentiated with respect to x)
+//
+// The contraction runs over n, the weight's row index, so the dequantised
+// weight is needed transposed.  One workgroup computes a 256 x 128 tile of
+// dX (tokens x input features) with four waves; wave w owns input features
+// 32w .. 32w+31 of the tile and all 256 tokens: eight accumulators of
+// v_mfma_f32_32x32x16_bf16, each a 32 (features) x 32 (tokens) block of dX^T.
+//
+//  * dY is staged through LDS exactly like X in the forward kernel: 256 x 64
+//    tiles in four buffers, filled by buffer loads that write LDS directly,
+//    rows of 128 bytes with the 16-byte pieces XOR-swizzled by (row >> 1) & 7.
+//  * The weight tile of a step (64 rows n x 128 features) is decoded once per
+//    workgroup: lane L of wave w decodes the 32 weights of row L in columns
+//    32w .. 32w+31 (16 packed bytes, one 8-bit code, one scale) with the
+//    standalone dequantiser's arithmetic
+//      a_hat = fp32(fp32(Q8[code] * scale) + mean),
+//      w_hat = bf16(fp32(Q4[nibble] * a_hat)),
+//    and writes them to LDS in the weight's own orientation.  The MFMA
+//    operands are then read with LDS transpose reads (ds_read_b64_tr_b16):
+//    eight consecutive rows n of one feature per lane.  The 16-byte pieces of
+//    row n are XOR-swizzled by ((n & 3) << 2) | ((n >> 2) & 3), which keeps
+//    both the decode stores and the transpose reads free of bank conflicts.
+//    Q8[code] is the exact quotient (code - 127) / 127 and the 16 NF4 levels
+//    are fetched from lanes 0..15 of a register with ds_bpermute, so no
+//    table occupies LDS.
+//  * The weight of step k+1 is decoded during step k into the second weight
+//    buffer; raw weight loads run three steps ahead.
+//  * The adapter term s U A is a last contraction over r into the same
+//    accumulators; each lane stores four consecutive features (8 bytes).
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qlk {
+
+constexpr int kDxBM = 256;                 // tokens per tile
+constexpr int kDxWaveK = 32;               // features per wave
+constexpr int kDxBK = 4 * kDxWaveK;        // features per tile
+constexpr int kDxStepN = 64;               // contraction (weight rows) per step
+constexpr int kDyTile = kDxBM * kDxStepN;  // elements per dY buffer
+constexpr int kWTile = kDxStepN * kDxBK;   // elements per weight buffer
+constexpr int kDxUnroll = 4;
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= 11, lgkmcnt <= 8, expcnt not waited on.
+constexpr int kDxWaitEnd = (11 & 0xF) | ((11 >> 4) << 14) | (0x7 << 4) | (8 << 8);
+
+struct DxArgs {
+  const uint16_t* dY;   // [M, N] bf16
+  int M;
+  NF4Weight w;          // N x K
+  const uint16_t* U;    // [M, r] bf16
+  const uint16_t* A;    // [r, K] bf16
+  int r;
+  float s;
+  uint16_t* dX;         // [M, K] bf16
+  int accumulate;
+  int tiles_m, tiles_k, group_m;
+};
+
+struct DxWRegs { uint4 p; uint32_t code; float sc; };
+
+__device__ __forceinline__ int wswz(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
+
+__global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t dy0[kDyTile];
+  __shared__ __attribute__((aligned(16))) uint16_t dy1[kDyTile];
+  __shared__ __attribute__((aligned(16))) uint16_t dy2[kDyTile];
+  __shared__ __attribute__((aligned(16))) uint16_t dy3[kDyTile];
+  __shared__ __attribute__((aligned(16))) uint16_t wt0[kWTile];
+  __shared__ __attribute__((aligned(16))) uint16_t wt1[kWTile];
+  uint16_t* const dyb[4] = {dy0, dy1, dy2, dy3};
+  uint16_t* const wtb[2] = {wt0, wt1};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, h = lane >> 5;
+
+  int tm, tk;
+  tile_coords(blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
+  const int m0 = tm * kDxBM;
+  const int64_t k0 = (int64_t)tk * kDxBK;
+  const int64_t N = g.w.N, K = g.w.K, nkb = K / kBlock;
+  const int nsteps = (int)(N / kDxStepN);
+  const float mean = g.w.mean[0];
+  const float qlev = nf4_level(lane & 15);   // source of the level lookups
+
+  // dY tile loads (as X in the forward kernel).
+  const uint32_t dybytes = (uint32_t)((int64_t)g.M * N * 2);
+  auto swz = [](int row) { return (row >> 1) & 7; };
+  uint32_t yoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + (lane >> 3);
+    const int piece = (lane & 7) ^ swz(row);
+    yoff[i] = m0 + row < g.M ? (uint32_t)(((int64_t)(m0 + row) * N + piece * 8) * 2) : kOOB;
+  }
+  int yrd[4];   // operand reads: row c, logical piece 2t + h
+#pragma unroll
+  for (int t = 0; t < 4; ++t) yrd[t] = c * kDxStepN + (((2 * t + h) ^ swz(c)) * 8);
+  auto load_dy = [&](uint16_t* buf, int kb) {
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(g.dY, dybytes, (uint32_t)kb * (kDxStepN * 2));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * i) * kDxStepN), 16,
+          yoff[i], 0, 0, 0);
+  };
+  auto yfrag = [&](const uint16_t* buf, int i, int t) -> bf16x8_t {
+    return *reinterpret_cast<const bf16x8_t*>(buf + 32 * i * kDxStepN + yrd[t]);
+  };
+
+  // Weight decode: lane L of wave w owns row n = L of the step and features
+  // 32w .. 32w+31 of the tile (16 packed bytes of one 64-block).
+  const int64_t kcol = k0 + 32 * wave;
+  const bool kvalid = kcol < K;
+  const uint32_t pbytes = (uint32_t)(N * (K / 2)), cbytes = (uint32_t)(N * nkb);
+  const uint32_t sbytes = (uint32_t)(((N * nkb + kDQBlock - 1) / kDQBlock) * 4);
+  const uint32_t poff = kvalid ? (uint32_t)((int64_t)lane * (K / 2) + kcol / 2) : kOOB;
+  const uint32_t coff = kvalid ? (uint32_t)((int64_t)lane * nkb + kcol / kBlock) : kOOB;
+  auto load_w = [&](DxWRegs& R, int kb) {   // rows 64 kb .. 64 kb + 63
+    kb = __builtin_amdgcn_readfirstlane(kb);
+    const __amdgpu_buffer_rsrc_t rp = rsrc_at(g.w.packed, pbytes, (uint32_t)kb * kDxStepN * (uint32_t)(K / 2));
+    const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.w.codes, cbytes, (uint32_t)kb * kDxStepN * (uint32_t)nkb);
+    const __amdgpu_buffer_rsrc_t rsc = rsrc_at(g.w.scales, sbytes, 0u);
+    R.p = bload128(rp, poff);
+    R.code = bload8(rc, coff);
+    const uint32_t blk = (uint32_t)kb * kDxStepN * (uint32_t)nkb + coff;
+    R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : (blk / kDQBlock) * 4u));
+  };
+  auto word = [](const DxWRegs& R, int t) -> uint32_t {
+    return t == 0 ? R.p.x : t == 1 ? R.p.y : t == 2 ? R.p.z : R.p.w;
+  };
+  // NF4 level of nibble `nib4 / 4` taken from lane (nib4 / 4) of qlev.
+  auto level = [&](uint32_t nib4, int e) -> float {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(
+        (int)__builtin_amdgcn_perm(0u, nib4, 0x0c0c0c00u | e), __float_as_int(qlev)));
+  };
+  auto hi4 = [](uint32_t w) { return (w >> 2) & 0x3C3C3C3Cu; };
+  auto lo4 = [](uint32_t w) { return (w << 2) & 0x3C3C3C3Cu; };
+  auto absmax = [&](const DxWRegs& R) -> float {
+#pragma clang fp contract(off)
+    const float q = (float)((int)R.code - 127) / 127.0f;
+    const float p = q * R.sc;
+    return p + mean;
+  };
+  // Decoded row: four 16-byte pieces (logical 4w .. 4w+3) of row `lane`.
+  const int wrow = lane;
+  auto wstore = [&](uint16_t* buf, int q, uint4 v) {
+    const int phys = (4 * wave + q) ^ wswz(wrow);
+    *reinterpret_cast<uint4*>(buf + wrow * kDxBK + phys * 8) = v;
+  };
+  // Transpose-read operand: features c of the wave's 32, rows 16t + 8h + 0..7.
+  const int grp = lane >> 4, gi = lane & 15;
+  int wrd[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int n = 16 * t + 8 * (grp >> 1) + 4 * half + (gi >> 2);
+      const int col = 32 * wave + 16 * (grp & 1) + 4 * (gi & 3);
+      const int phys = (col / 8) ^ wswz(n);
+      wrd[t][half] = n * kDxBK + phys * 8 + (col & 7);
+    }
+  auto wfrag = [&](const uint16_t* buf, int t) -> bf16x8_t {
+    const v4s_t lo = lds_read_tr16(buf + wrd[t][0]);
+    const v4s_t hi = lds_read_tr16(buf + wrd[t][1]);
+    typedef short v8s_t __attribute__((ext_vector_type(8)));
+    const v8s_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  auto decode_all = [&](const DxWRegs& R, uint16_t* buf) {
+    const float ah = absmax(R);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t hq = hi4(word(R, q)), lq = lo4(word(R, q));
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(level(hq, e) * ah, level(lq, e) * ah);
+      wstore(buf, q, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  };
+
+  f32x16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+
+  // dY(j) is in buffer j % 4 from its load (step j-3) to step j; the raw
+  // weight of step j in wr[j % 4] from its load (step j-3) to its decode
+  // (step j-1) into weight buffer j % 2, read during step j.
+  DxWRegs wr[4];
+  bf16x8_t b[2][8];   // dY operands
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    load_dy(dyb[j], min(j, nsteps - 1));
+    load_w(wr[j], min(j, nsteps - 1));
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  decode_all(wr[0], wtb[0]);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[0][i] = yfrag(dyb[0], i, 0);
+
+  auto step = [&](auto Pc, int kb) {
+    constexpr int P = decltype(Pc)::value;
+    const DxWRegs& wdec = wr[(P + 1) % 4];
+    DxWRegs& wload = wr[(P + 3) % 4];
+    const uint16_t* ycur = dyb[P];
+    const uint16_t* ynext = dyb[(P + 1) % 4];
+    const uint16_t* wcur = wtb[P % 2];
+    uint16_t* wnext = wtb[(P + 1) % 2];
+
+    load_w(wload, min(kb + 3, nsteps - 1));
+    load_dy(dyb[(P + 3) % 4], min(kb + 3, nsteps - 1));
+    bf16x8_t a[2];
+    a[0] = wfrag(wcur, 0);
+    float ah = 0.0f;
+    float lh[16], ll[16];
+    uint32_t nh[4], nl[4], o[16];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int t = u / 8, i = u % 8;
+      acc[i] = mfma_32x32x16(a[t & 1], b[t & 1][i], acc[i]);
+      if (i == 0 && t < 3) a[(t + 1) & 1] = wfrag(wcur, t + 1);
+      if (t < 3) b[(t + 1) & 1][i] = yfrag(ycur, i, t + 1);
+      else b[0][i] = yfrag(ynext, i, 0);
+      if (u < 16) {
+        if (u % 4 == 0) {
+          nh[u / 4] = hi4(word(wdec, u / 4));
+          nl[u / 4] = lo4(word(wdec, u / 4));
+        }
+        lh[u] = level(nh[u / 4], u % 4);
+        ll[u] = level(nl[u / 4], u % 4);
+      }
+      if (u == 1) ah = absmax(wdec);
+      if (u >= 4 && u < 20) {
+        const int v = u - 4;
+        o[v] = pack_bf16x2(lh[v] * ah, ll[v] * ah);
+      }
+      if (u >= 20 && u < 24) {
+        const int q = u - 20;
+        wstore(wnext, q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Before step kb+1: dY(kb+2) (loaded during step kb-1) in LDS from every
+    // wave (at most this step's 11 global loads outstanding) and this wave's
+    // decoded weight stores done (at most the 8 operand reads of slots
+    // 24..31 outstanding), then the barrier.
+    __builtin_amdgcn_s_waitcnt(kDxWaitEnd);
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int kb = 0; kb < nsteps; kb += kDxUnroll) {
+    step(std::integral_constant<int, 0>(), kb);
+    step(std::integral_constant<int, 1>(), kb + 1);
+    step(std::integral_constant<int, 2>(), kb + 2);
+    step(std::integral_constant<int, 3>(), kb + 3);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
+
+  // Adapter term: acc += (s A)^T U^T over r in steps of 16.
+  const int64_t kf = k0 + 32 * wave + c;   // this lane's feature (operand row)
+  for (int r0 = 0; r0 < g.r; r0 += 16) {
+    const int rr = r0 + 8 * h;
+    uint32_t av[4] = {0u, 0u, 0u, 0u};
+    if (kf < K && rr < g.r) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
+        const float hi = bf16_to_f32(g.A[(int64_t)(rr + 2 * q + 1) * K + kf]) * g.s;
+        av[q] = pack_bf16x2(lo, hi);
+      }
+    }
+    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + 32 * i + c;
+      uint4 uv = make_uint4(0, 0, 0, 0);
+      if (m < g.M && rr < g.r) uv = *reinterpret_cast<const uint4*>(g.U + (int64_t)m * g.r + rr);
+      acc[i] = mfma_32x32x16(afr, __builtin_bit_cast(bf16x8_t, uv), acc[i]);
+    }
+  }
+
+  // Accumulator i: lane holds token m = m0 + 32 i + c and features
+  // 8 (v / 4) + 4 h + (v % 4) of the wave's 32.
+  const int64_t kw0 = k0 + 32 * wave;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + 32 * i + c;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t k = kw0 + 8 * q + 4 * h;
+      if (k >= K) continue;   // K % 64 == 0
+      uint2* dst = reinterpret_cast<uint2*>(g.dX + (int64_t)m * K + k);
+      float v0 = acc[i][4 * q + 0], v1 = acc[i][4 * q + 1], v2 = acc[i][4 * q + 2], v3 = acc[i][4 * q + 3];
+      if (g.accumulate) {
+        const uint2 old = *dst;
+        v0 += bf16_to_f32(old.x & 0xffffu); v1 += bf16_to_f32(old.x >> 16);
+        v2 += bf16_to_f32(old.y & 0xffffu); v3 += bf16_to_f32(old.y >> 16);
+      }
+      *dst = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+    }
+  }
+}
+
+bool dx_nf4_supported(int64_t N) { return N % (kDxStepN * kDxUnroll) == 0; }
+
+hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
+                         const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
+                         hipStream_t st) {
+  if (!dx_nf4_supported(w.N)) return hipErrorInvalidValue;
+  DxArgs g;
+  g.dY = dY; g.M = (int)M; g.w = w; g.U = U; g.A = A; g.r = r; g.s = s; g.dX = dX;
+  g.accumulate = accumulate ? 1 : 0;
+  g.tiles_m = (int)((M + kDxBM - 1) / kDxBM);
+  g.tiles_k = (int)((w.K + kDxBK - 1) / kDxBK);
+  g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2, (double)kDxBK * w.N * 0.52);
+  hipLaunchKernelGGL(k_dx_nf4, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace qlk

@@ -592,6 +592,11 @@ constexpr int kBK = 64;
 #define QLK_FWD_TILE_ENGINE 0
 #endif
 
+// 1: dX runs on the generic tile engine; 0: on the dedicated dX kernel.
+#ifndef QLK_DX_TILE_ENGINE
+#define QLK_DX_TILE_ENGINE 0
+#endif
+
 // Token counts at or above this use 256-row forward tiles (fewer decodes of
 // each weight tile per MFMA flop).  Measured on MI355X the 128-row tile is
 // faster at every size tried, so the tall tile is off by default.
@@ -801,7 +806,9 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     g.c1_len = (int)N; g.c1_split = (int)N; g.c2_len = r;
     g.out = dX; g.ldo = K; g.accumulate = accumulate_dx ? 1 : 0;
     timer_begin(TK_DX_GEMM, st);
-    const hipError_t e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
+    const hipError_t e = (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N))
+        ? launch_dx_nf4(dY, M, w, U, A, r, s, dX, accumulate_dx, st)
+        : launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
                                      LdNF4T<QLK_DX_BN>, LdBF16K<QLK_DX_BM, kBK, false>,
                                      LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
         g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 0.52, st);

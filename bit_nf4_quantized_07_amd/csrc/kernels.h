@@ -51,6 +51,11 @@ int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes
 bool fwd_nf4_supported(int64_t K);
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
+// dX = dY W_hat (+ s U A) for N a multiple of 256 (else the tile engine runs).
+bool dx_nf4_supported(int64_t N);
+hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
+                         const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
+                         hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
                        hipStream_t st);

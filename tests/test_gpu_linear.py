@@ -53,6 +53,10 @@ CASES = [
     (130, 384, 320, 64, 128.0),   # two M tiles, ragged tail
     (257, 520, 704, 136, 272.0),  # r > 128: two adapter tiles
     (384, 1024, 1024, 16, 32.0),
+    # shapes that take the dedicated forward / dX kernels with ragged edges
+    (520, 264, 768, 72, 144.0),   # forward kernel: ragged M and N, r = 72
+    (300, 512, 704, 40, 80.0),    # dX kernel: ragged M, K % 128 == 64
+    (272, 768, 1280, 136, 272.0), # both kernels, r = 136 (nine adapter steps)
 ]
 
 
@@ -112,9 +116,11 @@ def test_special_cases():
         assert np.all(got["dB"] == 0) and np.all(got["T"] == 0)
 
 
-def test_identity_input_reads_weight_layout():
-    """X = I (M = K): Y = W_hat^T + s (B A)^T, checked element-wise."""
-    K = N = 128
+@pytest.mark.parametrize("K", [128, 256])
+def test_identity_input_reads_weight_layout(K):
+    """X = I (M = K): Y = W_hat^T + s (B A)^T, checked element-wise.  K = 256
+    takes the dedicated forward kernel (permuted contraction order)."""
+    N = K
     case = wl.linear_case(6, K, N, K, 16, 32.0)
     eye = np.eye(K, dtype=np.float32)
     case["X"] = wl.round_to_bf16_bits(eye)
