@@ -1,0 +1,114 @@
+// Rank-r projections of the adapter for more than 16 tokens:
+//
+//   T = X A^T   (forward, and the backward when T was not saved)
+//   U = dY B    (backward)             (llm-compass "QLoRA", 方法与公式, the
+//                                       equation and its derivative)
+//
+// out[m][j] = sum_c S[m][c] W(j, c), with S = X or dY ([M, C], bf16) and
+// W(j, c) = A[j][c] (contraction contiguous) or B[c][j] (transposed).
+// One workgroup owns 16 rows of S (or 8, with the MFMA's other 8 rows zero,
+// when 16-row tiles would leave CUs idle) and all r outputs; its NW waves take every
+// NW-th 32-wide slice of the contraction (v_mfma_f32_16x16x32_bf16, operands
+// loaded straight from memory, S read once in total; many waves per
+// workgroup keep enough loads in flight to stream S), and the NW partial sums
+// are added through LDS in a fixed order, so the bf16 result is written by
+// the same kernel and is bit-reproducible.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace qlk {
+
+constexpr int kRankRows = 16;
+constexpr int kRankMaxTiles = 16;   // r <= 256
+
+template <bool WT, int RT, int NW>
+__global__ void __launch_bounds__(NW * 64)
+k_rank16(const uint16_t* __restrict__ S, int M, int64_t C, const uint16_t* __restrict__ W, int r,
+         int rows, uint16_t* __restrict__ out) {
+  __shared__ float red[NW - 1][kRankRows][RT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int m0 = blockIdx.x * rows;
+  const int m = m0 + row;
+  const bool mvalid = row < rows && m < M;
+  const int64_t nsteps = (C + 31) / 32;
+  const uint16_t* srow = S + (int64_t)(mvalid ? m : 0) * C;
+
+  f32x4_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll 8
+  for (int64_t ks = wave; ks < nsteps; ks += NW) {
+    const int64_t k = ks * 32 + 8 * grp;   // this lane's 8 contraction indices
+    const bool kvalid = k < C;             // C % 8 == 0: a group of 8 is all in or all out
+    uint4 av = make_uint4(0, 0, 0, 0);
+    if (mvalid && kvalid) av = *reinterpret_cast<const uint4*>(srow + k);
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int j = 16 * t + row;
+      uint4 bv = make_uint4(0, 0, 0, 0);
+      if (j < r && kvalid) {
+        if (!WT) {
+          bv = *reinterpret_cast<const uint4*>(W + (int64_t)j * C + k);
+        } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            w[q] = (uint32_t)W[(k + 2 * q) * r + j] | ((uint32_t)W[(k + 2 * q + 1) * r + j] << 16);
+          bv = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+      acc[t] = mfma_16x16x32(a, __builtin_bit_cast(bf16x8_t, bv), acc[t]);
+    }
+  }
+
+  // acc[t][v]: row 4 grp + v, column 16 t + row of the tile.  Waves 1..NW-1
+  // hand their sums to wave 0, which adds them in the order 0, 1, ..., NW-1.
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave - 1][4 * grp + v][16 * t + row] = acc[t][v];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int j = 16 * t + row;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int mm = m0 + 4 * grp + v;
+      float sum = acc[t][v];
+#pragma unroll
+      for (int q = 0; q < NW - 1; ++q) sum += red[q][4 * grp + v][j];
+      if (4 * grp + v < rows && mm < M && j < r) out[(int64_t)mm * r + j] = f32_to_bf16(sum);
+    }
+  }
+}
+
+template <bool WT>
+static hipError_t rank16_dispatch(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, int r,
+                                  uint16_t* out, hipStream_t st) {
+  // 8 rows per workgroup when 16 would give fewer workgroups than CUs
+  const int rows = (M + kRankRows - 1) / kRankRows < 256 ? 8 : kRankRows;
+  const dim3 grid((unsigned)((M + rows - 1) / rows));
+  const int tiles = (r + 15) / 16;
+  // More waves (loads in flight) for small r; the LDS of the final sum bounds NW * r.
+  if (tiles <= 1) hipLaunchKernelGGL((k_rank16<WT, 1, 16>), grid, dim3(1024), 0, st, S, (int)M, C, W, r, rows, out);
+  else if (tiles <= 2) hipLaunchKernelGGL((k_rank16<WT, 2, 16>), grid, dim3(1024), 0, st, S, (int)M, C, W, r, rows, out);
+  else if (tiles <= 4) hipLaunchKernelGGL((k_rank16<WT, 4, 8>), grid, dim3(512), 0, st, S, (int)M, C, W, r, rows, out);
+  else if (tiles <= 8) hipLaunchKernelGGL((k_rank16<WT, 8, 4>), grid, dim3(256), 0, st, S, (int)M, C, W, r, rows, out);
+  else hipLaunchKernelGGL((k_rank16<WT, kRankMaxTiles, 4>), grid, dim3(256), 0, st, S, (int)M, C, W, r, rows, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, bool transposed,
+                         int r, uint16_t* out, hipStream_t st) {
+  return transposed ? rank16_dispatch<true>(S, M, C, W, r, out, st)
+                    : rank16_dispatch<false>(S, M, C, W, r, out, st);
+}
+
+}  // namespace qlk

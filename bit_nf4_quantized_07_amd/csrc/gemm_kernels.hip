@@ -630,9 +630,7 @@ FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r) {
   size_t off = align256((size_t)M * r * 2);
   p.off_part = off;
   if (!p.gemv) {
-    const int64_t blocks = (int64_t)ceil_div(M, 128) * ceil_div(r, r_tile(r));
-    p.t_splits = actual_splits(K, choose_splits(blocks, K));
-    off += align256((size_t)p.t_splits * M * r * 4);
+    p.t_splits = 1;   // T in one pass (no partial sums)
   } else {
     p.t_splits = kTSplits;
     off += align256((size_t)kTSplits * M * r * 4);
@@ -647,13 +645,11 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r) {
   p.off_T = align256((size_t)M * r * 2);
   p.off_part = p.off_T + align256((size_t)M * r * 2);
   const int64_t mt = ceil_div(M, 128), rt = ceil_div(r, r_tile(r));
-  p.t_splits = actual_splits(K, choose_splits(mt * rt, K));
-  p.u_splits = actual_splits(N, choose_splits(mt * rt, N));
+  p.t_splits = 1;   // T and U in one pass (no partial sums)
+  p.u_splits = 1;
   p.m_splits_a = actual_splits(M, choose_splits((int64_t)ceil_div(r, r_tile(r)) * ceil_div(K, 128), M));
   p.m_splits_b = actual_splits(M, choose_splits((int64_t)ceil_div(N, 128) * rt, M));
-  size_t part = (size_t)p.t_splits * M * r;
-  part = part > (size_t)p.u_splits * M * r ? part : (size_t)p.u_splits * M * r;
-  part = part > (size_t)p.m_splits_a * r * K ? part : (size_t)p.m_splits_a * r * K;
+  size_t part = (size_t)p.m_splits_a * r * K;
   part = part > (size_t)p.m_splits_b * N * r ? part : (size_t)p.m_splits_b * N * r;
   p.bytes = p.off_part + align256(part * 4);
   return p;
@@ -736,11 +732,10 @@ static hipError_t skinny(int rt, const Operand& a, const Operand& b, int P, int 
 #define QLK_TRY(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
 
 // T = X A^T (bf16 [M, r]) through split partials + fixed-order reduction.
+// T = X A^T (bf16 [M, r]) in one pass over X.
 static hipError_t compute_T(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
-                            int splits, float* part, uint16_t* T, hipStream_t st) {
-  QLK_TRY((skinny<0, 0, false>(r_tile(r), opnd(X, K, (int)M, M), opnd(A, K, r, r), (int)M, r, K, splits,
-                               part, st)));
-  return launch_reduce(part, actual_splits(K, splits), M * r, 1.0f, nullptr, T, st);
+                            uint16_t* T, hipStream_t st) {
+  return launch_rank16(X, M, K, A, false, r, T, st);
 }
 
 hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
@@ -751,7 +746,7 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   uint16_t* T = T_out ? T_out : reinterpret_cast<uint16_t*>(base + plan.off_T);
   float* part = reinterpret_cast<float*>(base + plan.off_part);
   if (plan.gemv) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st);
-  QLK_TRY(compute_T(X, M, K, A, r, plan.t_splits, part, T, st));
+  QLK_TRY(compute_T(X, M, K, A, r, T, st));
   GemmArgs g{};
   g.a1 = opnd(X, K, (int)M, M);
   g.b1 = opnd(nullptr, 0, (int)N, 0);
@@ -787,13 +782,11 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
   const int rt = r_tile(r);
   if (!T) {
     uint16_t* Tw = reinterpret_cast<uint16_t*>(base + plan.off_T);
-    QLK_TRY(compute_T(X, M, K, A, r, plan.t_splits, part, Tw, st));
+    QLK_TRY(compute_T(X, M, K, A, r, Tw, st));
     T = Tw;
   }
-  // U = dY B: rows m (dY, contraction n contiguous), cols j (B^T: transposed load of B [N, r]).
-  QLK_TRY((skinny<0, 1, false>(rt, opnd(dY, N, (int)M, M), opnd(B, r, r, N), (int)M, r, N, plan.u_splits,
-                               part, st)));
-  QLK_TRY(launch_reduce(part, actual_splits(N, plan.u_splits), M * r, 1.0f, nullptr, U, st));
+  // U = dY B (B [N, r] read transposed), in one pass over dY.
+  QLK_TRY(launch_rank16(dY, M, N, B, true, r, U, st));
   // dX = dY W_hat + s U A.
   if (dX) {
     GemmArgs g{};

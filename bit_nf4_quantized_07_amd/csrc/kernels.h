@@ -56,6 +56,9 @@ bool dx_nf4_supported(int64_t N);
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
                          const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
                          hipStream_t st);
+// out[M, r] (bf16) = S[M, C] W^T with W = [r, C] or, transposed, [C, r].
+hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, bool transposed,
+                         int r, uint16_t* out, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
                        hipStream_t st);
