@@ -19,6 +19,8 @@
 //     scales are fetched 16 blocks at a time.  The prologue sums the T
 //     partials in a fixed order into LDS; workgroup 0 also writes T (bf16) for
 //     the backward.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -195,6 +197,197 @@ k_gemv_nf4(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __re
   }
 }
 
+// Streaming variant of the small-M forward (taken when K / 64 is a multiple
+// of 16).  Same workgroup shape and arithmetic as k_gemv_nf4, but the packed
+// weight goes through LDS: per super-step of 4 blocks, a wave fetches its 64
+// rows x 128 bytes with 8 buffer loads that write LDS directly (8 rows x 128
+// contiguous bytes per load instead of 32 rows x 32 bytes), one super-step
+// ahead into the other of two LDS stages, and reads the MFMA operands back
+// from LDS.  The 16-byte pieces of
+// row i are XOR-swizzled by (i >> 1) & 7 so that the operand reads are
+// conflict-free.  Each wave owns its LDS region, so no barrier is needed in
+// the loop.  The activations of a super-step are loaded one super-step ahead
+// into registers; the 8-bit codes (4 per row) and the scale come with them.
+constexpr int kGemvSS = 4;                      // blocks per super-step
+constexpr int kGemvStage = 64 * 128;            // bytes per wave and stage
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= 28, expcnt and lgkmcnt not waited on.
+constexpr int kGemvWaitVm28 = (28 & 0xF) | ((28 >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+
+struct GemvSSRegs {
+  uint4 x[kGemvSS][4];    // activations: block b, MFMA step t
+  uint32_t code[2];       // 4 codes of row group g (byte b = block b)
+  float sc[2];
+};
+
+template <int MAXM>
+__global__ void __launch_bounds__(256)
+k_gemv_dma(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __restrict__ Tpart,
+           const uint16_t* __restrict__ B, int r, float s, uint16_t* __restrict__ Y,
+           uint16_t* __restrict__ T_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[4 * kGemvStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[4 * kGemvStage];
+  __shared__ uint32_t lut[256];   // byte -> (level of high nibble, level of low nibble), bf16
+  __shared__ float q8[256];
+  __shared__ uint16_t tl[kGemvMaxM * 256];   // T, bf16
+  const int tid = threadIdx.x;
+  lut[tid] = pack_bf16x2(nf4_level(tid >> 4), nf4_level(tid & 15));
+  q8[tid] = dq_level(tid);
+  for (int i = tid; i < M * r; i += 256) {
+    float t = 0.0f;
+    for (int z = 0; z < kTSplits; ++z) t += Tpart[(int64_t)z * M * r + i];
+    tl[i] = f32_to_bf16(t);
+    if (blockIdx.x == 0) T_out[i] = tl[i];
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int64_t N = w.N, K = w.K, nkb = K / kBlock;
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  int64_t nrow[2];
+  bool nvalid[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    nrow[g] = n0 + 32 * g + c;
+    nvalid[g] = nrow[g] < N;
+  }
+  const bool mvalid = c < M;
+  const float mean = w.mean[0];
+  const int64_t q = nkb / 4;                 // blocks per wave (a multiple of 4)
+  const int64_t kb0 = wave * q;
+  const int nss = (int)(q / kGemvSS);
+  uint8_t* const my0 = st0 + wave * kGemvStage;
+  uint8_t* const my1 = st1 + wave * kGemvStage;
+
+  // Weight loads: load i fills rows 8i .. 8i+7 of the wave's 64; lane L lands
+  // at 16 L: row 8i + L/8, physical piece L%8 = logical piece (L%8) ^ swz.
+  auto swz = [](int row) { return (row >> 1) & 7; };
+  const uint32_t pbytes = (uint32_t)(N * (K / 2));
+  uint32_t poff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    const int piece = (lane & 7) ^ swz(row);
+    poff[i] = n0 + row < N ? (uint32_t)((n0 + row) * (K / 2) + piece * 16) : kOOB;
+  }
+  auto load_w = [&](uint8_t* buf, int ss) {
+    const uint32_t shift = (uint32_t)((kb0 + (int64_t)ss * kGemvSS) * 32);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(w.packed, pbytes, shift);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, poff[i], 0, 0, 0);
+  };
+  // Operand of block b, half h, group g: row 32 g + c, logical piece 2 b + h.
+  auto wfrag = [&](const uint8_t* buf, int g, int b) -> uint4 {
+    const int row = 32 * g + c;
+    return *reinterpret_cast<const uint4*>(buf + row * 128 + (((2 * b + h) ^ swz(row)) * 16));
+  };
+  const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
+  const uint32_t xoff = mvalid ? (uint32_t)(((int64_t)c * K + 32 * h) * 2) : kOOB;
+  const uint32_t cbytes = (uint32_t)(N * nkb);
+  const uint32_t sbytes = (uint32_t)(((N * nkb + kDQBlock - 1) / kDQBlock) * 4);
+  auto load_r = [&](GemvSSRegs& R, int ss) {
+    const int64_t kb = kb0 + (int64_t)ss * kGemvSS;
+    const __amdgpu_buffer_rsrc_t rx = rsrc_at(X, xbytes, (uint32_t)(kb * kBlock * 2));
+#pragma unroll
+    for (int b = 0; b < kGemvSS; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) R.x[b][t] = bload128(rx, xoff == kOOB ? kOOB : xoff + (uint32_t)(b * 128 + t * 16));
+    const __amdgpu_buffer_rsrc_t rc = rsrc_at(w.codes, cbytes, 0u);
+    const __amdgpu_buffer_rsrc_t rsc = rsrc_at(w.scales, sbytes, 0u);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t blk = nvalid[g] ? (uint32_t)(nrow[g] * nkb + kb) : kOOB;
+      R.code[g] = bload32(rc, blk);
+      R.sc[g] = __uint_as_float(bload32(rsc, blk == kOOB ? kOOB : (blk / kDQBlock) * 4u));
+    }
+  };
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[g][v] = 0.0f;
+
+  auto compute = [&](const uint8_t* buf, const GemvSSRegs& R) {
+#pragma unroll
+    for (int b = 0; b < kGemvSS; ++b)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float ah = absmax_decode_tab((int)((R.code[g] >> (8 * b)) & 0xffu), R.sc[g], mean, q8);
+        const uint4 pv = wfrag(buf, g, b);
+        const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
+        f32x16_t part;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[v] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = lut[(pw[t] >> (8 * e)) & 0xffu];
+          part = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, R.x[b][t]),
+                               __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3])), part);
+        }
+#pragma unroll
+        for (int v = 0; v < (MAXM > 16 ? 16 : 8); ++v) acc[g][v] += ah * part[v];
+      }
+  };
+
+  // Super-step ss uses LDS stage ss % 2 and register set ss % 2.  At its
+  // start the loads of ss+1 are issued (8 weight, 16 activation, 4 code and
+  // scale loads), after which waiting for at most 28 outstanding loads means
+  // that everything of ss has arrived.
+  GemvSSRegs rg[2];
+  load_w(my0, 0);
+  load_r(rg[0], 0);
+  auto sstep = [&](auto Pc, int ss) {
+    constexpr int P = decltype(Pc)::value;
+    uint8_t* cur = P == 0 ? my0 : my1;
+    uint8_t* nxt = P == 0 ? my1 : my0;
+    if (ss + 1 < nss) {
+      load_w(nxt, ss + 1);
+      load_r(rg[(P + 1) % 2], ss + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kGemvWaitVm28);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, rg[P]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int ss = 0; ss < nss; ss += 2) {
+    sstep(std::integral_constant<int, 0>(), ss);
+    if (ss + 1 < nss) sstep(std::integral_constant<int, 1>(), ss + 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // Reduce the four K-quarters in a fixed order (through this wave's own
+  // stage-0 region), add the adapter term, store.
+  float* red = reinterpret_cast<float*>(st0);   // [wave][g][v][lane]
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[((wave * 2 + g) * 16 + v) * 64 + lane] = acc[g][v];
+  __syncthreads();
+  const int g = wave & 1;
+  const int vbeg = (wave >> 1) * 8;
+  if (!nvalid[g]) return;
+  const int64_t n = nrow[g];
+  for (int v = vbeg; v < vbeg + 8; ++v) {
+    const int m = (v >> 2) * 8 + 4 * h + (v & 3);
+    if (m < M) {
+      float base = red[((0 * 2 + g) * 16 + v) * 64 + lane];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) base += red[((ww * 2 + g) * 16 + v) * 64 + lane];
+      float l = 0.0f;
+      for (int j = 0; j < r; ++j) l += bf16_to_f32(tl[m * r + j]) * bf16_to_f32(B[n * r + j]);
+      Y[(int64_t)m * N + n] = f32_to_bf16(base + s * l);
+    }
+  }
+}
+
 // Partial sums of T = X A^T for M <= 16 over kTSplits slices of K: workgroup
 // (jt, z) covers adapter rows 32*jt .. +31 and K slice z; its four waves take
 // a quarter of the slice each and are reduced through LDS in a fixed order.
@@ -251,7 +444,10 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const u
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((w.N + 63) / 64);
   timer_begin(TK_GEMV, st);
-  hipLaunchKernelGGL(k_gemv_nf4<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
+  if ((w.K / kBlock) % (4 * kGemvSS) == 0)
+    hipLaunchKernelGGL(k_gemv_dma<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
+  else
+    hipLaunchKernelGGL(k_gemv_nf4<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
   timer_end(TK_GEMV, st);
   return hipGetLastError();
 }
