@@ -20,6 +20,7 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                    MFMA peak
   gemv             the small-M forward (W0 28672x8192, M = 1, 4, 16): bytes
                    the GEMV kernel must move over its average duration vs HBM
+  standalone       the load-time kernels (quantize, double quant, dequant) in GB/s
   cpu_baseline     the CPU oracle timed on the host cores on a bounded sample
 """
 from __future__ import annotations
@@ -48,12 +49,24 @@ def err(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(files=None) -> str:
+    """Hash of kernel sources: all of csrc/, or the named .hip files plus every
+    header (the sources one kernel is compiled from)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    names = sorted(os.listdir(CSRC)) if files is None else sorted(
+        set(files) | {f for f in os.listdir(CSRC) if f.endswith(".h")})
+    for f in names:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+# bench timer name -> (kernel symbol in profiler output, source file, workload)
+PROFILED = {
+    "dx_gemm": ("k_dx_nf4", "dx_kernels.hip", "c2_linear_4096"),
+    "fwd_gemm": ("k_fwd_nf4", "fwd_kernels.hip", "c2_linear_4096"),
+    "gemv": ("k_gemv_dma", "gemv_kernels.hip", "c4_gemv_28672x8192"),
+}
 
 
 class HipEvents:
@@ -90,6 +103,23 @@ def linear_flops(M, N, K, r):
     return 4.0 * M * N * K + 6.0 * M * r * (N + K)
 
 
+def weight_bytes(N, K):
+    """Packed nibbles, 8-bit codes, second-level scales and the mean."""
+    nb = N * K // 64
+    return N * K // 2 + nb + 4 * ((nb + 255) // 256) + 4
+
+
+def algorithmic_bytes(kernel: str, M=None) -> int:
+    """Bytes one launch must move at least, each operand once: the GEMMs on the
+    2048 x 4096 x 4096 layer (r = 16), the small-M forward on 28672 x 8192."""
+    if kernel == "gemv":
+        return gemv_bytes(M, 28672, 8192, 16)
+    M, N, K, r = 2048, 4096, 4096, 16
+    if kernel == "fwd_gemm":    # X, weight, T, B -> Y
+        return 2 * M * K + weight_bytes(N, K) + 2 * M * r + 2 * N * r + 2 * M * N
+    return 2 * M * N + weight_bytes(N, K) + 2 * M * r + 2 * r * K + 2 * M * K   # dY, weight, U, A -> dX
+
+
 def gemv_bytes(M, N, K, r):
     """Bytes the small-M forward kernel must move: packed nibbles, 8-bit codes,
     second-level scales, the mean, X, the adapter B and T = X A^T, and Y."""
@@ -106,10 +136,10 @@ def traffic_for(kernel: str, launch_units: dict):
             t = json.load(fh)
     except Exception:
         return None
-    if t.get("source_hash") != source_hash():
-        return None
     k = t.get("kernels", {}).get(kernel)
     if not k or k.get("workload") != launch_units.get("workload"):
+        return None
+    if k.get("source_hash") != source_hash([PROFILED[kernel][1]]):
         return None
     return k.get("hbm_bytes_per_launch")
 
@@ -191,7 +221,8 @@ def run_linear(args, q, torch, wl, lib, ev):
     for k, (a, b) in evs.items():
         d = [ev.elapsed_ms(a[i], b[i]) for i in range(K)]
         avg = float(np.mean(d))
-        kern[names[k]] = dict(avg_us=avg * 1e3, min_us=float(np.min(d)) * 1e3,
+        kern[names[k]] = dict(avg_us=avg * 1e3, median_us=float(np.median(d)) * 1e3,
+                              min_us=float(np.min(d)) * 1e3,
                               flops_per_launch=kflops[k],
                               tflops=kflops[k] / (avg * 1e-3) / 1e12)
         ev.destroy(a + b)
@@ -245,10 +276,72 @@ def run_gemv(args, q, torch, wl, lib, ev):
         avg = float(np.mean(d)) * 1e-3
         nbytes = gemv_bytes(M, lin.N, lin.K, lin.r)
         gbps = nbytes / avg / 1e9
-        out[f"M{M}"] = dict(kernel_avg_us=round(avg * 1e6, 2), bytes=nbytes,
+        out[f"M{M}"] = dict(kernel_avg_us=round(avg * 1e6, 2),
+                            kernel_median_us=round(float(np.median(d)) * 1e3, 2),
+                            kernel_min_us=round(float(np.min(d)) * 1e3, 2), bytes=nbytes,
                             GBps=round(gbps, 1), frac_hbm=round(gbps / PEAK_HBM_GBPS, 4),
                             call_us=round((t1 - t0) / n * 1e6, 2))
+        if M == 1:
+            out["M1"]["traffic"] = traffic_for("gemv", dict(workload=cfg.name))
     return dict(workload=cfg.name, N=lin.N, K=lin.K, r=lin.r, peak_GBps=PEAK_HBM_GBPS, **out)
+
+
+def run_standalone(args, q, torch, lib, ev):
+    """The load-time kernels on the default workload's weight shape (4096 x
+    4096), event-timed per call over 8 rotated weight sets (more than the
+    last-level cache holds), in GB/s of the bytes each must move:
+      nf4_quantize   fp32 in, packed nibbles + fp32 absmax out   (4 + 1/2 + 4/64 B/weight)
+      double_quant   fp32 absmax in, 8-bit codes + scales + mean out
+      nf4_dequant    packed + codes + scales in, bf16 out         (1/2 + 1/64 + 2 B/weight, + scales)"""
+    N = K = 4096
+    nb, nsets, n = N * K // 64, 8, max(args.steps * 3, 60)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    sets = []
+    for _ in range(nsets):
+        W = torch.randn(N, K, generator=g, device="cuda", dtype=torch.float32) * 0.02
+        qw = q.quantize(W)
+        absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
+        sets.append(dict(W=W, qw=qw, absmax=absmax,
+                         packed=torch.empty(N * K // 2, dtype=torch.uint8, device="cuda"),
+                         out=torch.empty(N, K, dtype=torch.bfloat16, device="cuda")))
+    stream = torch.cuda.current_stream().cuda_stream
+    ptr = lambda t: t.data_ptr()
+    nsc = (nb + 255) // 256
+
+    def quant(d):
+        return lib.nf4_quantize(ptr(d["W"]), N, K, 64, ptr(d["packed"]), ptr(d["absmax"]), stream)
+
+    def dq(d):
+        w = d["qw"]
+        return lib.double_quant(ptr(d["absmax"]), nb, 256, ptr(w.codes), ptr(w.scales),
+                                ptr(w.mean), stream)
+
+    def deq(d):
+        w = d["qw"]
+        return lib.nf4_dequant(ptr(w.packed), ptr(w.codes), ptr(w.scales), ptr(w.mean), N, K,
+                               64, 256, ptr(d["out"]), stream)
+    calls = [("nf4_quantize", quant, N * K * 4 + N * K // 2 + nb * 4),
+             ("double_quant", dq, nb * 4 + nb + nsc * 4 + 4),
+             ("nf4_dequant", deq, N * K // 2 + nb + nsc * 4 + 4 + N * K * 2)]
+    out = dict(shape=[N, K], sets=nsets, calls=n)
+    for name, fn, nbytes in calls:
+        for i in range(10):
+            assert fn(sets[i % nsets]) == 0, name
+        torch.cuda.synchronize()
+        a, b = ev.create(n), ev.create(n)
+        for i in range(n):
+            ev.hip.hipEventRecord(ctypes.c_void_p(a[i]), ctypes.c_void_p(stream))
+            assert fn(sets[i % nsets]) == 0, name
+            ev.hip.hipEventRecord(ctypes.c_void_p(b[i]), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        d = [ev.elapsed_ms(a[i], b[i]) for i in range(n)]
+        ev.destroy(a + b)
+        med = float(np.median(d)) * 1e-3
+        out[name] = dict(median_us=round(med * 1e6, 2), min_us=round(float(np.min(d)) * 1e3, 2),
+                         bytes=nbytes, GBps=round(nbytes / med / 1e9, 1),
+                         frac_hbm=round(nbytes / med / 1e9 / PEAK_HBM_GBPS, 4))
+    return out
 
 
 def run_cpu_baseline(budget_s: float):
@@ -265,9 +358,12 @@ def run_cpu_baseline(budget_s: float):
     cfg = wl.workloads()["c2_linear_4096"]
     lin = cfg.linears[0]
     W = wl.weight(0, cfg.cfg_id, 0, lin)
-    c4, am = oracle.quantize_nf4(W, 64)                       # load time, not timed
+    phases = dict(quantize_dq=0.0, dequant=0.0, forward=0.0, backward=0.0)
+    t0 = time.perf_counter()                                  # load time: reported, not in value
+    c4, am = oracle.quantize_nf4(W, 64)
     packed = oracle.pack_nibbles(c4)
     c8, sc, mu = oracle.double_quant(am, 256)
+    phases["quantize_dq"] = time.perf_counter() - t0
     A, B = wl.adapters(0, cfg.cfg_id, 0, lin)
     Af, Bf = oracle.bf16_bits_to_f64(A), oracle.bf16_bits_to_f64(B)
     done_flops, spent, Ms = 0.0, 0.0, 128
@@ -278,18 +374,46 @@ def run_cpu_baseline(budget_s: float):
         t0 = time.perf_counter()
         _, wb = oracle.dequant_nf4(packed, c8, sc, mu, lin.N, lin.K)
         Wh = oracle.bf16_bits_to_f64(wb)
+        t1 = time.perf_counter()
         oracle.forward(X, Wh, Af, Bf, lin.alpha, lin.r)
+        t2 = time.perf_counter()
         oracle.backward(dY, X, Wh, Af, Bf, lin.alpha, lin.r)
-        dt = time.perf_counter() - t0
-        spent += dt
+        t3 = time.perf_counter()
+        phases["dequant"] += t1 - t0
+        phases["forward"] += t2 - t1
+        phases["backward"] += t3 - t2
+        spent += t3 - t0
         done_flops += linear_flops(Ms, lin.N, lin.K, lin.r)
-        rounds.append((Ms, round(dt, 3)))
+        rounds.append((Ms, round(t3 - t0, 3)))
         Ms *= 2
     value = done_flops / spent / 1e12
     return dict(value=round(value, 5), unit="TFLOP/s", cores=cores, kind="oracle",
                 sample=f"{cfg.name}: full-weight dequant + fp64 fwd+bwd for token counts "
                        f"{[m for m, _ in rounds]} of {cfg.M} (seconds {[t for _, t in rounds]})",
-                seconds=round(spent, 2))
+                seconds=round(spent, 2),
+                phase_seconds={k: round(v, 3) for k, v in phases.items()},
+                host=dict(cpu_count=os.cpu_count(), cpu_model=cpu_model(),
+                          blas=blas_backend()))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_backend() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        return ",".join(sorted({f"{i.get('internal_api')}:{i.get('num_threads')}"
+                                for i in threadpool_info()})) or "unknown"
+    except Exception:
+        return "unknown"
 
 
 def copy_calibration(torch):
@@ -304,6 +428,167 @@ def copy_calibration(torch):
     err(f"copy calibration: 3 x {4 * n} bytes read and written")
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 runs behind profiles/ and their summaries
+# ---------------------------------------------------------------------------
+
+COUNTER_SETS = {
+    "p1": "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+          "SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT",
+    "p2": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
+          "SQ_ACTIVE_INST_VMEM SQ_INST_CYCLES_VMEM_RD SQ_INSTS_LDS SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE",
+    "f": "FETCH_SIZE",
+    "w": "WRITE_SIZE",
+}
+SHORT_RUN = "--steps 3 --warmup 1 --no-cpu-baseline --no-standalone"
+
+
+def profile_commands(out: str) -> dict:
+    """The rocprofv3 runs (from /tmp, program after --) whose output
+    --summarize reads; `out` is the output folder."""
+    me = os.path.abspath(__file__)
+    cmds = {"kt": f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/kt -o kt "
+                  f"-- python3 {me} --no-cpu-baseline"}
+    for k, ctr in COUNTER_SETS.items():
+        extra = " --copy-calib" if k in ("f", "w") else ""
+        cmds[k] = (f"rocprofv3 --pmc {ctr} --output-format csv -d {out}/{k} -o {k} "
+                   f"-- python3 {me} {SHORT_RUN}{extra}")
+    return cmds
+
+
+def _csv(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _dispatch_counters(path, symbol):
+    """{dispatch id: {counter: value}} for the dispatches of one kernel, in order."""
+    out = {}
+    for r in _csv(path):
+        if symbol in r["Kernel_Name"]:
+            d = out.setdefault(int(r["Dispatch_Id"]), dict(_ns=int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [out[k] for k in sorted(out)]
+
+
+def _groups(symbol, ds):
+    """The small-M forward runs M = 1, 4, 16 in that order with equal call
+    counts; every other kernel is one group."""
+    if symbol != PROFILED["gemv"][0]:
+        return {"": ds}
+    n = len(ds) // 3
+    return {" M=1": ds[:n], " M=4": ds[n:2 * n], " M=16": ds[2 * n:3 * n]}
+
+
+def _med(ds, key):
+    return float(np.median([d.get(key, 0.0) for d in ds])) if ds else float("nan")
+
+
+def summarize(out: str):
+    """Write profiles/*.md and profiles/traffic.json from the runs of
+    profile_commands(out)."""
+    prof = os.path.join(ROOT, "profiles")
+    cmds = {k: "cd /tmp && " + v.replace(ROOT, "<repo>") for k, v in profile_commands(out).items()}
+    cmds = {k: v.replace(out.replace(ROOT, "<repo>"), "<out>").replace(out, "<out>")
+            for k, v in cmds.items()}
+    head = ("Commands run from `/tmp` on one MI355X; `<repo>` is the repository path and `<out>` "
+            "the output folder.\n")
+    # kernel trace
+    rows = _csv(os.path.join(out, "kt", "kt_kernel_stats.csv"))
+    md = ["# Kernel statistics of the default bench run", "",
+          "The default `bench.py` run: the 2048 x 4096 x 4096 linear layer (r = 16) forward and "
+          "backward (warm-up, timed pass, event pass), the 28672 x 8192 small-M forward at "
+          "M = 1, 4, 16, and the standalone quantize / double-quant / dequant calls.", "",
+          head, "```", cmds["kt"], "```", "",
+          "| calls | total us | avg us | min us | max us | % | kernel |",
+          "|---:|---:|---:|---:|---:|---:|---|"]
+    for r in rows:
+        name = r["Name"].replace("qlk::", "")
+        name = name if name.startswith("void k_gemm") else name.split("(")[0]
+        md.append("| %s | %.1f | %.2f | %.2f | %.2f | %.2f | `%s` |" % (
+            r["Calls"], float(r["TotalDurationNs"]) / 1e3, float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"]), name))
+    with open(os.path.join(prof, "kernel_stats_default_bench.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+
+    # traffic: FETCH_SIZE / WRITE_SIZE scaled by the copy calibration
+    fpath = os.path.join(out, "f", "f_counter_collection.csv")
+    wpath = os.path.join(out, "w", "w_counter_collection.csv")
+    cal_f = [d["FETCH_SIZE"] for d in _dispatch_counters(fpath, "copyBuffer")
+             if d.get("FETCH_SIZE", 0) > 4e5][:3]
+    cal_w = [d["WRITE_SIZE"] for d in _dispatch_counters(wpath, "copyBuffer")
+             if d.get("WRITE_SIZE", 0) > 8e5][:3]
+    copy_kib = (1 << 30) / 1024.0
+    ff, wf = copy_kib / float(np.median(cal_f)), copy_kib / float(np.median(cal_w))
+    traffic = dict(calibration=dict(copy_bytes=1 << 30, fetch_kib=cal_f, write_kib=cal_w,
+                                    fetch_factor=ff, write_factor=wf),
+                   commands=[cmds["f"], cmds["w"]], kernels={})
+    md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "", head,
+          "```", cmds["f"], cmds["w"], "```", "",
+          f"Calibration: `--copy-calib` copies 1 GiB device to device three times; FETCH_SIZE "
+          f"reads {np.median(cal_f):.0f} KiB per copy (factor {ff:.3f}), WRITE_SIZE "
+          f"{np.median(cal_w):.0f} KiB (factor {wf:.3f}). Counters are scaled by these factors "
+          f"(median over the dispatches of each kernel).", "",
+          "| kernel | workload | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch (scaled) | "
+          "algorithmic bytes / launch |",
+          "|---|---|---:|---:|---:|---:|"]
+    for key, (sym, src, wk) in PROFILED.items():
+        fd, wd = _dispatch_counters(fpath, sym), _dispatch_counters(wpath, sym)
+        if not fd or not wd:
+            continue
+        for (gname, fg), (_, wg) in zip(_groups(sym, fd).items(), _groups(sym, wd).items()):
+            fk, wk_ = _med(fg, "FETCH_SIZE"), _med(wg, "WRITE_SIZE")
+            hbm = fk * 1024 * ff + wk_ * 1024 * wf
+            alg = algorithmic_bytes(key, int(gname.split("=")[1]) if gname else None)
+            md.append(f"| `{sym}` ({key}{gname}) | {wk}{gname} | {fk:.0f} | {wk_:.0f} | "
+                      f"{hbm / 1e6:.2f} MB | {alg / 1e6:.2f} MB |")
+            if not gname or gname == " M=1":
+                traffic["kernels"][key] = dict(kernel=sym, workload=wk, dispatches=len(fg),
+                                               fetch_kib=round(fk, 1), write_kib=round(wk_, 1),
+                                               hbm_bytes_per_launch=int(hbm),
+                                               algorithmic_bytes_per_launch=int(alg),
+                                               source_hash=source_hash([src]))
+    with open(os.path.join(prof, "traffic.json"), "w") as fh:
+        json.dump(traffic, fh, indent=1)
+    with open(os.path.join(prof, "traffic_gemms_gemv.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+
+    # execution counters
+    p1 = os.path.join(out, "p1", "p1_counter_collection.csv")
+    p2 = os.path.join(out, "p2", "p2_counter_collection.csv")
+    md = ["# Execution counters of the GEMMs and the small-M forward (rocprofv3 --pmc)", "",
+          head, "```", cmds["p1"], cmds["p2"], "```", "",
+          "Medians over the dispatches of each kernel. GRBM_GUI_ACTIVE is summed over the 8 XCDs, "
+          "SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs: MFMA busy = "
+          "SQ_VALU_MFMA_BUSY_CYCLES / 1024 / (GRBM_GUI_ACTIVE / 8); effective clock = "
+          "(GRBM_GUI_ACTIVE / 8) / dispatch duration. Wave-cycle shares divide by SQ_WAVE_CYCLES; "
+          "the LDS conflict share divides SQ_LDS_BANK_CONFLICT by SQ_ACTIVE_INST_LDS.", "",
+          "| kernel | clock GHz | MFMA busy | VALU instr / MFMA | LDS instr / MFMA | "
+          "VALU active / wave cycles | waiting (any) / wave cycles | waiting on LDS / wave cycles | "
+          "LDS bank-conflict cycles / LDS active |",
+          "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for key, (sym, src, wk) in PROFILED.items():
+        a, b = _dispatch_counters(p1, sym), _dispatch_counters(p2, sym)
+        if not a or not b:
+            continue
+        for (gname, ag), (_, bg) in zip(_groups(sym, a).items(), _groups(sym, b).items()):
+            gui = _med(bg, "GRBM_GUI_ACTIVE") / 8
+            clk = gui / _med(bg, "_ns")
+            mf = _med(bg, "SQ_INSTS_MFMA")
+            busy = _med(bg, "SQ_VALU_MFMA_BUSY_CYCLES") / 1024 / gui
+            wc = _med(ag, "SQ_WAVE_CYCLES")
+            div = lambda x, y: x / y if y else float("nan")
+            md.append("| `%s`%s | %.2f | %.1f %% | %.2f | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+                sym, gname, clk, 100 * busy, div(_med(bg, "SQ_INSTS_VALU") - mf, mf),
+                div(_med(bg, "SQ_INSTS_LDS"), mf), div(_med(bg, "SQ_ACTIVE_INST_VALU"), wc),
+                div(_med(ag, "SQ_WAIT_INST_ANY"), wc), div(_med(ag, "SQ_WAIT_INST_LDS"), wc),
+                div(_med(ag, "SQ_LDS_BANK_CONFLICT"), _med(ag, "SQ_ACTIVE_INST_LDS"))))
+    md += ["", "VALU instructions exclude the MFMAs (SQ_INSTS_VALU counts both)."]
+    with open(os.path.join(prof, "counters_gemms_gemv.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,9 +597,21 @@ def main():
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-standalone", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--profile-commands", metavar="OUT",
+                    help="print the rocprofv3 runs behind profiles/ (one per line) and exit")
+    ap.add_argument("--summarize", metavar="OUT",
+                    help="write profiles/ from the output of those runs and exit")
     args = ap.parse_args()
+    if args.profile_commands:
+        for v in profile_commands(os.path.abspath(args.profile_commands)).values():
+            print(v)
+        return
+    if args.summarize:
+        summarize(os.path.abspath(args.summarize))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -338,6 +635,11 @@ def main():
         err("[bench] small-M forward ...")
         gemv = run_gemv(args, q, torch, wl, lib, ev)
         err(f"[bench] gemv {gemv}")
+    standalone = None
+    if not args.no_standalone:
+        err("[bench] standalone quantize / double quant / dequant ...")
+        standalone = run_standalone(args, q, torch, lib, ev)
+        err(f"[bench] standalone {standalone}")
     cpu = None
     if not args.no_cpu_baseline:
         err("[bench] CPU oracle baseline ...")
@@ -347,7 +649,7 @@ def main():
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(lin["ms"], 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
                 data="synthetic", config=lin["config"], roofline=lin["roofline"],
-                cpu_baseline=cpu, kernels=lin["kernels"], gemv=gemv,
+                cpu_baseline=cpu, kernels=lin["kernels"], gemv=gemv, standalone=standalone,
                 source_hash=source_hash())
     print(json.dumps(line), flush=True)
 
