@@ -31,9 +31,18 @@ constexpr int kZeroCode8 = 127;
 __device__ __forceinline__ float nf4_level(int i) { return __uint_as_float(kNF4Bits[i]); }
 
 // 8-bit level i of the symmetric linear code: the correctly rounded fp32
-// quotient (i - 127) / 127.
+// quotient (i - 127) / 127.  Computed as a multiply by fl(1/127) followed by
+// one fused correction step, q = fma(fma(-q0, 127, x), fl(1/127), q0) with
+// q0 = x fl(1/127); for the 256 numerators x = -127 .. 128 this equals the
+// correctly rounded quotient (verified exhaustively in exact rational
+// arithmetic), in three instructions instead of a division.
 __device__ __forceinline__ float dq_level(int i) {
-  return (float)(i - 127) / 127.0f;
+#pragma clang fp contract(off)
+  const float x = (float)(i - 127);
+  const float inv = 1.0f / 127.0f;
+  const float q0 = x * inv;
+  const float r = __builtin_fmaf(-q0, 127.0f, x);
+  return __builtin_fmaf(r, inv, q0);
 }
 
 // Decision threshold between NF4 levels i and i+1: their exact midpoint
@@ -161,8 +170,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint
       const_cast<char*>(reinterpret_cast<const char*>(base) + shift), (short)0, (int)rem,
       kRsrcWord3);
 }
+// A resource over a whole array, built once per kernel.  Loads then add a
+// wave-uniform byte offset in the instruction's scalar offset field, so a
+// K-step costs one scalar add instead of a new resource.  Out-of-range lanes
+// still use kOOB in the per-lane offset; every in-range access lies inside
+// the array, so the result does not depend on whether the hardware's range
+// check includes the scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_whole(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload128s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint2 bload64s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t bload32s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t bload8s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ uint2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
 }
 __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);

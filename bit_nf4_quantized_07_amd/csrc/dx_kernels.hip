@@ -6,16 +6,19 @@
 //
 // The contraction runs over n, the weight's row index, so the dequantised
 // weight is needed transposed.  One workgroup computes a 256 x 128 tile of
-// dX (tokens x input features) with four waves; wave w owns input features
-// 32w .. 32w+31 of the tile and all 256 tokens: eight accumulators of
-// v_mfma_f32_32x32x16_bf16, each a 32 (features) x 32 (tokens) block of dX^T.
+// dX (tokens x input features) with eight waves, two per SIMD: wave w owns
+// input features 32 (w % 4) .. +31 of the tile and tokens 128 (w / 4) .. +127,
+// four accumulators of v_mfma_f32_32x32x16_bf16, each a 32 (features) x 32
+// (tokens) block of dX^T.  At one wave per SIMD an MFMA and the same wave's
+// other instructions barely overlap; the second wave issues its MFMAs while
+// the first decodes, reads LDS or waits.
 //
 //  * dY is staged through LDS exactly like X in the forward kernel: 256 x 64
 //    tiles in four buffers, filled by buffer loads that write LDS directly,
 //    rows of 128 bytes with the 16-byte pieces XOR-swizzled by (row >> 1) & 7.
 //  * The weight tile of a step (64 rows n x 128 features) is decoded once per
-//    workgroup: lane L of wave w decodes the 32 weights of row L in columns
-//    32w .. 32w+31 (16 packed bytes, one 8-bit code, one scale) with the
+//    workgroup: lane L of wave w decodes the 16 weights of row L in features
+//    16w .. 16w+15 (8 packed bytes, one 8-bit code, one scale) with the
 //    standalone dequantiser's arithmetic
 //      a_hat = fp32(fp32(Q8[code] * scale) + mean),
 //      w_hat = bf16(fp32(Q4[nibble] * a_hat)),
@@ -24,9 +27,9 @@
 //    eight consecutive rows n of one feature per lane.  The 16-byte pieces of
 //    row n are XOR-swizzled by ((n & 3) << 2) | ((n >> 2) & 3), which keeps
 //    both the decode stores and the transpose reads free of bank conflicts.
-//    Q8[code] is the exact quotient (code - 127) / 127 and the 16 NF4 levels
-//    are fetched from lanes 0..15 of a register with ds_bpermute, so no
-//    table occupies LDS.
+//    Q8[code] is the correctly rounded quotient (code - 127) / 127 (three
+//    instructions) and the 16 NF4 levels, repeated every 16 lanes of a
+//    register, are fetched with ds_bpermute, so no table occupies LDS.
 //  * The weight of step k+1 is decoded during step k into the second weight
 //    buffer; raw weight loads run three steps ahead.
 //  * The adapter term s U A is a last contraction over r into the same
@@ -39,14 +42,18 @@
 namespace qlk {
 
 constexpr int kDxBM = 256;                 // tokens per tile
+constexpr int kDxWaves = 8;
 constexpr int kDxWaveK = 32;               // features per wave
+constexpr int kDxWaveM = 128;              // tokens per wave
 constexpr int kDxBK = 4 * kDxWaveK;        // features per tile
 constexpr int kDxStepN = 64;               // contraction (weight rows) per step
 constexpr int kDyTile = kDxBM * kDxStepN;  // elements per dY buffer
 constexpr int kWTile = kDxStepN * kDxBK;   // elements per weight buffer
 constexpr int kDxUnroll = 4;
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= 11, lgkmcnt <= 8, expcnt not waited on.
-constexpr int kDxWaitEnd = (11 & 0xF) | ((11 >> 4) << 14) | (0x7 << 4) | (8 << 8);
+// s_waitcnt immediates (gfx9 encoding), expcnt not waited on:
+// vmcnt <= 7, lgkmcnt <= 4 (end of a step); vmcnt <= 14, lgkmcnt = 0 (prologue).
+constexpr int kDxWaitEnd = (7 & 0xF) | ((7 >> 4) << 14) | (0x7 << 4) | (4 << 8);
+constexpr int kDxWaitPro = (14 & 0xF) | ((14 >> 4) << 14) | (0x7 << 4) | (0 << 8);
 
 struct DxArgs {
   const uint16_t* dY;   // [M, N] bf16
@@ -61,11 +68,11 @@ struct DxArgs {
   int tiles_m, tiles_k, group_m;
 };
 
-struct DxWRegs { uint4 p; uint32_t code; float sc; };
+struct DxWRegs { uint2 p; uint32_t code; float sc; };
 
 __device__ __forceinline__ int wswz(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
 
-__global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
+__global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t dy0[kDyTile];
   __shared__ __attribute__((aligned(16))) uint16_t dy1[kDyTile];
   __shared__ __attribute__((aligned(16))) uint16_t dy2[kDyTile];
@@ -74,8 +81,10 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t wt1[kWTile];
   uint16_t* const dyb[4] = {dy0, dy1, dy2, dy3};
   uint16_t* const wtb[2] = {wt0, wt1};
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: LDS bases, offsets
   const int c = lane & 31, h = lane >> 5;
+  const int fg = wave & 3, th = wave >> 2;   // feature group, token half
 
   int tm, tk;
   tile_coords(blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
@@ -86,70 +95,70 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
   const float mean = g.w.mean[0];
   const float qlev = nf4_level(lane & 15);   // source of the level lookups
 
-  // dY tile loads (as X in the forward kernel).
+  // dY tile loads: wave w fills rows 32w .. 32w+31, 8 rows per load.
   const uint32_t dybytes = (uint32_t)((int64_t)g.M * N * 2);
   auto swz = [](int row) { return (row >> 1) & 7; };
-  uint32_t yoff[8];
+  uint32_t yoff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
     const int piece = (lane & 7) ^ swz(row);
     yoff[i] = m0 + row < g.M ? (uint32_t)(((int64_t)(m0 + row) * N + piece * 8) * 2) : kOOB;
   }
   int yrd[4];   // operand reads: row c, logical piece 2t + h
 #pragma unroll
   for (int t = 0; t < 4; ++t) yrd[t] = c * kDxStepN + (((2 * t + h) ^ swz(c)) * 8);
+  const __amdgpu_buffer_rsrc_t rdy = rsrc_whole(g.dY, dybytes);
   auto load_dy = [&](uint16_t* buf, int kb) {
-    kb = __builtin_amdgcn_readfirstlane(kb);
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(g.dY, dybytes, (uint32_t)kb * (kDxStepN * 2));
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * (kDxStepN * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * i) * kDxStepN), 16,
-          yoff[i], 0, 0, 0);
+          rdy, (__attribute__((address_space(3))) void*)(buf + (32 * wave + 8 * i) * kDxStepN), 16,
+          yoff[i], soff, 0, 0);
   };
+  // Operand of token block i (32 tokens) of this wave's half, MFMA step t.
   auto yfrag = [&](const uint16_t* buf, int i, int t) -> bf16x8_t {
-    return *reinterpret_cast<const bf16x8_t*>(buf + 32 * i * kDxStepN + yrd[t]);
+    return *reinterpret_cast<const bf16x8_t*>(buf + (kDxWaveM * th + 32 * i) * kDxStepN + yrd[t]);
   };
 
   // Weight decode: lane L of wave w owns row n = L of the step and features
-  // 32w .. 32w+31 of the tile (16 packed bytes of one 64-block).
-  const int64_t kcol = k0 + 32 * wave;
+  // 16w .. 16w+15 of the tile (8 packed bytes of one 64-block).
+  const int64_t kcol = k0 + 16 * wave;
   const bool kvalid = kcol < K;
   const uint32_t pbytes = (uint32_t)(N * (K / 2)), cbytes = (uint32_t)(N * nkb);
   const uint32_t sbytes = (uint32_t)(((N * nkb + kDQBlock - 1) / kDQBlock) * 4);
   const uint32_t poff = kvalid ? (uint32_t)((int64_t)lane * (K / 2) + kcol / 2) : kOOB;
   const uint32_t coff = kvalid ? (uint32_t)((int64_t)lane * nkb + kcol / kBlock) : kOOB;
+  const __amdgpu_buffer_rsrc_t rp = rsrc_whole(g.w.packed, pbytes);
+  const __amdgpu_buffer_rsrc_t rc = rsrc_whole(g.w.codes, cbytes);
+  const __amdgpu_buffer_rsrc_t rsc = rsrc_whole(g.w.scales, sbytes);
   auto load_w = [&](DxWRegs& R, int kb) {   // rows 64 kb .. 64 kb + 63
-    kb = __builtin_amdgcn_readfirstlane(kb);
-    const __amdgpu_buffer_rsrc_t rp = rsrc_at(g.w.packed, pbytes, (uint32_t)kb * kDxStepN * (uint32_t)(K / 2));
-    const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.w.codes, cbytes, (uint32_t)kb * kDxStepN * (uint32_t)nkb);
-    const __amdgpu_buffer_rsrc_t rsc = rsrc_at(g.w.scales, sbytes, 0u);
-    R.p = bload128(rp, poff);
-    R.code = bload8(rc, coff);
-    const uint32_t blk = (uint32_t)kb * kDxStepN * (uint32_t)nkb + coff;
+    const uint32_t row0 = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * kDxStepN;
+    R.p = bload64s(rp, poff, row0 * (uint32_t)(K / 2));
+    R.code = bload8s(rc, coff, row0 * (uint32_t)nkb);
+    const uint32_t blk = row0 * (uint32_t)nkb + coff;
     R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : (blk / kDQBlock) * 4u));
   };
-  auto word = [](const DxWRegs& R, int t) -> uint32_t {
-    return t == 0 ? R.p.x : t == 1 ? R.p.y : t == 2 ? R.p.z : R.p.w;
+  auto word = [](const DxWRegs& R, int t) -> uint32_t { return t == 0 ? R.p.x : R.p.y; };
+  // NF4 level of the nibble at bits b .. b+3 of w.  ds_bpermute reads lane
+  // addr[7:2] and ignores every other address bit, and qlev repeats the 16
+  // levels every 16 lanes, so only addr[5:2] matters: a shift that brings
+  // the nibble to bits 2..5 is the whole address computation.
+  auto lev = [&](uint32_t w, int b) -> float {
+    const uint32_t addr = b >= 2 ? w >> (b - 2) : w << (2 - b);
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((int)addr, __float_as_int(qlev)));
   };
-  // NF4 level of nibble `nib4 / 4` taken from lane (nib4 / 4) of qlev.
-  auto level = [&](uint32_t nib4, int e) -> float {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(
-        (int)__builtin_amdgcn_perm(0u, nib4, 0x0c0c0c00u | e), __float_as_int(qlev)));
-  };
-  auto hi4 = [](uint32_t w) { return (w >> 2) & 0x3C3C3C3Cu; };
-  auto lo4 = [](uint32_t w) { return (w << 2) & 0x3C3C3C3Cu; };
   auto absmax = [&](const DxWRegs& R) -> float {
 #pragma clang fp contract(off)
-    const float q = (float)((int)R.code - 127) / 127.0f;
+    const float q = dq_level((int)R.code);
     const float p = q * R.sc;
     return p + mean;
   };
-  // Decoded row: four 16-byte pieces (logical 4w .. 4w+3) of row `lane`.
+  // Decoded row: two 16-byte pieces (logical 2w, 2w+1) of row `lane`.
   const int wrow = lane;
   auto wstore = [&](uint16_t* buf, int q, uint4 v) {
-    const int phys = (4 * wave + q) ^ wswz(wrow);
+    const int phys = (2 * wave + q) ^ wswz(wrow);
     *reinterpret_cast<uint4*>(buf + wrow * kDxBK + phys * 8) = v;
   };
   // Transpose-read operand: features c of the wave's 32, rows 16t + 8h + 0..7.
@@ -160,7 +169,7 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int n = 16 * t + 8 * (grp >> 1) + 4 * half + (gi >> 2);
-      const int col = 32 * wave + 16 * (grp & 1) + 4 * (gi & 3);
+      const int col = 32 * fg + 16 * (grp & 1) + 4 * (gi & 3);
       const int phys = (col / 8) ^ wswz(n);
       wrd[t][half] = n * kDxBK + phys * 8 + (col & 7);
     }
@@ -174,18 +183,18 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
   auto decode_all = [&](const DxWRegs& R, uint16_t* buf) {
     const float ah = absmax(R);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t hq = hi4(word(R, q)), lq = lo4(word(R, q));
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t w = word(R, q);
       uint32_t o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(level(hq, e) * ah, level(lq, e) * ah);
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(lev(w, 8 * e + 4) * ah, lev(w, 8 * e) * ah);
       wstore(buf, q, make_uint4(o[0], o[1], o[2], o[3]));
     }
   };
 
-  f32x16_t acc[8];
+  f32x16_t acc[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
@@ -193,19 +202,29 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
   // weight of step j in wr[j % 4] from its load (step j-3) to its decode
   // (step j-1) into weight buffer j % 2, read during step j.
   DxWRegs wr[4];
-  bf16x8_t b[2][8];   // dY operands
+  bf16x8_t b[2][4];   // dY operands
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     load_dy(dyb[j], min(j, nsteps - 1));
     load_w(wr[j], min(j, nsteps - 1));
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  // Only step 0's seven loads must have arrived (those of steps 1 and 2 may
+  // still be in flight) before its weight is decoded and the barrier
+  // publishes dY(0) and W(0).
+  __builtin_amdgcn_s_waitcnt(kDxWaitPro);
   decode_all(wr[0], wtb[0]);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kDxWaitPro);
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) b[0][i] = yfrag(dyb[0], i, 0);
+  for (int i = 0; i < 4; ++i) b[0][i] = yfrag(dyb[0], i, 0);
 
+  // One step: 16 MFMA slots (t = u / 4 of the 64-row step, token block
+  // i = u % 4); the operands of the next MFMA step, the decode of the next
+  // weight tile and its two LDS stores are spread over the slots.  The 16
+  // level lookups go out in the first four slots and are used from slot 6
+  // on, so their latency is covered by MFMAs; the first operands of the next
+  // step are read in the last slot, after the decoded weight's stores.
   auto step = [&](auto Pc, int kb) {
     constexpr int P = decltype(Pc)::value;
     const DxWRegs& wdec = wr[(P + 1) % 4];
@@ -220,39 +239,42 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
     bf16x8_t a[2];
     a[0] = wfrag(wcur, 0);
     float ah = 0.0f;
-    float lh[16], ll[16];
-    uint32_t nh[4], nl[4], o[16];
+    float lh[8], ll[8];
+    uint32_t o[8];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int t = u / 8, i = u % 8;
+    for (int u = 0; u < 16; ++u) {
+      const int t = u / 4, i = u % 4;
       acc[i] = mfma_32x32x16(a[t & 1], b[t & 1][i], acc[i]);
       if (i == 0 && t < 3) a[(t + 1) & 1] = wfrag(wcur, t + 1);
-      if (t < 3) b[(t + 1) & 1][i] = yfrag(ycur, i, t + 1);
-      else b[0][i] = yfrag(ynext, i, 0);
-      if (u < 16) {
-        if (u % 4 == 0) {
-          nh[u / 4] = hi4(word(wdec, u / 4));
-          nl[u / 4] = lo4(word(wdec, u / 4));
+      if (u < 4) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int v = 2 * u + e;   // byte v % 4 of word v / 4: element 2v high, 2v+1 low
+          lh[v] = lev(word(wdec, v / 4), 8 * (v % 4) + 4);
+          ll[v] = lev(word(wdec, v / 4), 8 * (v % 4));
         }
-        lh[u] = level(nh[u / 4], u % 4);
-        ll[u] = level(nl[u / 4], u % 4);
       }
       if (u == 1) ah = absmax(wdec);
-      if (u >= 4 && u < 20) {
-        const int v = u - 4;
+      if (u >= 6 && u < 14) {
+        const int v = u - 6;
         o[v] = pack_bf16x2(lh[v] * ah, ll[v] * ah);
       }
-      if (u >= 20 && u < 24) {
-        const int q = u - 20;
+      if (u == 13 || u == 14) {
+        const int q = u - 13;
         wstore(wnext, q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+      }
+      if (t < 3) b[(t + 1) & 1][i] = yfrag(ycur, i, t + 1);
+      if (u == 15) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[0][j] = yfrag(ynext, j, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // Before step kb+1: dY(kb+2) (loaded during step kb-1) in LDS from every
-    // wave (at most this step's 11 global loads outstanding) and this wave's
-    // decoded weight stores done (at most the 8 operand reads of slots
-    // 24..31 outstanding), then the barrier.
+    // wave (at most this step's 7 global loads outstanding) and this wave's
+    // decoded weight stores done (at most the 4 operand reads of slot 15
+    // outstanding), then the barrier.
     __builtin_amdgcn_s_waitcnt(kDxWaitEnd);
     __builtin_amdgcn_s_barrier();
   };
@@ -265,7 +287,8 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
   __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
 
   // Adapter term: acc += (s A)^T U^T over r in steps of 16.
-  const int64_t kf = k0 + 32 * wave + c;   // this lane's feature (operand row)
+  const int64_t kf = k0 + 32 * fg + c;   // this lane's feature (operand row)
+  const int mw = m0 + kDxWaveM * th;     // first token of this wave
   for (int r0 = 0; r0 < g.r; r0 += 16) {
     const int rr = r0 + 8 * h;
     uint32_t av[4] = {0u, 0u, 0u, 0u};
@@ -279,20 +302,20 @@ __global__ void __launch_bounds__(256) k_dx_nf4(DxArgs g) {
     }
     const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + 32 * i + c;
+    for (int i = 0; i < 4; ++i) {
+      const int m = mw + 32 * i + c;
       uint4 uv = make_uint4(0, 0, 0, 0);
       if (m < g.M && rr < g.r) uv = *reinterpret_cast<const uint4*>(g.U + (int64_t)m * g.r + rr);
       acc[i] = mfma_32x32x16(afr, __builtin_bit_cast(bf16x8_t, uv), acc[i]);
     }
   }
 
-  // Accumulator i: lane holds token m = m0 + 32 i + c and features
+  // Accumulator i: lane holds token m = mw + 32 i + c and features
   // 8 (v / 4) + 4 h + (v % 4) of the wave's 32.
-  const int64_t kw0 = k0 + 32 * wave;
+  const int64_t kw0 = k0 + 32 * fg;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + 32 * i + c;
+  for (int i = 0; i < 4; ++i) {
+    const int m = mw + 32 * i + c;
     if (m >= g.M) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -322,7 +345,7 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
   g.tiles_m = (int)((M + kDxBM - 1) / kDxBM);
   g.tiles_k = (int)((w.K + kDxBK - 1) / kDxBK);
   g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2, (double)kDxBK * w.N * 0.52);
-  hipLaunchKernelGGL(k_dx_nf4, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, g);
+  hipLaunchKernelGGL(k_dx_nf4, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
   return hipGetLastError();
 }
 
