@@ -83,7 +83,8 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t xs2[kXTile];
   __shared__ __attribute__((aligned(16))) uint16_t xs3[kXTile];
   uint16_t* const xbuf[kXBufs] = {xs0, xs1, xs2, xs3};
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: LDS bases, offsets
   const int c = lane & 31, h = lane >> 5;
   if (tid < 16) q4[tid] = nf4_level(tid);
   q8[tid] = dq_level(tid);
@@ -119,24 +120,25 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   const uint32_t poff = nvalid ? (uint32_t)(nrow * (K / 2) + 16 * h) : kOOB;
   const uint32_t coff = nvalid ? (uint32_t)(nrow * nkb) : kOOB;
 
-  // kb is wave-uniform; readfirstlane keeps the buffer resources scalar.
-  // Eight buffer loads straight into LDS buffer `buf`.
+  // One resource per array for the whole kernel; kb is wave-uniform and
+  // moves the loads through the scalar offset field.  Eight buffer loads go
+  // straight into LDS buffer `buf`.
+  const __amdgpu_buffer_rsrc_t rx = rsrc_whole(g.X, xbytes);
+  const __amdgpu_buffer_rsrc_t rp = rsrc_whole(g.w.packed, pbytes);
+  const __amdgpu_buffer_rsrc_t rc = rsrc_whole(g.w.codes, cbytes);
+  const __amdgpu_buffer_rsrc_t rsc = rsrc_whole(g.w.scales, sbytes);
   auto load_x = [&](uint16_t* buf, int kb) {
-    kb = __builtin_amdgcn_readfirstlane(kb);
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(g.X, xbytes, (uint32_t)kb * (kBlock * 2));
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * (kBlock * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * i) * kXRow), 16,
-          xoff[i], 0, 0, 0);
+          rx, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * i) * kXRow), 16,
+          xoff[i], soff, 0, 0);
   };
   auto load_w = [&](FwdWRegs& R, int kb) {
     kb = __builtin_amdgcn_readfirstlane(kb);
-    const __amdgpu_buffer_rsrc_t rp = rsrc_at(g.w.packed, pbytes, (uint32_t)kb * (kBlock / 2));
-    const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.w.codes, cbytes, (uint32_t)kb);
-    const __amdgpu_buffer_rsrc_t rsc = rsrc_at(g.w.scales, sbytes, 0u);
-    R.p = bload128(rp, poff);
-    R.code = bload8(rc, coff);
+    R.p = bload128s(rp, poff, (uint32_t)kb * (kBlock / 2));
+    R.code = bload8s(rc, coff, (uint32_t)kb);
     R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + (uint32_t)kb) / kDQBlock) * 4u));
   };
   auto word = [](const FwdWRegs& R, int t) -> uint32_t {
