@@ -240,7 +240,8 @@ k_gemv_dma(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __re
   }
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, h = lane >> 5;
   const int64_t N = w.N, K = w.K, nkb = K / kBlock;
   const int64_t n0 = (int64_t)blockIdx.x * 64;
@@ -270,13 +271,13 @@ k_gemv_dma(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __re
     const int piece = (lane & 7) ^ swz(row);
     poff[i] = n0 + row < N ? (uint32_t)((n0 + row) * (K / 2) + piece * 16) : kOOB;
   }
+  const __amdgpu_buffer_rsrc_t rp = rsrc_whole(w.packed, pbytes);
   auto load_w = [&](uint8_t* buf, int ss) {
-    const uint32_t shift = (uint32_t)((kb0 + (int64_t)ss * kGemvSS) * 32);
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(w.packed, pbytes, shift);
+    const uint32_t soff = (uint32_t)(kb0 + (int64_t)__builtin_amdgcn_readfirstlane(ss) * kGemvSS) * 32u;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, poff[i], 0, 0, 0);
+          rp, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, poff[i], soff, 0, 0);
   };
   // Operand of block b, half h, group g: row 32 g + c, logical piece 2 b + h.
   auto wfrag = [&](const uint8_t* buf, int g, int b) -> uint4 {
@@ -287,20 +288,25 @@ k_gemv_dma(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __re
   const uint32_t xoff = mvalid ? (uint32_t)(((int64_t)c * K + 32 * h) * 2) : kOOB;
   const uint32_t cbytes = (uint32_t)(N * nkb);
   const uint32_t sbytes = (uint32_t)(((N * nkb + kDQBlock - 1) / kDQBlock) * 4);
+  const __amdgpu_buffer_rsrc_t rx = rsrc_whole(X, xbytes);
+  const __amdgpu_buffer_rsrc_t rc = rsrc_whole(w.codes, cbytes);
+  const __amdgpu_buffer_rsrc_t rsc = rsrc_whole(w.scales, sbytes);
+  uint32_t coff[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) coff[g] = nvalid[g] ? (uint32_t)(nrow[g] * nkb + kb0) : kOOB;
   auto load_r = [&](GemvSSRegs& R, int ss) {
-    const int64_t kb = kb0 + (int64_t)ss * kGemvSS;
-    const __amdgpu_buffer_rsrc_t rx = rsrc_at(X, xbytes, (uint32_t)(kb * kBlock * 2));
+    const uint32_t kbs = (uint32_t)__builtin_amdgcn_readfirstlane(ss) * kGemvSS;   // from kb0
+    const uint32_t xs = (uint32_t)(kb0 + kbs) * (kBlock * 2);
 #pragma unroll
     for (int b = 0; b < kGemvSS; ++b)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) R.x[b][t] = bload128(rx, xoff == kOOB ? kOOB : xoff + (uint32_t)(b * 128 + t * 16));
-    const __amdgpu_buffer_rsrc_t rc = rsrc_at(w.codes, cbytes, 0u);
-    const __amdgpu_buffer_rsrc_t rsc = rsrc_at(w.scales, sbytes, 0u);
+      for (int t = 0; t < 4; ++t)
+        R.x[b][t] = bload128s(rx, xoff == kOOB ? kOOB : xoff + (uint32_t)(b * 128 + t * 16), xs);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const uint32_t blk = nvalid[g] ? (uint32_t)(nrow[g] * nkb + kb) : kOOB;
-      R.code[g] = bload32(rc, blk);
-      R.sc[g] = __uint_as_float(bload32(rsc, blk == kOOB ? kOOB : (blk / kDQBlock) * 4u));
+      R.code[g] = bload32s(rc, coff[g], kbs);
+      R.sc[g] = __uint_as_float(
+          bload32(rsc, coff[g] == kOOB ? kOOB : ((coff[g] + kbs) / kDQBlock) * 4u));
     }
   };
 
