@@ -102,10 +102,11 @@ struct LdBF16K {
     }
   }
   __device__ void load(Regs& R, const Operand& op, const GemmArgs&, int c0, int c_end) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(op.p, op.bytes, (uint32_t)c0 * 2u);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_whole(op.p, op.bytes);
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(c0) * 2u;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i)
-      R.v[i] = bload128(rs, c0 + cc[i] < c_end ? voff[i] : kOOB);
+      R.v[i] = bload128s(rs, c0 + cc[i] < c_end ? voff[i] : kOOB, soff);
   }
   __device__ void store(const Regs& R, const Operand& op, uint16_t* lds, const Dec&) {
 #pragma unroll
@@ -150,10 +151,11 @@ struct LdBF16T {
     }
   }
   __device__ void load(Regs& R, const Operand& op, const GemmArgs&, int c0, int c_end) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(op.p, op.bytes, (uint32_t)((int64_t)c0 * op.ld * 2));
+    const __amdgpu_buffer_rsrc_t rs = rsrc_whole(op.p, op.bytes);
+    const uint32_t soff = (uint32_t)((int64_t)__builtin_amdgcn_readfirstlane(c0) * op.ld * 2);
 #pragma unroll
     for (int i = 0; i < PER_T; ++i)
-      R.v[i] = bload128(rs, (voff[i] != kOOB && c0 + cl[i] < c_end) ? voff[i] : kOOB);
+      R.v[i] = bload128s(rs, (voff[i] != kOOB && c0 + cl[i] < c_end) ? voff[i] : kOOB, soff);
   }
   __device__ void store(const Regs& R, const Operand& op, uint16_t* lds, const Dec&) {
 #pragma unroll
@@ -213,12 +215,13 @@ struct LdNF4K {
   }
   __device__ void load(Regs& R, const Operand&, const GemmArgs& g, int c0, int) {
     const uint32_t pbytes = (uint32_t)(g.w.N * (g.w.K / 2)), cbytes = (uint32_t)(g.w.N * (g.w.K / kBlock));
-    const __amdgpu_buffer_rsrc_t rp = rsrc_at(g.w.packed, pbytes, (uint32_t)c0 / 2u);
-    const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.w.codes, cbytes, (uint32_t)c0 / kBlock);
+    const __amdgpu_buffer_rsrc_t rp = rsrc_whole(g.w.packed, pbytes);
+    const __amdgpu_buffer_rsrc_t rc = rsrc_whole(g.w.codes, cbytes);
+    const uint32_t cu = (uint32_t)__builtin_amdgcn_readfirstlane(c0);
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      R.p[i] = bload128(rp, voff_p[i]);
-      R.code[i] = bload8(rc, voff_c[i]);
+      R.p[i] = bload128s(rp, voff_p[i], cu / 2u);
+      R.code[i] = bload8s(rc, voff_c[i], cu / kBlock);
       R.sc[i] = g.w.scales[(blk0[i] + (uint32_t)c0 / kBlock) / kDQBlock];
     }
   }
@@ -273,14 +276,15 @@ struct LdNF4T {
   __device__ void load(Regs& R, const Operand&, const GemmArgs& g, int c0, int c_end) {
     const int64_t nkb = g.w.K / kBlock;
     const uint32_t pbytes = (uint32_t)(g.w.N * (g.w.K / 2)), cbytes = (uint32_t)(g.w.N * nkb);
-    const __amdgpu_buffer_rsrc_t rp = rsrc_at(g.w.packed, pbytes, (uint32_t)((int64_t)c0 * (g.w.K / 2)));
-    const __amdgpu_buffer_rsrc_t rc = rsrc_at(g.w.codes, cbytes, (uint32_t)((int64_t)c0 * nkb));
-    const uint32_t s0 = (uint32_t)((int64_t)c0 * nkb);
+    const __amdgpu_buffer_rsrc_t rp = rsrc_whole(g.w.packed, pbytes);
+    const __amdgpu_buffer_rsrc_t rc = rsrc_whole(g.w.codes, cbytes);
+    const int64_t cu = __builtin_amdgcn_readfirstlane(c0);
+    const uint32_t s0 = (uint32_t)(cu * nkb);
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const bool ok = kok[i] && c0 + nl[i] < c_end;
-      R.p[i] = bload128(rp, ok ? voff_p[i] : kOOB);
-      R.code[i] = bload8(rc, ok ? voff_c[i] : kOOB);
+      R.p[i] = bload128s(rp, ok ? voff_p[i] : kOOB, (uint32_t)(cu * (g.w.K / 2)));
+      R.code[i] = bload8s(rc, ok ? voff_c[i] : kOOB, s0);
       R.sc[i] = g.w.scales[ok ? (s0 + kb_of[i]) / kDQBlock : 0u];
       R.mask[i] = ok ? 1.0f : 0.0f;
     }
