@@ -653,9 +653,8 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r) {
   p.u_splits = 1;
   p.m_splits_a = actual_splits(M, choose_splits((int64_t)ceil_div(r, r_tile(r)) * ceil_div(K, 128), M));
   p.m_splits_b = actual_splits(M, choose_splits((int64_t)ceil_div(N, 128) * rt, M));
-  size_t part = (size_t)p.m_splits_a * r * K;
-  part = part > (size_t)p.m_splits_b * N * r ? part : (size_t)p.m_splits_b * N * r;
-  p.bytes = p.off_part + align256(part * 4);
+  p.off_part_b = p.off_part + align256((size_t)p.m_splits_a * r * K * 4);
+  p.bytes = p.off_part_b + align256((size_t)p.m_splits_b * N * r * 4);
   return p;
 }
 
@@ -684,6 +683,44 @@ static hipError_t launch_gemm(GemmArgs g, int splits, double a_tile_bytes, doubl
   hipLaunchKernelGGL((k_gemm<BM, BN, BK, WGM, WGN, LA1, LB1, LA2, LB2, EPI>), grid, dim3(kThreads),
                      0, st, g);
   return hipGetLastError();
+}
+
+// Both split reductions of the backward (dA and dB) in one launch: blocks
+// [0, blocks of dA) take dA, the rest dB; each block runs the same fixed
+// order as k_reduce_splits.
+__global__ void __launch_bounds__(256)
+k_reduce_splits2(const float* __restrict__ part_a, int splits_a, int64_t n_a, float* __restrict__ out_a,
+                 const float* __restrict__ part_b, int splits_b, int64_t n_b, float* __restrict__ out_b,
+                 int blocks_a, float scale) {
+  __shared__ float4 red[kRedLanes][kRedCols];
+  const bool first = (int)blockIdx.x < blocks_a;
+  const float* part = first ? part_a : part_b;
+  const int splits = first ? splits_a : splits_b;
+  const int64_t n4 = (first ? n_a : n_b) / 4;
+  float* out = first ? out_a : out_b;
+  const int64_t blk = first ? blockIdx.x : blockIdx.x - blocks_a;
+  const int tid = threadIdx.x, col = tid % kRedCols, g = tid / kRedCols;
+  const int64_t i4 = blk * kRedCols + col;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (i4 < n4) {
+    const float4* p = reinterpret_cast<const float4*>(part) + i4;
+#pragma unroll 2
+    for (int z = g; z < splits; z += kRedLanes) {
+      const float4 v = p[(int64_t)z * n4];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  }
+  red[g][col] = acc;
+  __syncthreads();
+  if (g != 0 || i4 >= n4) return;
+  float4 t = red[0][col];
+#pragma unroll
+  for (int q = 1; q < kRedLanes; ++q) {
+    const float4 v = red[q][col];
+    t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+  }
+  t.x *= scale; t.y *= scale; t.z *= scale; t.w *= scale;
+  reinterpret_cast<float4*>(out)[i4] = t;
 }
 
 static hipError_t launch_reduce(const float* part, int splits, int64_t n, float scale, float* of,
@@ -783,6 +820,7 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
   char* base = reinterpret_cast<char*>(ws);
   uint16_t* U = reinterpret_cast<uint16_t*>(base + plan.off_U);
   float* part = reinterpret_cast<float*>(base + plan.off_part);
+  float* part_b = reinterpret_cast<float*>(base + plan.off_part_b);
   const int rt = r_tile(r);
   if (!T) {
     uint16_t* Tw = reinterpret_cast<uint16_t*>(base + plan.off_T);
@@ -815,11 +853,17 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
   // dA = s U^T X: rows j (U^T, transposed), cols k (X^T, transposed), contraction m.
   QLK_TRY((skinny<1, 1, true>(rt, opnd(U, r, r, M), opnd(X, K, (int)K, M), r, (int)K, M, plan.m_splits_a,
                               part, st)));
-  QLK_TRY(launch_reduce(part, actual_splits(M, plan.m_splits_a), (int64_t)r * K, s, dA, nullptr, st));
   // dB = s dY^T T: rows n (dY^T), cols j (T^T), contraction m.
   QLK_TRY((skinny<1, 1, false>(rt, opnd(dY, N, (int)N, M), opnd(T, r, r, M), (int)N, r, M,
-                               plan.m_splits_b, part, st)));
-  return launch_reduce(part, actual_splits(M, plan.m_splits_b), N * r, s, dB, nullptr, st);
+                               plan.m_splits_b, part_b, st)));
+  // Both fixed-order split reductions in one launch.
+  const int64_t na = (int64_t)r * K, nb = N * r;
+  const int blocks_a = (int)((na / 4 + kRedCols - 1) / kRedCols);
+  const int blocks_b = (int)((nb / 4 + kRedCols - 1) / kRedCols);
+  hipLaunchKernelGGL(k_reduce_splits2, dim3((unsigned)(blocks_a + blocks_b)), dim3(256), 0, st, part,
+                     actual_splits(M, plan.m_splits_a), na, dA, part_b, actual_splits(M, plan.m_splits_b),
+                     nb, dB, blocks_a, s);
+  return hipGetLastError();
 }
 
 }  // namespace qlk

@@ -35,7 +35,7 @@ struct FwdPlan {
 };
 struct BwdPlan {
   int u_splits, t_splits, m_splits_a, m_splits_b;
-  size_t off_U, off_T, off_part, bytes;
+  size_t off_U, off_T, off_part, off_part_b, bytes;   // dA partials at off_part, dB at off_part_b
 };
 FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r);
 BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r);
