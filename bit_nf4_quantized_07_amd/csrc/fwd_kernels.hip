@@ -127,19 +127,30 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   const __amdgpu_buffer_rsrc_t rp = rsrc_whole(g.w.packed, pbytes);
   const __amdgpu_buffer_rsrc_t rc = rsrc_whole(g.w.codes, cbytes);
   const __amdgpu_buffer_rsrc_t rsc = rsrc_whole(g.w.scales, sbytes);
+  // X load j (0..7) of step kb fills rows 64 w + 8 j .. +7 of buffer `buf`;
+  // weight load j (0..2) brings the packed bytes, the code, the scale.
+  auto load_xj = [&](int j, uint16_t* buf, int kb) {
+    const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rx, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * j) * kXRow), 16,
+        xoff[j], k * (kBlock * 2), 0, 0);
+  };
+  auto load_wj = [&](int j, FwdWRegs& R, int kb) {
+    const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
+    if (j == 0)
+      R.p = bload128s(rp, poff, k * (kBlock / 2));
+    else if (j == 1)
+      R.code = bload8s(rc, coff, k);
+    else
+      R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + k) / kDQBlock) * 4u));
+  };
   auto load_x = [&](uint16_t* buf, int kb) {
-    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * (kBlock * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * i) * kXRow), 16,
-          xoff[i], soff, 0, 0);
+    for (int j = 0; j < 8; ++j) load_xj(j, buf, kb);
   };
   auto load_w = [&](FwdWRegs& R, int kb) {
-    kb = __builtin_amdgcn_readfirstlane(kb);
-    R.p = bload128s(rp, poff, (uint32_t)kb * (kBlock / 2));
-    R.code = bload8s(rc, coff, (uint32_t)kb);
-    R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + (uint32_t)kb) / kDQBlock) * 4u));
+#pragma unroll
+    for (int j = 0; j < 3; ++j) load_wj(j, R, kb);
   };
   auto word = [](const FwdWRegs& R, int t) -> uint32_t {
     return t == 0 ? R.p.x : t == 1 ? R.p.y : t == 2 ? R.p.z : R.p.w;
@@ -203,8 +214,11 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
 
     // 3 weight loads, then 8 X loads into the buffer of step kb-1 (its
     // operand reads by this wave completed before the last barrier).
-    load_w(wload, min(kb + 3, nk - 1));
-    load_x(xbuf[(P + 3) % kXBufs], min(kb + 3, nk - 1));
+    // This step's 11 loads (for step kb+3) go out one per MFMA slot 0..10,
+    // so that the workgroup's waves, released together by the barrier, do
+    // not queue 44 loads at the address unit before their first MFMA.
+    const int kload = min(kb + 3, nk - 1);
+    uint16_t* const xload = xbuf[(P + 3) % kXBufs];
     const float q8v = q8[wdec.code];
     float ah = 0.0f;
     float lh[16], ll[16];
@@ -214,6 +228,8 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     for (int u = 0; u < 32; ++u) {
       const int t = u / 8, i = u % 8;
       acc[i] = mfma_32x32x16(as_frag(bc.d[t]), a[t & 1][i], acc[i]);
+      if (u < 8) load_xj(u, xload, kload);
+      else if (u < 11) load_wj(u - 8, wload, kload);
       if (t < 3) a[(t + 1) & 1][i] = xfrag(xcur, i, t + 1);
       else a[0][i] = xfrag(xnext, i, 0);
       if (u < 16) {
