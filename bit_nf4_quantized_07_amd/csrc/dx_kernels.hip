@@ -109,13 +109,16 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) yrd[t] = c * kDxStepN + (((2 * t + h) ^ swz(c)) * 8);
   const __amdgpu_buffer_rsrc_t rdy = rsrc_whole(g.dY, dybytes);
-  auto load_dy = [&](uint16_t* buf, int kb) {
+  // dY load i (0..3) of step kb fills rows 32 w + 8 i .. +7 of buffer `buf`.
+  auto load_dyi = [&](int i, uint16_t* buf, int kb) {
     const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * (kDxStepN * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rdy, (__attribute__((address_space(3))) void*)(buf + (32 * wave + 8 * i) * kDxStepN), 16,
+        yoff[i], soff, 0, 0);
+  };
+  auto load_dy = [&](uint16_t* buf, int kb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rdy, (__attribute__((address_space(3))) void*)(buf + (32 * wave + 8 * i) * kDxStepN), 16,
-          yoff[i], soff, 0, 0);
+    for (int i = 0; i < 4; ++i) load_dyi(i, buf, kb);
   };
   // Operand of token block i (32 tokens) of this wave's half, MFMA step t.
   auto yfrag = [&](const uint16_t* buf, int i, int t) -> bf16x8_t {
@@ -133,12 +136,21 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   const __amdgpu_buffer_rsrc_t rp = rsrc_whole(g.w.packed, pbytes);
   const __amdgpu_buffer_rsrc_t rc = rsrc_whole(g.w.codes, cbytes);
   const __amdgpu_buffer_rsrc_t rsc = rsrc_whole(g.w.scales, sbytes);
-  auto load_w = [&](DxWRegs& R, int kb) {   // rows 64 kb .. 64 kb + 63
+  // Weight load j (0..2) of rows 64 kb .. 64 kb + 63: packed bytes, code, scale.
+  auto load_wj = [&](int j, DxWRegs& R, int kb) {
     const uint32_t row0 = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * kDxStepN;
-    R.p = bload64s(rp, poff, row0 * (uint32_t)(K / 2));
-    R.code = bload8s(rc, coff, row0 * (uint32_t)nkb);
-    const uint32_t blk = row0 * (uint32_t)nkb + coff;
-    R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : (blk / kDQBlock) * 4u));
+    if (j == 0) {
+      R.p = bload64s(rp, poff, row0 * (uint32_t)(K / 2));
+    } else if (j == 1) {
+      R.code = bload8s(rc, coff, row0 * (uint32_t)nkb);
+    } else {
+      const uint32_t blk = row0 * (uint32_t)nkb + coff;
+      R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : (blk / kDQBlock) * 4u));
+    }
+  };
+  auto load_w = [&](DxWRegs& R, int kb) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) load_wj(j, R, kb);
   };
   auto word = [](const DxWRegs& R, int t) -> uint32_t { return t == 0 ? R.p.x : R.p.y; };
   // NF4 level of the nibble at bits b .. b+3 of w.  ds_bpermute reads lane
@@ -234,8 +246,11 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     const uint16_t* wcur = wtb[P % 2];
     uint16_t* wnext = wtb[(P + 1) % 2];
 
-    load_w(wload, min(kb + 3, nsteps - 1));
-    load_dy(dyb[(P + 3) % 4], min(kb + 3, nsteps - 1));
+    // This step's 7 loads (for step kb+3) go out one per MFMA slot 0..6, so
+    // that the waves released together by the barrier do not queue 56 loads
+    // at the address unit before their first MFMA.
+    const int kload = min(kb + 3, nsteps - 1);
+    uint16_t* const yload = dyb[(P + 3) % 4];
     bf16x8_t a[2];
     a[0] = wfrag(wcur, 0);
     float ah = 0.0f;
@@ -246,6 +261,8 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     for (int u = 0; u < 16; ++u) {
       const int t = u / 4, i = u % 4;
       acc[i] = mfma_32x32x16(a[t & 1], b[t & 1][i], acc[i]);
+      if (u < 4) load_dyi(u, yload, kload);
+      else if (u < 7) load_wj(u - 4, wload, kload);
       if (i == 0 && t < 3) a[(t + 1) & 1] = wfrag(wcur, t + 1);
       if (u < 4) {
 #pragma unroll
