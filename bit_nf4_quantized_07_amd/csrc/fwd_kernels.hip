@@ -51,6 +51,8 @@ constexpr int kXTile = kFwdBM * kXRow;         // elements per X buffer
 constexpr int kXBufs = 4;
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= 11, expcnt and lgkmcnt not waited on.
 constexpr int kWaitVm11 = (11 & 0xF) | ((11 >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+// vmcnt <= 22, lgkmcnt = 0, expcnt not waited on (end of the prologue).
+constexpr int kWaitPro = (22 & 0xF) | ((22 >> 4) << 14) | (0x7 << 4) | (0 << 8);
 constexpr int kFwdUnroll = 4;                  // K-steps per loop iteration (register sets)
 
 struct FwdArgs {
@@ -195,9 +197,11 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     load_x(xbuf[j], min(j, nk - 1));
     load_w(wr[j], min(j, nk - 1));
   }
+  // Only step 0's eleven loads must have arrived (those of steps 1 and 2 may
+  // still be in flight) before the barrier publishes X(0).
   decode_all(wr[0], bf[0]);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitPro);
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[0][i] = xfrag(xbuf[0], i, 0);
 
