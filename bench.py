@@ -20,7 +20,9 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                    MFMA peak
   gemv             the small-M forward (W0 28672x8192, M = 1, 4, 16): bytes
                    the GEMV kernel must move over its average duration vs HBM
-  standalone       the load-time kernels (quantize, double quant, dequant) in GB/s
+  standalone       the load-time kernels (quantize, double quant, dequant) and the
+                   adapter merge in GB/s, with the merge's error against the
+                   unquantised base
   cpu_baseline     the CPU oracle timed on the host cores on a bounded sample
 """
 from __future__ import annotations
@@ -287,12 +289,14 @@ def run_gemv(args, q, torch, wl, lib, ev):
 
 
 def run_standalone(args, q, torch, lib, ev):
-    """The load-time kernels on the default workload's weight shape (4096 x
-    4096), event-timed per call over 8 rotated weight sets (more than the
-    last-level cache holds), in GB/s of the bytes each must move:
+    """The load-time kernels and the adapter merge on the default workload's
+    weight shape (4096 x 4096, r = 16), event-timed per call over 8 rotated
+    weight sets (more than the last-level cache holds), in GB/s of the bytes
+    each must move:
       nf4_quantize   fp32 in, packed nibbles + fp32 absmax out   (4 + 1/2 + 4/64 B/weight)
       double_quant   fp32 absmax in, 8-bit codes + scales + mean out
-      nf4_dequant    packed + codes + scales in, bf16 out         (1/2 + 1/64 + 2 B/weight, + scales)"""
+      nf4_dequant    packed + codes + scales in, bf16 out         (1/2 + 1/64 + 2 B/weight, + scales)
+      qlora_merge    as nf4_dequant, plus A and B in               (bf16(w_hat + s B A))"""
     N = K = 4096
     nb, nsets, n = N * K // 64, 8, max(args.steps * 3, 60)
     g = torch.Generator(device="cuda")
@@ -321,9 +325,19 @@ def run_standalone(args, q, torch, lib, ev):
         w = d["qw"]
         return lib.nf4_dequant(ptr(w.packed), ptr(w.codes), ptr(w.scales), ptr(w.mean), N, K,
                                64, 256, ptr(d["out"]), stream)
+    r, alpha = 16, 32.0
+    A = (torch.rand(r, K, generator=g, device="cuda") * 2 - 1) / K ** 0.5
+    B = torch.randn(N, r, generator=g, device="cuda") * 0.01
+    A, B = A.to(torch.bfloat16), B.to(torch.bfloat16)
+
+    def mrg(d):
+        w = d["qw"]
+        return lib.qlora_merge(ptr(w.packed), ptr(w.codes), ptr(w.scales), ptr(w.mean), N, K, 64,
+                               256, ptr(A), ptr(B), r, alpha, ptr(d["out"]), stream)
     calls = [("nf4_quantize", quant, N * K * 4 + N * K // 2 + nb * 4),
              ("double_quant", dq, nb * 4 + nb + nsc * 4 + 4),
-             ("nf4_dequant", deq, N * K // 2 + nb + nsc * 4 + 4 + N * K * 2)]
+             ("nf4_dequant", deq, N * K // 2 + nb + nsc * 4 + 4 + N * K * 2),
+             ("qlora_merge", mrg, N * K // 2 + nb + nsc * 4 + 4 + 2 * r * (N + K) + N * K * 2)]
     out = dict(shape=[N, K], sets=nsets, calls=n)
     for name, fn, nbytes in calls:
         for i in range(10):
@@ -341,6 +355,18 @@ def run_standalone(args, q, torch, lib, ev):
         out[name] = dict(median_us=round(med * 1e6, 2), min_us=round(float(np.min(d)) * 1e3, 2),
                          bytes=nbytes, GBps=round(nbytes / med / 1e9, 1),
                          frac_hbm=round(nbytes / med / 1e9 / PEAK_HBM_GBPS, 4))
+    # Merge error against the unquantised base: the merged weight of the last
+    # set versus W0 + s B A in fp64, and, for comparison, the same adapter
+    # merged into a bf16 copy of the base (the lossless serving path).
+    d = sets[(n - 1) % nsets]
+    assert mrg(d) == 0
+    torch.cuda.synchronize()
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    exact = f64(d["W"]) + np.float64(np.float32(alpha) / np.float32(r)) * (f64(B) @ f64(A))
+    nrm = np.linalg.norm(exact)
+    bf16_path = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16)
+    out["qlora_merge"]["rel_err_vs_unquantized"] = float(np.linalg.norm(f64(d["out"]) - exact) / nrm)
+    out["qlora_merge"]["rel_err_bf16_base_merge"] = float(np.linalg.norm(f64(bf16_path) - exact) / nrm)
     return out
 
 

@@ -39,6 +39,7 @@ SIGNATURES = {
     "qlora_linear_bwd": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F, _P,
                               _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
     "qlora_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I, _I]),
+    "qlora_merge": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P, _I, _F, _P, _P]),
     "silu_mul_fwd": (_I, [_P, _P, _I64, _P, _P]),
     "silu_mul_bwd": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "nf4_codebook": (_I, [_P]),
@@ -165,6 +166,21 @@ def nf4_dequant(qw: QuantizedWeight):
     _check("nf4_dequant", load_library().nf4_dequant(
         _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean), qw.N, qw.K,
         BLOCKSIZE, DQ_BLOCKSIZE, _ptr(out), _stream(out.device)))
+    return out
+
+
+def merge(qw: QuantizedWeight, A, B, alpha: float, out=None):
+    """-> bf16 [N, K]: bf16(w_hat + (alpha / r) B A), the adapter folded into
+    the dequantised base (qlora_merge)."""
+    torch = _torch()
+    _need_cuda(A, B)
+    r = A.shape[0]
+    if out is None:
+        out = torch.empty(qw.N, qw.K, dtype=torch.bfloat16, device=qw.packed.device)
+    _check("qlora_merge", load_library().qlora_merge(
+        _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean), qw.N, qw.K,
+        BLOCKSIZE, DQ_BLOCKSIZE, _ptr(A), _ptr(B), r, float(alpha), _ptr(out),
+        _stream(out.device)))
     return out
 
 

@@ -73,6 +73,10 @@ void set_kernel_timer(int kernel, hipEvent_t start, hipEvent_t stop);
 void timer_begin(int kernel, hipStream_t st);
 void timer_end(int kernel, hipStream_t st);
 
+// W_merged = bf16(w_hat + s B A), bf16 [N, K].
+hipError_t launch_merge(const NF4Weight& w, const uint16_t* A, const uint16_t* B, int r, float s,
+                        uint16_t* out, hipStream_t st);
+
 hipError_t launch_silu_mul_fwd(const uint16_t* G, const uint16_t* U, int64_t n, uint16_t* H,
                                hipStream_t st);
 hipError_t launch_silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* U,

@@ -12,6 +12,7 @@ namespace {
 constexpr int kBlock = 64;
 constexpr int kDQBlock = 256;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // keeps every tile index in int
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -40,6 +41,10 @@ int check_linear(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8
   if (st) return st;
   if (N % 8 != 0) return QLORA_ERR_SHAPE;
   if (r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_SHAPE;
+  // The kernels address X, dY, Y, dX and the packed weight with 32-bit
+  // buffer offsets and mark out-of-range lanes with offset 2^31.
+  if (M * K * 2 >= kMaxBufferBytes || M * N * 2 >= kMaxBufferBytes || N * K / 2 >= kMaxBufferBytes)
+    return QLORA_ERR_SHAPE;
   if (!isfinite(alpha)) return QLORA_ERR_ARG;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(codes) || !aligned16(scales) ||
       !aligned16(mean) || !aligned16(A) || !aligned16(B))
@@ -93,6 +98,24 @@ int nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales
     return QLORA_ERR_ALIGN;
   return launch_status(
       qlk::launch_nf4_dequant(packed, codes, scales, mean, N * K, W_bf16, as_stream(stream)));
+}
+
+int qlora_merge(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
+                const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* W_merged,
+                void* stream) {
+  if (!packed || !codes || !scales || !mean || !A || !B || !W_merged) return QLORA_ERR_NULL;
+  if (blocksize != kBlock || dq_blocksize != kDQBlock) return QLORA_ERR_UNSUPPORTED;
+  int st = check_weight_shape(N, K);
+  if (st) return st;
+  if (N % 8 != 0 || r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_SHAPE;
+  if (N * K > ((int64_t)1 << 40) || (N + 63) / 64 > 65535) return QLORA_ERR_SHAPE;
+  if (!isfinite(alpha)) return QLORA_ERR_ARG;
+  if (!aligned16(packed) || !aligned16(codes) || !aligned16(scales) || !aligned16(mean) ||
+      !aligned16(A) || !aligned16(B) || !aligned16(W_merged))
+    return QLORA_ERR_ALIGN;
+  return launch_status(qlk::launch_merge(weight(packed, codes, scales, mean, N, K), A, B, r,
+                                         alpha / (float)r, W_merged, as_stream(stream)));
 }
 
 size_t qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int r, int is_bwd) {

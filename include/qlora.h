@@ -49,7 +49,7 @@ extern "C" {
 #define QLORA_OK                 0
 #define QLORA_ERR_NULL          -1  /* a required pointer is NULL                   */
 #define QLORA_ERR_SHAPE         -2  /* M,N,K <= 0; K % 64; N % 8; r % 8 or r > 256;
-                                       N*K odd or too large                           */
+                                       N*K odd or too large; an operand >= 2 GiB      */
 #define QLORA_ERR_UNSUPPORTED   -3  /* blocksize != 64 or dq_blocksize != 256       */
 #define QLORA_ERR_ALIGN         -4  /* a pointer is not 16-byte aligned             */
 #define QLORA_ERR_WORKSPACE     -5  /* workspace NULL or smaller than required      */
@@ -109,8 +109,9 @@ int nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales
  * Accumulation is fp32; Y is rounded to bf16 once.  Results meet
  * |err|_F / |ref|_F <= 1e-2 and max|err| <= 3e-2 max|ref| against an exact
  * evaluation of the same bf16 inputs.
- * Requires 1 <= M, K % 64 == 0, N % 8 == 0, r % 8 == 0, 8 <= r <= 256, and
- * workspace_bytes >= qlora_workspace_bytes(M, K, N, r, 0). */
+ * Requires 1 <= M, K % 64 == 0, N % 8 == 0, r % 8 == 0, 8 <= r <= 256, each
+ * of X, Y (2 M K, 2 M N bytes) and the packed weight (N K / 2 bytes) under
+ * 2 GiB, and workspace_bytes >= qlora_workspace_bytes(M, K, N, r, 0). */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
                      const uint8_t* packed, const uint8_t* codes, const float* scales,
                      const float* mean, const uint16_t* A, const uint16_t* B,
@@ -138,6 +139,27 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K
 /* Bytes of device workspace the forward (is_bwd = 0) or backward (is_bwd = 1)
  * needs for these sizes; 0 means none.  Returns 0 for invalid sizes too. */
 size_t qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int r, int is_bwd);
+
+/* ---- serving: fold the adapter into the base ---------------------------- */
+
+/* W_merged = RNE_bf16( w_hat_bf16 + s (B A) ),  s = fp32(alpha / r).
+ * A 4-bit base must be dequantised before an adapter can be merged into it,
+ * and the merged weight keeps the base's quantisation error (llm-compass
+ * "QLoRA", 与 baseline 对比 table, row 部署合并, and 实现要点, the item on
+ * merging; auryth.ai "QLoRA", FAQ, the question on inference; skillbyai
+ * "QLoRA: Fine-Tuning on One Consumer GPU", "Quantized base plus LoRA").
+ *   w_hat_bf16  the weight nf4_dequant produces (same bits)
+ *   A  bf16 [r, K],  B  bf16 [N, r]
+ *   W_merged  bf16 [N, K] (caller-owned, overwritten)
+ * B A is accumulated in fp32 (MFMA), added with one fp32 fused multiply-add
+ * and rounded to bf16 once; each value is within one bf16 rounding step of
+ * the exactly evaluated merge.
+ * Requires K % 64 == 0, N % 8 == 0, r % 8 == 0, 8 <= r <= 256,
+ * blocksize == 64, dq_blocksize == 256, finite alpha. */
+int qlora_merge(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
+                const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* W_merged,
+                void* stream);
 
 /* ---- gated-MLP glue (not a QLoRA step; used by MLP workloads) ----------- */
 

@@ -26,6 +26,9 @@ Functions and what pins them (tests/test_oracle_*.py):
   forward/backward  exact directional derivatives, special cases (B=0, A=0,
                     X=I, one-hot dY), fp64 torch autograd
   silu glue         fp64 torch autograd
+  merge             B = 0 reduces to the dequantised base; constant
+                    adapters give the closed form W + alpha a b; hand-worked
+                    bf16 rounding ties; bf16 rounding against torch
 No function is "parity unpinned".
 """
 from .nf4 import (  # noqa: F401
@@ -35,5 +38,5 @@ from .nf4 import (  # noqa: F401
 )
 from .qlora import (  # noqa: F401
     lora_scale, forward, backward, silu_mul_forward, silu_mul_backward,
-    mlp_forward, mlp_backward,
+    mlp_forward, mlp_backward, merge, f64_to_bf16_bits,
 )

@@ -100,3 +100,31 @@ def mlp_backward(dY, X, saved, gate, up, down):
     dXu, dA_u, dB_u = backward(dUp, X, up["W_hat"], up["A"], up["B"],
                                up["alpha"], up["r"])
     return dXg + dXu, dict(gate=(dA_g, dB_g), up=(dA_u, dB_u), down=(dA_d, dB_d))
+
+
+# ---------------------------------------------------------------------------
+# Merging the adapter into the dequantised base (serving path)
+# ---------------------------------------------------------------------------
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round fp64 values to bf16 once (round to nearest, ties to even), as
+    uint16 bits.  Values are finite and normal in bf16 (|x| >= 2^-126)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1
+    q = np.rint(m * 256.0)                   # 8 significant bits, half to even
+    r = np.ldexp(q, e - 8)                   # exactly representable in bf16
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def merge(W_hat, A, B, alpha: float, r: int):
+    """W_merged = W_hat + s B A in fp64, s = fp32(alpha / r).
+
+    After training the adapter can be folded into the base for serving; for a
+    4-bit base the base must first be dequantised, and the merged weight then
+    carries the quantisation error of the base ([LC] 与 baseline 对比 table,
+    row 部署合并, and 实现要点, the item on merging with care; [AU] FAQ, the
+    question on inference; [SB] "Quantized base plus LoRA").  W_hat is the
+    bf16 dequantised weight [N, K]; the exact result is returned (round it
+    with f64_to_bf16_bits for the bf16 merged weight)."""
+    W_hat, A, B = _f64(W_hat), _f64(A), _f64(B)
+    return W_hat + lora_scale(alpha, r) * (B @ A)

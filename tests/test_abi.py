@@ -149,3 +149,35 @@ def test_silu_validation():
     assert lib.silu_mul_fwd(D, D, 64, MIS, None) == q.ERR_ALIGN
     assert lib.silu_mul_bwd(D, D, D, 64, D, None, None) == q.ERR_NULL
     assert lib.silu_mul_bwd(D, D, D, 0, D, D, None) == q.ERR_SHAPE
+
+
+def test_linear_size_limits():
+    """Operands of 2 GiB or more are refused (32-bit buffer offsets)."""
+    assert _fwd(M=1 << 18, K=1 << 12) == q.ERR_SHAPE          # X = 2 GiB
+    assert _fwd(M=1 << 18, N=1 << 12) == q.ERR_SHAPE          # Y = 2 GiB
+    assert _bwd(M=1 << 18, N=1 << 12) == q.ERR_SHAPE          # dY = 2 GiB
+    assert _fwd(N=1 << 16, K=1 << 16) == q.ERR_SHAPE          # packed = 2 GiB
+
+
+def test_merge_validation():
+    f = lib.qlora_merge
+    ok = (D, D, D, D, 256, 128, 64, 256, D, D, 16, 32.0, D, None)   # valid: never called as is
+
+    def call(**kw):
+        a = list(ok)
+        names = ["packed", "codes", "scales", "mean", "N", "K", "bs", "dqbs", "A", "B", "r",
+                 "alpha", "out", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+    assert call(out=None) == q.ERR_NULL
+    assert call(A=None) == q.ERR_NULL
+    assert call(bs=32) == q.ERR_UNSUPPORTED
+    assert call(dqbs=128) == q.ERR_UNSUPPORTED
+    assert call(K=100) == q.ERR_SHAPE
+    assert call(N=12) == q.ERR_SHAPE
+    assert call(r=12) == q.ERR_SHAPE
+    assert call(r=264) == q.ERR_SHAPE
+    assert call(alpha=float("nan")) == q.ERR_ARG
+    assert call(B=MIS) == q.ERR_ALIGN
+    assert call(out=MIS) == q.ERR_ALIGN
