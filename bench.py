@@ -18,6 +18,8 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                    average duration (HIP events recorded on the launch stream
                    in a second pass over the same K steps) vs the dense bf16
                    MFMA peak
+  lora_bf16_base   the same step with an unquantised bf16 base weight (LoRA
+                   versus QLoRA), and the QLoRA / LoRA step-time ratio
   gemv             the small-M forward (W0 28672x8192, M = 1, 4, 16): bytes
                    the GEMV kernel must move over its average duration vs HBM
   standalone       the load-time kernels (quantize, double quant, dequant) and the
@@ -174,11 +176,11 @@ def make_linear_sets(q, torch, wl, cfg_name, idx, M, sets):
     return out
 
 
-def linear_step(q, d, ws):
+def linear_step(q, d, ws, weight="qw"):
     lin = d["lin"]
-    q.linear_fwd(d["X"], d["qw"], d["A"], d["B"], lin.alpha, out=d["Y"], T_out=d["T"],
+    q.linear_fwd(d["X"], d[weight], d["A"], d["B"], lin.alpha, out=d["Y"], T_out=d["T"],
                  workspace=ws)
-    q.linear_bwd(d["dY"], d["X"], d["qw"], d["A"], d["B"], lin.alpha, T=d["T"],
+    q.linear_bwd(d["dY"], d["X"], d[weight], d["A"], d["B"], lin.alpha, T=d["T"],
                  dX_out=d["dX"], dA_out=d["dA"], dB_out=d["dB"], workspace=ws)
 
 
@@ -237,11 +239,27 @@ def run_linear(args, q, torch, wl, lib, ev):
                     traffic=traffic_for(dom, units),
                     avg_us=round(kd["avg_us"], 2))
     value = flops / (ms * 1e-3) / 1e12
+    # The same step with an unquantised bf16 base (the dequantised weight, so
+    # the values are identical): LoRA on a bf16 base versus QLoRA, the
+    # comparison the pages quantify as 20-40 % slower per step.
+    for d in sets:
+        d["Wbf"] = q.nf4_dequant(d["qw"])
+    for i in range(args.warmup):
+        linear_step(q, sets[i % len(sets)], ws, "Wbf")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        linear_step(q, sets[i % len(sets)], ws, "Wbf")
+    torch.cuda.synchronize()
+    ms_bf16 = (time.perf_counter() - t0) * 1e3 / K
+    lora_bf16 = dict(ms_per_step=round(ms_bf16, 4),
+                     value=round(flops / (ms_bf16 * 1e-3) / 1e12, 2), unit="TFLOP/s",
+                     qlora_step_over_lora_step=round(ms / ms_bf16, 4))
     config = dict(workload=cfg.name, M=M, N=lin.N, K=lin.K, r=lin.r, alpha=lin.alpha,
                   blocksize=64, dq_blocksize=256, input_sets=args.sets,
                   step="qlora_linear_fwd + qlora_linear_bwd",
                   flops_per_step=flops)
-    return dict(value=value, ms=ms, config=config, roofline=roofline,
+    return dict(value=value, ms=ms, config=config, roofline=roofline, lora_bf16=lora_bf16,
                 kernels={k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()})
 
 
@@ -675,7 +693,8 @@ def main():
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(lin["ms"], 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
                 data="synthetic", config=lin["config"], roofline=lin["roofline"],
-                cpu_baseline=cpu, kernels=lin["kernels"], gemv=gemv, standalone=standalone,
+                cpu_baseline=cpu, kernels=lin["kernels"], lora_bf16_base=lin["lora_bf16"],
+                gemv=gemv, standalone=standalone,
                 source_hash=source_hash())
     print(json.dumps(line), flush=True)
 

@@ -40,6 +40,10 @@ SIGNATURES = {
                               _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
     "qlora_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I, _I]),
     "qlora_merge": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P, _I, _F, _P, _P]),
+    "qlora_linear_fwd_bf16": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _I, _F, _P, _P, _P,
+                                   ctypes.c_size_t, _P]),
+    "qlora_linear_bwd_bf16": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _I, _F, _P, _P, _P,
+                                   _P, _I, _P, ctypes.c_size_t, _P]),
     "silu_mul_fwd": (_I, [_P, _P, _I64, _P, _P]),
     "silu_mul_bwd": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "nf4_codebook": (_I, [_P]),
@@ -214,30 +218,47 @@ def _ws(device, nbytes):
     return _default_ws[key].get(nbytes)
 
 
-def linear_fwd(X, qw: QuantizedWeight, A, B, alpha: float, save_T: bool = True,
+def _weight_rows(w) -> int:
+    return w.N if isinstance(w, QuantizedWeight) else w.shape[0]
+
+
+def linear_fwd(X, qw, A, B, alpha: float, save_T: bool = True,
                out=None, T_out=None, workspace=None):
-    """Y = X W_hat^T + (alpha/r) (X A^T) B^T.  Returns (Y, T or None)."""
+    """Y = X W_hat^T + (alpha/r) (X A^T) B^T.  Returns (Y, T or None).
+
+    `qw` is a QuantizedWeight (NF4, qlora_linear_fwd) or a bf16 tensor [N, K]
+    (unquantised base, qlora_linear_fwd_bf16)."""
     torch = _torch()
     M, K = X.shape
     r = A.shape[0]
+    N = _weight_rows(qw)
     _need_cuda(X, A, B)
-    Y = out if out is not None else torch.empty(M, qw.N, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
     T = T_out if T_out is not None else (
         torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if save_T else None)
-    nb = workspace_bytes(M, K, qw.N, r, False)
+    nb = workspace_bytes(M, K, N, r, False)
     ws, wsb = (workspace.get(nb) if workspace is not None else _ws(X.device, nb))
-    _check("qlora_linear_fwd", load_library().qlora_linear_fwd(
-        _ptr(X), M, K, qw.N, _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean),
-        _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(T), _ptr(ws), wsb, _stream(X.device)))
+    lib = load_library()
+    if isinstance(qw, QuantizedWeight):
+        _check("qlora_linear_fwd", lib.qlora_linear_fwd(
+            _ptr(X), M, K, N, _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean),
+            _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(T), _ptr(ws), wsb, _stream(X.device)))
+    else:
+        _need_cuda(qw)
+        _check("qlora_linear_fwd_bf16", lib.qlora_linear_fwd_bf16(
+            _ptr(X), M, K, N, _ptr(qw), _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(T),
+            _ptr(ws), wsb, _stream(X.device)))
     return Y, T
 
 
-def linear_bwd(dY, X, qw: QuantizedWeight, A, B, alpha: float, T=None, need_dX: bool = True,
+def linear_bwd(dY, X, qw, A, B, alpha: float, T=None, need_dX: bool = True,
                accumulate_into=None, dX_out=None, dA_out=None, dB_out=None, workspace=None):
-    """Returns (dX bf16 [M,K] or None, dA fp32 [r,K], dB fp32 [N,r])."""
+    """Returns (dX bf16 [M,K] or None, dA fp32 [r,K], dB fp32 [N,r]).  `qw` as in
+    linear_fwd (QuantizedWeight or a bf16 [N, K] tensor)."""
     torch = _torch()
     M, K = X.shape
     r = A.shape[0]
+    N = _weight_rows(qw)
     _need_cuda(dY, X, A, B, T)
     flags = 0
     if accumulate_into is not None:
@@ -248,14 +269,21 @@ def linear_bwd(dY, X, qw: QuantizedWeight, A, B, alpha: float, T=None, need_dX: 
     else:
         dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device) if need_dX else None
     dA = dA_out if dA_out is not None else torch.empty(r, K, dtype=torch.float32, device=X.device)
-    dB = dB_out if dB_out is not None else torch.empty(qw.N, r, dtype=torch.float32,
+    dB = dB_out if dB_out is not None else torch.empty(N, r, dtype=torch.float32,
                                                        device=X.device)
-    nb = workspace_bytes(M, K, qw.N, r, True)
+    nb = workspace_bytes(M, K, N, r, True)
     ws, wsb = (workspace.get(nb) if workspace is not None else _ws(X.device, nb))
-    _check("qlora_linear_bwd", load_library().qlora_linear_bwd(
-        _ptr(dY), _ptr(X), M, K, qw.N, _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales),
-        _ptr(qw.mean), _ptr(A), _ptr(B), r, float(alpha), _ptr(T), _ptr(dX), _ptr(dA), _ptr(dB),
-        flags, _ptr(ws), wsb, _stream(X.device)))
+    lib = load_library()
+    if isinstance(qw, QuantizedWeight):
+        _check("qlora_linear_bwd", lib.qlora_linear_bwd(
+            _ptr(dY), _ptr(X), M, K, N, _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales),
+            _ptr(qw.mean), _ptr(A), _ptr(B), r, float(alpha), _ptr(T), _ptr(dX), _ptr(dA),
+            _ptr(dB), flags, _ptr(ws), wsb, _stream(X.device)))
+    else:
+        _need_cuda(qw)
+        _check("qlora_linear_bwd_bf16", lib.qlora_linear_bwd_bf16(
+            _ptr(dY), _ptr(X), M, K, N, _ptr(qw), _ptr(A), _ptr(B), r, float(alpha), _ptr(T),
+            _ptr(dX), _ptr(dA), _ptr(dB), flags, _ptr(ws), wsb, _stream(X.device)))
     return dX, dA, dB
 
 

@@ -52,8 +52,7 @@ constexpr int kWTile = kDxStepN * kDxBK;   // elements per weight buffer
 constexpr int kDxUnroll = 4;
 // s_waitcnt immediates (gfx9 encoding), expcnt not waited on:
 // vmcnt <= 7, lgkmcnt <= 4 (end of a step); vmcnt <= 14, lgkmcnt = 0 (prologue).
-constexpr int kDxWaitEnd = (7 & 0xF) | ((7 >> 4) << 14) | (0x7 << 4) | (4 << 8);
-constexpr int kDxWaitPro = (14 & 0xF) | ((14 >> 4) << 14) | (0x7 << 4) | (0 << 8);
+constexpr int dx_wait(int vm, int lgkm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (lgkm << 8); }
 
 struct DxArgs {
   const uint16_t* dY;   // [M, N] bf16
@@ -72,6 +71,11 @@ struct DxWRegs { uint2 p; uint32_t code; float sc; };
 
 __device__ __forceinline__ int wswz(int n) { return ((n & 3) << 2) | ((n >> 2) & 3); }
 
+// BF16W: the base weight is plain bf16 (g.w.bf16): each step's 64 x 128
+// weight tile is copied into LDS by buffer loads that write LDS directly (two
+// per wave, the same swizzled layout the decode writes), with nothing to
+// decode -- the same kernel with the dequantisation switched off.
+template <bool BF16W>
 __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t dy0[kDyTile];
   __shared__ __attribute__((aligned(16))) uint16_t dy1[kDyTile];
@@ -92,7 +96,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   const int64_t k0 = (int64_t)tk * kDxBK;
   const int64_t N = g.w.N, K = g.w.K, nkb = K / kBlock;
   const int nsteps = (int)(N / kDxStepN);
-  const float mean = g.w.mean[0];
+  const float mean = BF16W ? 0.0f : g.w.mean[0];
   const float qlev = nf4_level(lane & 15);   // source of the level lookups
 
   // dY tile loads: wave w fills rows 32w .. 32w+31, 8 rows per load.
@@ -151,6 +155,24 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   auto load_w = [&](DxWRegs& R, int kb) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) load_wj(j, R, kb);
+  };
+  // bf16 weight tile (rows 64 kb .. +63, features k0 .. k0+127) into LDS:
+  // load i of wave w fills rows 8 w + 4 i .. +3 (1 KB); lane L lands at row
+  // 8 w + 4 i + L / 16, physical piece L % 16, i.e. logical piece
+  // (L % 16) ^ wswz(row).
+  const __amdgpu_buffer_rsrc_t rwb = rsrc_whole(g.w.bf16, (uint32_t)(BF16W ? N * K * 2 : 0));
+  uint32_t wboff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * wave + 4 * i + (lane >> 4);
+    const int64_t col = k0 + 8 * ((lane & 15) ^ wswz(row));
+    wboff[i] = col < K ? (uint32_t)(((int64_t)row * K + col) * 2) : kOOB;
+  }
+  auto load_wbi = [&](int i, uint16_t* buf, int kb) {
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * kDxStepN * (uint32_t)K * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rwb, (__attribute__((address_space(3))) void*)(buf + (8 * wave + 4 * i) * kDxBK), 16,
+        wboff[i], soff, 0, 0);
   };
   auto word = [](const DxWRegs& R, int t) -> uint32_t { return t == 0 ? R.p.x : R.p.y; };
   // NF4 level of the nibble at bits b .. b+3 of w.  ds_bpermute reads lane
@@ -216,17 +238,26 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   DxWRegs wr[4];
   bf16x8_t b[2][4];   // dY operands
   __syncthreads();
+  if constexpr (BF16W) {
+    // W(0) into weight buffer 0, then dY(0..2); W(j+1) is copied during step j.
+    load_wbi(0, wtb[0], 0);
+    load_wbi(1, wtb[0], 0);
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    load_dy(dyb[j], min(j, nsteps - 1));
-    load_w(wr[j], min(j, nsteps - 1));
+    for (int j = 0; j < 3; ++j) load_dy(dyb[j], min(j, nsteps - 1));
+    __builtin_amdgcn_s_waitcnt(dx_wait(8, 0));   // W(0) and dY(0) arrived
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      load_dy(dyb[j], min(j, nsteps - 1));
+      load_w(wr[j], min(j, nsteps - 1));
+    }
+    // Only step 0's seven loads must have arrived (those of steps 1 and 2
+    // may still be in flight) before its weight is decoded and the barrier
+    // publishes dY(0) and W(0).
+    __builtin_amdgcn_s_waitcnt(dx_wait(14, 0));
+    decode_all(wr[0], wtb[0]);
+    __builtin_amdgcn_s_waitcnt(dx_wait(14, 0));
   }
-  // Only step 0's seven loads must have arrived (those of steps 1 and 2 may
-  // still be in flight) before its weight is decoded and the barrier
-  // publishes dY(0) and W(0).
-  __builtin_amdgcn_s_waitcnt(kDxWaitPro);
-  decode_all(wr[0], wtb[0]);
-  __builtin_amdgcn_s_waitcnt(kDxWaitPro);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 4; ++i) b[0][i] = yfrag(dyb[0], i, 0);
@@ -261,25 +292,33 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     for (int u = 0; u < 16; ++u) {
       const int t = u / 4, i = u % 4;
       acc[i] = mfma_32x32x16(a[t & 1], b[t & 1][i], acc[i]);
-      if (u < 4) load_dyi(u, yload, kload);
-      else if (u < 7) load_wj(u - 4, wload, kload);
+      if constexpr (BF16W) {
+        // W(kb+1) first (it must be complete at this step's end), then dY(kb+3)
+        if (u < 2) load_wbi(u, wnext, min(kb + 1, nsteps - 1));
+        else if (u < 6) load_dyi(u - 2, yload, kload);
+      } else {
+        if (u < 4) load_dyi(u, yload, kload);
+        else if (u < 7) load_wj(u - 4, wload, kload);
+      }
       if (i == 0 && t < 3) a[(t + 1) & 1] = wfrag(wcur, t + 1);
-      if (u < 4) {
+      if constexpr (!BF16W) {
+        if (u < 4) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int v = 2 * u + e;   // byte v % 4 of word v / 4: element 2v high, 2v+1 low
-          lh[v] = lev(word(wdec, v / 4), 8 * (v % 4) + 4);
-          ll[v] = lev(word(wdec, v / 4), 8 * (v % 4));
+          for (int e = 0; e < 2; ++e) {
+            const int v = 2 * u + e;   // byte v % 4 of word v / 4: element 2v high, 2v+1 low
+            lh[v] = lev(word(wdec, v / 4), 8 * (v % 4) + 4);
+            ll[v] = lev(word(wdec, v / 4), 8 * (v % 4));
+          }
         }
-      }
-      if (u == 1) ah = absmax(wdec);
-      if (u >= 6 && u < 14) {
-        const int v = u - 6;
-        o[v] = pack_bf16x2(lh[v] * ah, ll[v] * ah);
-      }
-      if (u == 13 || u == 14) {
-        const int q = u - 13;
-        wstore(wnext, q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+        if (u == 1) ah = absmax(wdec);
+        if (u >= 6 && u < 14) {
+          const int v = u - 6;
+          o[v] = pack_bf16x2(lh[v] * ah, ll[v] * ah);
+        }
+        if (u == 13 || u == 14) {
+          const int q = u - 13;
+          wstore(wnext, q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+        }
       }
       if (t < 3) b[(t + 1) & 1][i] = yfrag(ycur, i, t + 1);
       if (u == 15) {
@@ -289,10 +328,11 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // Before step kb+1: dY(kb+2) (loaded during step kb-1) in LDS from every
-    // wave (at most this step's 7 global loads outstanding) and this wave's
-    // decoded weight stores done (at most the 4 operand reads of slot 15
-    // outstanding), then the barrier.
-    __builtin_amdgcn_s_waitcnt(kDxWaitEnd);
+    // wave (at most this step's 7 global loads outstanding; with a bf16
+    // weight, at most this step's 4 dY loads, so that W(kb+1) has arrived)
+    // and this wave's decoded weight stores done (at most the 4 operand
+    // reads of slot 15 outstanding), then the barrier.
+    __builtin_amdgcn_s_waitcnt(BF16W ? dx_wait(4, 4) : dx_wait(7, 4));
     __builtin_amdgcn_s_barrier();
   };
   for (int kb = 0; kb < nsteps; kb += kDxUnroll) {
@@ -361,8 +401,12 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
   g.accumulate = accumulate ? 1 : 0;
   g.tiles_m = (int)((M + kDxBM - 1) / kDxBM);
   g.tiles_k = (int)((w.K + kDxBK - 1) / kDxBK);
-  g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2, (double)kDxBK * w.N * 0.52);
-  hipLaunchKernelGGL(k_dx_nf4, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
+  g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2,
+                        (double)kDxBK * w.N * (w.bf16 ? 2.0 : 0.52));
+  if (w.bf16)
+    hipLaunchKernelGGL(k_dx_nf4<true>, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
+  else
+    hipLaunchKernelGGL(k_dx_nf4<false>, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
   return hipGetLastError();
 }
 

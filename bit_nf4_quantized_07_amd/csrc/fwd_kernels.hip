@@ -49,10 +49,10 @@ constexpr int kFwdBN = 4 * kFwdWaveN;          // weight rows per tile
 constexpr int kXRow = kBlock;                  // LDS row of the X tile (elements, swizzled)
 constexpr int kXTile = kFwdBM * kXRow;         // elements per X buffer
 constexpr int kXBufs = 4;
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= 11, expcnt and lgkmcnt not waited on.
-constexpr int kWaitVm11 = (11 & 0xF) | ((11 >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-// vmcnt <= 22, lgkmcnt = 0, expcnt not waited on (end of the prologue).
-constexpr int kWaitPro = (22 & 0xF) | ((22 >> 4) << 14) | (0x7 << 4) | (0 << 8);
+// s_waitcnt immediates (gfx9 encoding), expcnt not waited on: vmcnt <= the
+// loads of one step, lgkmcnt not waited on (end of a step); vmcnt <= the
+// loads of two steps, lgkmcnt = 0 (end of the prologue).
+constexpr int wait_vm(int n, int lgkm) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (lgkm << 8); }
 constexpr int kFwdUnroll = 4;                  // K-steps per loop iteration (register sets)
 
 struct FwdArgs {
@@ -67,14 +67,21 @@ struct FwdArgs {
   int tiles_m, tiles_n, group_m;
 };
 
-struct FwdWRegs { uint4 p; uint32_t code; float sc; };
+struct FwdWRegs { uint4 p; uint32_t code; float sc; };   // NF4: 32 weights + block constant
+struct FwdWRegsB { uint4 p[4]; };                          // bf16: 32 weights
 struct FwdBFrag { uint32_t d[4][4]; };   // [MFMA step][dword]
 
 __device__ __forceinline__ bf16x8_t as_frag(const uint32_t (&d)[4]) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
+// BF16W: the base weight is plain bf16 (g.w.bf16) and there is nothing to
+// decode: the same kernel with the dequantisation switched off.
+template <bool BF16W>
 __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
+  using WRegs = std::conditional_t<BF16W, FwdWRegsB, FwdWRegs>;
+  constexpr int kWLoads = BF16W ? 4 : 3;          // weight loads per step
+  constexpr int kLoads = 8 + kWLoads;             // global loads per step
   // Tables first (low LDS addresses fit the instructions' offset field),
   // then the X buffers as four separate objects, so that the compiler can
   // tell that a load into one buffer does not alias reads of another.
@@ -96,7 +103,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   const int m0 = tm * kFwdBM;
   const int64_t K = g.w.K, N = g.w.N, nkb = K / kBlock;
   const int nk = (int)nkb;
-  const float mean = g.w.mean[0];
+  const float mean = BF16W ? 0.0f : g.w.mean[0];
 
   // X tile loads: wave w, load i fills rows 64 w + 8 i .. +7 (1 KB of LDS);
   // lane L lands at LDS offset 16 L, i.e. row 64 w + 8 i + L / 8, physical
@@ -137,22 +144,29 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
         rx, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * j) * kXRow), 16,
         xoff[j], k * (kBlock * 2), 0, 0);
   };
-  auto load_wj = [&](int j, FwdWRegs& R, int kb) {
+  // bf16 weight: the lane's 32 weights of a step are 64 contiguous bytes.
+  const __amdgpu_buffer_rsrc_t rb = rsrc_whole(g.w.bf16, (uint32_t)(BF16W ? N * K * 2 : 0));
+  const uint32_t boff = nvalid ? (uint32_t)((nrow * K + 32 * h) * 2) : kOOB;
+  auto load_wj = [&](int j, WRegs& R, int kb) {
     const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
-    if (j == 0)
-      R.p = bload128s(rp, poff, k * (kBlock / 2));
-    else if (j == 1)
-      R.code = bload8s(rc, coff, k);
-    else
-      R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + k) / kDQBlock) * 4u));
+    if constexpr (BF16W) {
+      R.p[j] = bload128s(rb, boff == kOOB ? kOOB : boff + 16u * j, k * (kBlock * 2));
+    } else {
+      if (j == 0)
+        R.p = bload128s(rp, poff, k * (kBlock / 2));
+      else if (j == 1)
+        R.code = bload8s(rc, coff, k);
+      else
+        R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + k) / kDQBlock) * 4u));
+    }
   };
   auto load_x = [&](uint16_t* buf, int kb) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) load_xj(j, buf, kb);
   };
-  auto load_w = [&](FwdWRegs& R, int kb) {
+  auto load_w = [&](WRegs& R, int kb) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) load_wj(j, R, kb);
+    for (int j = 0; j < kWLoads; ++j) load_wj(j, R, kb);
   };
   auto word = [](const FwdWRegs& R, int t) -> uint32_t {
     return t == 0 ? R.p.x : t == 1 ? R.p.y : t == 2 ? R.p.z : R.p.w;
@@ -188,7 +202,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   // Register sets: W(j) in wr[j % 4] from its load (step j-3) to its decode
   // (step j-1); the decoded W(j) in bf[j % 2] during step j.  X(j) is in LDS
   // buffer j % 4 from its load (step j-3) to step j.
-  FwdWRegs wr[4];
+  WRegs wr[4];
   FwdBFrag bf[2];
   bf16x8_t a[2][8];
   __syncthreads();   // tables
@@ -197,10 +211,10 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     load_x(xbuf[j], min(j, nk - 1));
     load_w(wr[j], min(j, nk - 1));
   }
-  // Only step 0's eleven loads must have arrived (those of steps 1 and 2 may
-  // still be in flight) before the barrier publishes X(0).
-  decode_all(wr[0], bf[0]);
-  __builtin_amdgcn_s_waitcnt(kWaitPro);
+  // Only step 0's loads must have arrived (those of steps 1 and 2 may still
+  // be in flight) before the barrier publishes X(0).
+  if constexpr (!BF16W) decode_all(wr[0], bf[0]);
+  __builtin_amdgcn_s_waitcnt(wait_vm(2 * kLoads, 0));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[0][i] = xfrag(xbuf[0], i, 0);
@@ -208,8 +222,8 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   // One K-step; P = kb % kFwdUnroll selects the register sets.
   auto step = [&](auto Pc, int kb) {
     constexpr int P = decltype(Pc)::value;
-    const FwdWRegs& wdec = wr[(P + 1) % 4];
-    FwdWRegs& wload = wr[(P + 3) % 4];
+    const WRegs& wdec = wr[(P + 1) % 4];
+    WRegs& wload = wr[(P + 3) % 4];
     const FwdBFrag& bc = bf[P % 2];
     FwdBFrag& bn = bf[(P + 1) % 2];
     // kb % 4 == P: the loop starts at 0 and steps by 4
@@ -223,7 +237,8 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     // not queue 44 loads at the address unit before their first MFMA.
     const int kload = min(kb + 3, nk - 1);
     uint16_t* const xload = xbuf[(P + 3) % kXBufs];
-    const float q8v = q8[wdec.code];
+    float q8v = 0.0f;
+    if constexpr (!BF16W) q8v = q8[wdec.code];
     float ah = 0.0f;
     float lh[16], ll[16];
     uint32_t nh[4], nl[4];
@@ -231,34 +246,39 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
       const int t = u / 8, i = u % 8;
-      acc[i] = mfma_32x32x16(as_frag(bc.d[t]), a[t & 1][i], acc[i]);
+      if constexpr (BF16W)
+        acc[i] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, wr[P].p[t]), a[t & 1][i], acc[i]);
+      else
+        acc[i] = mfma_32x32x16(as_frag(bc.d[t]), a[t & 1][i], acc[i]);
       if (u < 8) load_xj(u, xload, kload);
-      else if (u < 11) load_wj(u - 8, wload, kload);
+      else if (u < 8 + kWLoads) load_wj(u - 8, wload, kload);
       if (t < 3) a[(t + 1) & 1][i] = xfrag(xcur, i, t + 1);
       else a[0][i] = xfrag(xnext, i, 0);
-      if (u < 16) {
-        if (u % 4 == 0) {
-          nh[u / 4] = hi4(word(wdec, u / 4));
-          nl[u / 4] = lo4(word(wdec, u / 4));
+      if constexpr (!BF16W) {
+        if (u < 16) {
+          if (u % 4 == 0) {
+            nh[u / 4] = hi4(word(wdec, u / 4));
+            nl[u / 4] = lo4(word(wdec, u / 4));
+          }
+          lh[u] = level(nh[u / 4], u % 4);
+          ll[u] = level(nl[u / 4], u % 4);
         }
-        lh[u] = level(nh[u / 4], u % 4);
-        ll[u] = level(nl[u / 4], u % 4);
-      }
-      if (u == 2) {
+        if (u == 2) {
 #pragma clang fp contract(off)
-        const float p = q8v * wdec.sc;
-        ah = p + mean;
-      }
-      if (u >= 16) {
-        const int v = u - 16;
-        bn.d[v / 4][v % 4] = pack_bf16x2(lh[v] * ah, ll[v] * ah);
+          const float p = q8v * wdec.sc;
+          ah = p + mean;
+        }
+        if (u >= 16) {
+          const int v = u - 16;
+          bn.d[v / 4][v % 4] = pack_bf16x2(lh[v] * ah, ll[v] * ah);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // X(kb+2) (loaded during step kb-1) must be in LDS, from every wave,
-    // before step kb+1 reads it: wait until at most this step's 11 loads
-    // are outstanding, then barrier.
-    __builtin_amdgcn_s_waitcnt(kWaitVm11);
+    // before step kb+1 reads it: wait until at most this step's loads are
+    // outstanding, then barrier.
+    __builtin_amdgcn_s_waitcnt(wait_vm(kLoads, 0xF));
     __builtin_amdgcn_s_barrier();
   };
   for (int kb = 0; kb < nk; kb += kFwdUnroll) {
@@ -320,8 +340,12 @@ hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, cons
   g.X = X; g.M = (int)M; g.w = w; g.T = T; g.B = B; g.r = r; g.s = s; g.Y = Y;
   g.tiles_m = (int)((M + kFwdBM - 1) / kFwdBM);
   g.tiles_n = (int)((w.N + kFwdBN - 1) / kFwdBN);
-  g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * w.K * 2, (double)kFwdBN * w.K * 0.52);
-  hipLaunchKernelGGL(k_fwd_nf4, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
+  g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * w.K * 2,
+                        (double)kFwdBN * w.K * (w.bf16 ? 2.0 : 0.52));
+  if (w.bf16)
+    hipLaunchKernelGGL(k_fwd_nf4<true>, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

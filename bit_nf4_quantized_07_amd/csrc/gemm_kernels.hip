@@ -786,7 +786,7 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   char* base = reinterpret_cast<char*>(ws);
   uint16_t* T = T_out ? T_out : reinterpret_cast<uint16_t*>(base + plan.off_T);
   float* part = reinterpret_cast<float*>(base + plan.off_part);
-  if (plan.gemv) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st);
+  if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st);
   QLK_TRY(compute_T(X, M, K, A, r, T, st));
   GemmArgs g{};
   g.a1 = opnd(X, K, (int)M, M);
@@ -801,6 +801,11 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   hipError_t e;
   if (!QLK_FWD_TILE_ENGINE && fwd_nf4_supported(K)) {
     e = launch_fwd_nf4(X, M, w, T, B, r, s, Y, st);
+  } else if (w.bf16) {
+    g.b1 = opnd(w.bf16, K, (int)N, N);
+    e = launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdBF16K<128, kBK, false>,
+                    LdBF16K<128, kBK, false>, LdBF16K<128, kBK, true>, EPI_BF16>(
+        g, 1, 128.0 * K * 2, 128.0 * K * 2, st);
   } else if (M >= QLK_FWD_TALL_MIN_M) {
     e = launch_gemm<256, 128, kBK, LdBF16K<256, kBK, false>, LdNF4K<128>, LdBF16K<256, kBK, false>,
                     LdBF16K<128, kBK, true>, EPI_BF16>(g, 1, 256.0 * K * 2, 128.0 * K * 0.52, st);
@@ -841,12 +846,21 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     g.c1_len = (int)N; g.c1_split = (int)N; g.c2_len = r;
     g.out = dX; g.ldo = K; g.accumulate = accumulate_dx ? 1 : 0;
     timer_begin(TK_DX_GEMM, st);
-    const hipError_t e = (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N))
-        ? launch_dx_nf4(dY, M, w, U, A, r, s, dX, accumulate_dx, st)
-        : launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
-                                     LdNF4T<QLK_DX_BN>, LdBF16K<QLK_DX_BM, kBK, false>,
-                                     LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
-        g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 0.52, st);
+    hipError_t e;
+    if (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N)) {
+      e = launch_dx_nf4(dY, M, w, U, A, r, s, dX, accumulate_dx, st);
+    } else if (w.bf16) {
+      g.b1 = opnd(w.bf16, K, (int)K, N);   // transposed load of W [N, K]: rows k, contraction n
+      e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
+                      LdBF16T<QLK_DX_BN, kBK, false>, LdBF16K<QLK_DX_BM, kBK, false>,
+                      LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
+          g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 2, st);
+    } else {
+      e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
+                      LdNF4T<QLK_DX_BN>, LdBF16K<QLK_DX_BM, kBK, false>,
+                      LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
+          g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 0.52, st);
+    }
     timer_end(TK_DX_GEMM, st);
     QLK_TRY(e);
   }

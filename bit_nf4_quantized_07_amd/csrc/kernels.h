@@ -12,13 +12,16 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, 
 hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
                               const float* mean, int64_t numel, uint16_t* out, hipStream_t st);
 
-// Quantised base weight, as stored.
+// Base weight [N, K] as stored: NF4 (packed, codes, scales, mean) or, for
+// the unquantised comparison path, plain bf16 (`bf16` non-null, the NF4
+// fields unused).
 struct NF4Weight {
   const uint8_t* packed;
   const uint8_t* codes;
   const float* scales;
   const float* mean;
   int64_t N, K;
+  const uint16_t* bf16 = nullptr;
 };
 
 // Token counts up to this take the small-M (GEMV) forward.

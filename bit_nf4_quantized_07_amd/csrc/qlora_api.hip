@@ -32,24 +32,41 @@ int check_weight_shape(int64_t N, int64_t K) {
   return QLORA_OK;
 }
 
-int check_linear(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* packed,
-                 const uint8_t* codes, const float* scales, const float* mean, const uint16_t* A,
-                 const uint16_t* B, int r, float alpha) {
-  if (!X || !packed || !codes || !scales || !mean || !A || !B) return QLORA_ERR_NULL;
+// Checks shared by both weight formats; `weight_bytes` is the size of the
+// stored base weight the kernels address with buffer offsets.
+int check_linear_common(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* A,
+                        const uint16_t* B, int r, float alpha, bool weight_null, int64_t weight_bytes) {
+  if (!X || !A || !B || weight_null) return QLORA_ERR_NULL;
   if (M <= 0 || M > kMaxDim) return QLORA_ERR_SHAPE;
   int st = check_weight_shape(N, K);
   if (st) return st;
   if (N % 8 != 0) return QLORA_ERR_SHAPE;
   if (r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_SHAPE;
-  // The kernels address X, dY, Y, dX and the packed weight with 32-bit
+  // The kernels address X, dY, Y, dX and the stored weight with 32-bit
   // buffer offsets and mark out-of-range lanes with offset 2^31.
-  if (M * K * 2 >= kMaxBufferBytes || M * N * 2 >= kMaxBufferBytes || N * K / 2 >= kMaxBufferBytes)
+  if (M * K * 2 >= kMaxBufferBytes || M * N * 2 >= kMaxBufferBytes || weight_bytes >= kMaxBufferBytes)
     return QLORA_ERR_SHAPE;
   if (!isfinite(alpha)) return QLORA_ERR_ARG;
-  if (!aligned16(X) || !aligned16(packed) || !aligned16(codes) || !aligned16(scales) ||
-      !aligned16(mean) || !aligned16(A) || !aligned16(B))
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+int check_linear(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* packed,
+                 const uint8_t* codes, const float* scales, const float* mean, const uint16_t* A,
+                 const uint16_t* B, int r, float alpha) {
+  const bool wnull = !packed || !codes || !scales || !mean;
+  int st = check_linear_common(X, M, K, N, A, B, r, alpha, wnull, wnull ? 0 : N * K / 2);
+  if (st) return st;
+  if (!aligned16(packed) || !aligned16(codes) || !aligned16(scales) || !aligned16(mean))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
+}
+
+int check_linear_bf16(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                      const uint16_t* A, const uint16_t* B, int r, float alpha) {
+  int st = check_linear_common(X, M, K, N, A, B, r, alpha, !W, W ? N * K * 2 : 0);
+  if (st) return st;
+  return aligned16(W) ? QLORA_OK : QLORA_ERR_ALIGN;
 }
 
 qlk::NF4Weight weight(const uint8_t* packed, const uint8_t* codes, const float* scales,
@@ -57,6 +74,44 @@ qlk::NF4Weight weight(const uint8_t* packed, const uint8_t* codes, const float* 
   qlk::NF4Weight w;
   w.packed = packed; w.codes = codes; w.scales = scales; w.mean = mean; w.N = N; w.K = K;
   return w;
+}
+
+qlk::NF4Weight weight_bf16(const uint16_t* W, int64_t N, int64_t K) {
+  qlk::NF4Weight w;
+  w.packed = nullptr; w.codes = nullptr; w.scales = nullptr; w.mean = nullptr;
+  w.N = N; w.K = K; w.bf16 = W;
+  return w;
+}
+
+int fwd_common(const uint16_t* X, int64_t M, int64_t K, int64_t N, const qlk::NF4Weight& w,
+               const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
+               uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Y) return QLORA_ERR_NULL;
+  if (!aligned16(Y) || (T_out && !aligned16(T_out))) return QLORA_ERR_ALIGN;
+  const qlk::FwdPlan plan = qlk::plan_fwd(M, K, N, r);
+  if (workspace_bytes < plan.bytes || (plan.bytes && !workspace)) return QLORA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+  const float s = alpha / (float)r;
+  return launch_status(qlk::launch_qlora_fwd(X, M, w, A, B, r, s, Y, T_out, workspace, plan,
+                                             as_stream(stream)));
+}
+
+int bwd_common(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
+               const qlk::NF4Weight& w, const uint16_t* A, const uint16_t* B, int r, float alpha,
+               const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!dY || !dA || !dB) return QLORA_ERR_NULL;
+  if (flags & ~QLORA_BWD_ACCUMULATE_DX) return QLORA_ERR_ARG;
+  if (!aligned16(dY) || !aligned16(dA) || !aligned16(dB) || (dX && !aligned16(dX)) ||
+      (T && !aligned16(T)))
+    return QLORA_ERR_ALIGN;
+  const qlk::BwdPlan plan = qlk::plan_bwd(M, K, N, r);
+  if (workspace_bytes < plan.bytes || !workspace) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
+  const float s = alpha / (float)r;
+  return launch_status(qlk::launch_qlora_bwd(dY, X, M, w, A, B, r, s, T, dX, dA, dB,
+                                             (flags & QLORA_BWD_ACCUMULATE_DX) != 0, workspace,
+                                             plan, as_stream(stream)));
 }
 
 }  // namespace
@@ -129,15 +184,17 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const u
                      uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
   if (st) return st;
-  if (!Y) return QLORA_ERR_NULL;
-  if (!aligned16(Y) || (T_out && !aligned16(T_out))) return QLORA_ERR_ALIGN;
-  const qlk::FwdPlan plan = qlk::plan_fwd(M, K, N, r);
-  if (workspace_bytes < plan.bytes || (plan.bytes && !workspace)) return QLORA_ERR_WORKSPACE;
-  if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
-  const float s = alpha / (float)r;
-  return launch_status(qlk::launch_qlora_fwd(X, M, weight(packed, codes, scales, mean, N, K), A,
-                                             B, r, s, Y, T_out, workspace, plan,
-                                             as_stream(stream)));
+  return fwd_common(X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, Y,
+                    T_out, workspace, workspace_bytes, stream);
+}
+
+int qlora_linear_fwd_bf16(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                          const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
+                          uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_linear_bf16(X, M, K, N, W, A, B, r, alpha);
+  if (st) return st;
+  return fwd_common(X, M, K, N, weight_bf16(W, N, K), A, B, r, alpha, Y, T_out, workspace,
+                    workspace_bytes, stream);
 }
 
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
@@ -147,18 +204,18 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K
                      void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
   if (st) return st;
-  if (!dY || !dA || !dB) return QLORA_ERR_NULL;
-  if (flags & ~QLORA_BWD_ACCUMULATE_DX) return QLORA_ERR_ARG;
-  if (!aligned16(dY) || !aligned16(dA) || !aligned16(dB) || (dX && !aligned16(dX)) ||
-      (T && !aligned16(T)))
-    return QLORA_ERR_ALIGN;
-  const qlk::BwdPlan plan = qlk::plan_bwd(M, K, N, r);
-  if (workspace_bytes < plan.bytes || !workspace) return QLORA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
-  const float s = alpha / (float)r;
-  return launch_status(qlk::launch_qlora_bwd(
-      dY, X, M, weight(packed, codes, scales, mean, N, K), A, B, r, s, T, dX, dA, dB,
-      (flags & QLORA_BWD_ACCUMULATE_DX) != 0, workspace, plan, as_stream(stream)));
+  return bwd_common(dY, X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, T,
+                    dX, dA, dB, flags, workspace, workspace_bytes, stream);
+}
+
+int qlora_linear_bwd_bf16(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                          const uint16_t* W, const uint16_t* A, const uint16_t* B, int r,
+                          float alpha, const uint16_t* T, uint16_t* dX, float* dA, float* dB,
+                          int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_linear_bf16(X, M, K, N, W, A, B, r, alpha);
+  if (st) return st;
+  return bwd_common(dY, X, M, K, N, weight_bf16(W, N, K), A, B, r, alpha, T, dX, dA, dB, flags,
+                    workspace, workspace_bytes, stream);
 }
 
 int silu_mul_fwd(const uint16_t* G, const uint16_t* Up, int64_t n, uint16_t* H, void* stream) {

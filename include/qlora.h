@@ -136,6 +136,23 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K
                      uint16_t* dX, float* dA, float* dB, int flags,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same layer with an unquantised bf16 base weight W [N, K] (bf16,
+ * row-major): the comparison the pages draw between LoRA on a bf16 base and
+ * QLoRA, where QLoRA trains 20-40 % slower per step because of the
+ * dequantisation in every forward pass (aigrafen.se "QLoRA", paragraph
+ * "Priset"; llm-compass "QLoRA", 与 baseline 对比 table, row 训练速度).  The
+ * same kernels run with the dequantisation switched off; everything else
+ * (adapter branch, reductions, tolerances, workspace size) is as in
+ * qlora_linear_fwd / qlora_linear_bwd, with W_hat = W.  Requires W under
+ * 2 GiB (2 N K bytes) in addition to their shape rules. */
+int qlora_linear_fwd_bf16(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W,
+                          const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
+                          uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream);
+int qlora_linear_bwd_bf16(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                          const uint16_t* W, const uint16_t* A, const uint16_t* B, int r,
+                          float alpha, const uint16_t* T, uint16_t* dX, float* dA, float* dB,
+                          int flags, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace the forward (is_bwd = 0) or backward (is_bwd = 1)
  * needs for these sizes; 0 means none.  Returns 0 for invalid sizes too. */
 size_t qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int r, int is_bwd);
