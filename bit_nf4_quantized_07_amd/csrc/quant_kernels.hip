@@ -83,6 +83,53 @@ k_dq_mean(const float* __restrict__ absmax, int64_t nb, float* __restrict__ mean
   if (threadIdx.x == 0) mean[0] = (float)(total / (double)nb);
 }
 
+// double_quant, step 1 for more than one group, in two launches with the same
+// summation order: (a) one thread per group of 256 constants forms the
+// group's sequential fp64 sum; (b) one workgroup stages the group sums in LDS
+// and one thread adds them in index order.  The group sums live in the codes
+// buffer until step 2 overwrites it (8 bytes per group, 256 code bytes).
+__global__ void __launch_bounds__(64)
+k_dq_group_sums(const float* __restrict__ absmax, int64_t nb, double* __restrict__ sums) {
+  const int64_t ngroups = (nb + kDQBlock - 1) / kDQBlock;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= ngroups) return;
+  const int64_t lo = g * kDQBlock;
+  const int64_t hi = (lo + kDQBlock < nb) ? lo + kDQBlock : nb;
+  double s = 0.0;
+  if (hi - lo == kDQBlock) {
+    // a whole group: all 64 loads in flight, then the ordered additions
+    const float4* p = reinterpret_cast<const float4*>(absmax + lo);
+#pragma unroll 16
+    for (int i = 0; i < kDQBlock / 4; ++i) {
+      const float4 v = p[i];
+      s += (double)v.x; s += (double)v.y; s += (double)v.z; s += (double)v.w;
+    }
+  } else {
+    for (int64_t i = lo; i < hi; ++i) s += (double)absmax[i];
+  }
+  sums[g] = s;
+}
+
+constexpr int kDqChunk = 4096;   // group sums staged in LDS per round (32 KB)
+
+__global__ void __launch_bounds__(256)
+k_dq_mean_ordered(const double* __restrict__ sums, int64_t ngroups, int64_t nb,
+                  float* __restrict__ mean) {
+  __shared__ double part[kDqChunk];
+  double total = 0.0;
+  for (int64_t base = 0; base < ngroups; base += kDqChunk) {
+    const int64_t n = (ngroups - base < kDqChunk) ? ngroups - base : kDqChunk;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) part[i] = sums[base + i];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll 16
+      for (int64_t j = 0; j < n; ++j) total += part[j];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mean[0] = (float)(total / (double)nb);
+}
+
 // ---------------------------------------------------------------------------
 // double_quant, step 2: one workgroup per group of 256 constants.
 // ---------------------------------------------------------------------------
@@ -158,10 +205,21 @@ hipError_t launch_nf4_quantize(const float* W, int64_t numel, uint8_t* packed, f
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, float* scales,
                                float* mean, hipStream_t st) {
-  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(1024), 0, st, absmax, nb, mean);
+  const int64_t ng = (nb + kDQBlock - 1) / kDQBlock;
+  if (ng == 1) {
+    hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(1024), 0, st, absmax, nb, mean);
+  } else {
+    // ng >= 2 groups: nb > 256 (ng - 1) >= 8 ng, so the codes buffer (nb
+    // bytes, 16-byte aligned) holds the ng fp64 group sums.
+    double* sums = reinterpret_cast<double*>(codes);
+    hipLaunchKernelGGL(k_dq_group_sums, dim3((unsigned)((ng + 63) / 64)), dim3(64), 0, st, absmax,
+                       nb, sums);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+    hipLaunchKernelGGL(k_dq_mean_ordered, dim3(1), dim3(256), 0, st, sums, ng, nb, mean);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ng = (nb + kDQBlock - 1) / kDQBlock;
   hipLaunchKernelGGL(k_dq_codes, dim3((unsigned)ng), dim3(256), 0, st, absmax, nb, mean, codes, scales);
   return hipGetLastError();
 }

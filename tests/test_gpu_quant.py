@@ -48,6 +48,14 @@ def test_storage_bit_exact_config1_and_2():
         check_full(wl.weight(0, w.cfg_id, 0, lin), cfg)
 
 
+@pytest.mark.parametrize("N,K", [(4100, 4096), (262244, 64)])
+def test_storage_bit_exact_many_groups(N, K):
+    """More than 1024 groups of 256 constants take the two-launch mean; the
+    second shape ends with a partial group of 100 constants."""
+    W = wl.weight(0, 100, N * 10000 + K, wl.Linear("w", N, K, 8, 16.0))
+    check_full(W, f"N={N} K={K}")
+
+
 def test_storage_special_blocks():
     """Zero blocks, exact ties at representable midpoints, +-absmax, -0.0,
     subnormal and tiny values."""
