@@ -15,9 +15,10 @@
 //     A [r, K] is staged in LDS and read back with transpose reads, eight
 //     consecutive r of one column per lane.  Wave w owns columns 32 w .. +31.
 //  2. The fp32 product goes through LDS so that
-//  3. each thread then handles 32 consecutive weights of one row: it decodes
+//  3. each thread then handles four runs of 8 consecutive weights (laid out
+//     so that a wave's stores cover whole 256-byte row segments): it decodes
 //     them exactly as nf4_dequant does (same bf16 values), adds s (B A) with
-//     one fused multiply-add in fp32, rounds to bf16 and stores 64 bytes.
+//     one fused multiply-add in fp32, rounds to bf16 and stores 16 bytes.
 // HBM-bound: 0.5 + 1/64 bytes in and 2 bytes out per weight, plus A and B
 // (read from L2 by every tile).
 #include "device_common.h"
@@ -93,32 +94,32 @@ k_merge(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
       prod[(32 * nb + 8 * (v >> 2) + 4 * h + (v & 3)) * kMgLdP + 32 * wave + c] = acc[nb][v];
   __syncthreads();
 
-  // 32 weights per thread: row tid / 4, columns 32 (tid % 4) .. +31 (one
-  // 64-block half, so one scale constant).
-  const int rn = tid >> 2, kc = (tid & 3) * 32;
-  const int64_t n = n0 + rn, k = k0 + kc;
-  if (n >= N || k >= K) return;
+  // Eight weights per thread and round: in round q thread t takes row
+  // 16 q + t / 16 and columns 8 (t % 16) .. +7 of the tile, so each store
+  // instruction of a wave writes four whole 256-byte row segments.
   const int64_t nkb = K / kBlock;
-  const int64_t blk = n * nkb + k / kBlock;
-  float ah;
-  {
-#pragma clang fp contract(off)
-    const float p = dq_level((int)codes[blk]) * scales[blk / kDQBlock];
-    ah = p + mean_p[0];
-  }
-  const uint4 pw = *reinterpret_cast<const uint4*>(packed + (n * K + k) / 2);
-  const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
-  const float* prow = prod + rn * kMgLdP + kc;
-  uint4* dst = reinterpret_cast<uint4*>(out + n * K + k);
+  const float mu = mean_p[0];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float4 p0 = *reinterpret_cast<const float4*>(prow + 8 * q);
-    const float4 p1 = *reinterpret_cast<const float4*>(prow + 8 * q + 4);
+    const int rn = 16 * q + (tid >> 4), kc = 8 * (tid & 15);
+    const int64_t n = n0 + rn, k = k0 + kc;
+    if (n >= N || k >= K) continue;
+    const int64_t blk = n * nkb + k / kBlock;
+    float ah;
+    {
+#pragma clang fp contract(off)
+      const float p = dq_level((int)codes[blk]) * scales[blk / kDQBlock];
+      ah = p + mu;
+    }
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + (n * K + k) / 2);
+    const float* prow = prod + rn * kMgLdP + kc;
+    const float4 p0 = *reinterpret_cast<const float4*>(prow);
+    const float4 p1 = *reinterpret_cast<const float4*>(prow + 4);
     const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     uint32_t o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t byte = (words[q] >> (8 * e)) & 0xffu;   // element 2e high, 2e+1 low nibble
+      const uint32_t byte = (word >> (8 * e)) & 0xffu;   // element 2e high, 2e+1 low nibble
       float wv[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -133,7 +134,7 @@ k_merge(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
       }
       o[e] = pack_bf16x2(wv[0], wv[1]);
     }
-    dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(out + n * K + k) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 

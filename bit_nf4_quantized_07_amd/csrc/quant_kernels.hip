@@ -163,32 +163,39 @@ k_dq_codes(const float* __restrict__ absmax, int64_t nb, const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// nf4_dequant: each lane expands 16 packed bytes (32 weights, half a block).
+// nf4_dequant: a wave expands 2048 consecutive weights (1 KB packed, 4 KB
+// out) in four rounds; in round q lane L turns packed word 64 q + L (8
+// weights) into 16 bytes at output offset 1 KB q + 16 L, so every load and
+// every store instruction of the wave covers one contiguous range.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 k_nf4_dequant(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
               const float* __restrict__ scales, const float* __restrict__ mean,
-              int64_t nchunks, uint16_t* __restrict__ out) {
+              int64_t nwords, uint16_t* __restrict__ out) {
   __shared__ float q4[16];
   if (threadIdx.x < 16) q4[threadIdx.x] = nf4_level(threadIdx.x);
   __syncthreads();
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= nchunks) return;
-  const int64_t blk = c >> 1;
-  const uint4 p = reinterpret_cast<const uint4*>(packed)[c];
-  const float ah = absmax_decode(codes[blk], scales[blk / kDQBlock], mean[0]);
-  const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-  uint32_t o[16];
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 256;  // first word of the wave
+  const float mu = mean[0];
+  const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t byte = (pw[j >> 2] >> ((j & 3) * 8)) & 0xffu;
-    const float w0 = q4[byte >> 4] * ah;     // element 2j: high nibble
-    const float w1 = q4[byte & 15u] * ah;
-    o[j] = pack_bf16x2(w0, w1);
+  for (int q = 0; q < 4; ++q) {
+    const int64_t wd = w0 + 64 * q + lane;   // packed word: weights 8 wd .. 8 wd + 7
+    if (wd >= nwords) break;
+    const uint32_t p = pw[wd];
+    const int64_t blk = wd >> 3;             // 8 words per block of 64
+    const float ah = absmax_decode(codes[blk], scales[blk / kDQBlock], mu);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t byte = (p >> (j * 8)) & 0xffu;
+      const float a = q4[byte >> 4] * ah;    // element 2j: high nibble
+      const float b = q4[byte & 15u] * ah;
+      o[j] = pack_bf16x2(a, b);
+    }
+    reinterpret_cast<uint4*>(out)[wd] = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  uint4* dst = reinterpret_cast<uint4*>(out + c * 32);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -226,10 +233,10 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, 
 
 hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
                               const float* mean, int64_t numel, uint16_t* out, hipStream_t st) {
-  const int64_t nchunks = numel / 32;
-  const int64_t grid = (nchunks + 255) / 256;
+  const int64_t nwords = numel / 8;                  // numel % 64 == 0
+  const int64_t grid = (nwords + 1023) / 1024;        // 4 waves x 256 words
   hipLaunchKernelGGL(k_nf4_dequant, dim3((unsigned)grid), dim3(256), 0, st, packed, codes, scales,
-                     mean, nchunks, out);
+                     mean, nwords, out);
   return hipGetLastError();
 }
 
