@@ -1,0 +1,152 @@
+"""GPU parity of the SiLU-gated MLP glue (silu_mul_fwd / silu_mul_bwd) and of
+the gated MLP block built from three QLoRA linears (the configuration-3 and
+configuration-5 workloads) against the fp64 oracle.
+
+The glue is not a QLoRA step; the pages only name gate/up/down projections as
+LoRA targets.  silu(g) = g sigmoid(g) is the textbook definition.  Elementwise
+outputs are bf16 (one rounding of an fp32 evaluation), so each must lie within
+two bf16 rounding steps of the exact value; the composed block meets the
+linear layer's tolerances (||err||_F / ||ref||_F <= 1e-2, max|err| <= 3e-2
+max|ref|)."""
+import numpy as np
+import pytest
+
+import bit_nf4_quantized_07_amd as q
+import oracle
+import qlora_workloads as wl
+from gpu_helpers import (OracleWeight, assert_close, dev_bf16, dev_f32, f64, host,
+                         host_bf16_bits, host_bf16_f64, log, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_step(x: np.ndarray) -> np.ndarray:
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, e - 8)
+
+
+def check_elementwise(got_bits, exact, name):
+    got = oracle.bf16_bits_to_f64(got_bits)
+    tol = 2.0 * bf16_step(exact) + 1e-30
+    bad = np.abs(got - exact) > tol
+    assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} outside two bf16 steps"
+
+
+def rand_bf16(seed, n, scale=1.0):
+    x = np.random.default_rng(seed).normal(0, scale, n).astype(np.float32)
+    return wl.round_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("n", [8, 8 * 37, 4096 * 3 + 8])
+def test_silu_mul_parity(n):
+    t = pytest.importorskip("torch")
+    G, Up, dH = rand_bf16(1, n, 3.0), rand_bf16(2, n), rand_bf16(3, n)
+    Hd = q.silu_mul_fwd(dev_bf16(G), dev_bf16(Up))
+    dGd, dUd = q.silu_mul_bwd(dev_bf16(dH), dev_bf16(G), dev_bf16(Up))
+    t.cuda.synchronize()
+    Gf, Uf, dHf = f64(G), f64(Up), f64(dH)
+    check_elementwise(host_bf16_bits(Hd), oracle.silu_mul_forward(Gf, Uf), "H")
+    dGr, dUr = oracle.silu_mul_backward(dHf, Gf, Uf)
+    check_elementwise(host_bf16_bits(dGd), dGr, "dG")
+    check_elementwise(host_bf16_bits(dUd), dUr, "dUp")
+
+
+def test_silu_mul_special_values():
+    """g = 0: h = 0, dUp = 0, dG = dh up / 2.  Large |g|: sigmoid saturates,
+    h = g up for g >> 0 and h -> 0 for g << 0."""
+    t = pytest.importorskip("torch")
+    G = wl.round_to_bf16_bits(np.array([0, 0, 30, -30, 88, -88, 1, -1], np.float32))
+    Up = wl.round_to_bf16_bits(np.array([2, -3, 1.5, 1.5, 0.25, 0.25, 4, 4], np.float32))
+    dH = wl.round_to_bf16_bits(np.array([1, 0.5, 1, 1, 2, 2, 1, 1], np.float32))
+    Hd = q.silu_mul_fwd(dev_bf16(G), dev_bf16(Up))
+    dGd, dUd = q.silu_mul_bwd(dev_bf16(dH), dev_bf16(G), dev_bf16(Up))
+    t.cuda.synchronize()
+    H, dG, dU = (host_bf16_f64(x) for x in (Hd, dGd, dUd))
+    assert H[0] == 0 and H[1] == 0 and dU[0] == 0 and dU[1] == 0
+    assert dG[0] == 1.0 and dG[1] == -0.75
+    assert H[2] == 45.0 and H[4] == 22.0
+    assert abs(H[3]) < 1e-10 and abs(H[5]) < 1e-30
+    Gf, Uf, dHf = f64(G), f64(Up), f64(dH)
+    check_elementwise(host_bf16_bits(Hd), oracle.silu_mul_forward(Gf, Uf), "H special")
+    dGr, dUr = oracle.silu_mul_backward(dHf, Gf, Uf)
+    check_elementwise(host_bf16_bits(dGd), dGr, "dG special")
+    check_elementwise(host_bf16_bits(dUd), dUr, "dUp special")
+
+
+def run_block(X, dY, lins):
+    """Forward and backward of the gated MLP on the GPU through the public
+    entry points.  lins: dict name -> (QuantizedWeight, A, B, alpha)."""
+    t = pytest.importorskip("torch")
+    (qg, Ag, Bg, ag), (qu, Au, Bu, au), (qd, Ad, Bd, ad) = lins["gate"], lins["up"], lins["down"]
+    G, Tg = q.linear_fwd(X, qg, Ag, Bg, ag)
+    U, Tu = q.linear_fwd(X, qu, Au, Bu, au)
+    H = q.silu_mul_fwd(G, U)
+    Y, Td = q.linear_fwd(H, qd, Ad, Bd, ad)
+    dH, dAd, dBd = q.linear_bwd(dY, H, qd, Ad, Bd, ad, T=Td)
+    dG, dU = q.silu_mul_bwd(dH, G, U)
+    dX, dAg, dBg = q.linear_bwd(dG, X, qg, Ag, Bg, ag, T=Tg)
+    _, dAu, dBu = q.linear_bwd(dU, X, qu, Au, Bu, au, T=Tu, accumulate_into=dX)
+    t.cuda.synchronize()
+    return dict(Y=Y, dX=dX, dA=dict(gate=dAg, up=dAu, down=dAd), dB=dict(gate=dBg, up=dBu, down=dBd))
+
+
+def make_block(seed, M, D, I, r, alpha):
+    shapes = dict(gate=(I, D), up=(I, D), down=(D, I))
+    host_w, dev_w = {}, {}
+    for j, (name, (N, K)) in enumerate(shapes.items()):
+        lin = wl.Linear(name, N, K, r, alpha)
+        W = wl.weight(seed, 100, j, lin)
+        A, B = wl.adapters(seed, 100, j, lin)
+        host_w[name] = (W, A, B)
+        dev_w[name] = (q.quantize(dev_f32(W)), dev_bf16(A), dev_bf16(B), alpha)
+    X = wl.activations(seed, 100, M, D)
+    dY = wl.grad_output(seed, 100, M, D)
+    return X, dY, host_w, dev_w
+
+
+@pytest.mark.parametrize("M,D,I,r,alpha", [(130, 256, 384, 16, 32.0), (300, 512, 1408, 64, 128.0)])
+def test_mlp_block_parity(M, D, I, r, alpha):
+    log(f"[mlp] M={M} D={D} I={I} r={r}")
+    X, dY, host_w, dev_w = make_block(41, M, D, I, r, alpha)
+    got = run_block(dev_bf16(X), dev_bf16(dY), dev_w)
+    ref_lin = {n: dict(W_hat=f64(OracleWeight(W).w_bf16()), A=f64(A), B=f64(B), alpha=alpha, r=r)
+               for n, (W, A, B) in host_w.items()}
+    Yr, saved = oracle.mlp_forward(f64(X), ref_lin["gate"], ref_lin["up"], ref_lin["down"])
+    dXr, grads = oracle.mlp_backward(f64(dY), f64(X), saved, ref_lin["gate"], ref_lin["up"],
+                                     ref_lin["down"])
+    assert_close(host_bf16_f64(got["Y"]), Yr, "Y")
+    assert_close(host_bf16_f64(got["dX"]), dXr, "dX")
+    for n in ("gate", "up", "down"):
+        assert_close(host(got["dA"][n]).astype(np.float64), grads[n][0], f"dA {n}")
+        assert_close(host(got["dB"][n]).astype(np.float64), grads[n][1], f"dB {n}")
+
+
+@pytest.mark.timeout(400)
+def test_mlp_block_config3_sampled_tokens():
+    """Full configuration-3 shapes (gate/up 11008 x 4096, down 4096 x 11008,
+    4096 tokens, r = 64): Y and dX depend on their own token only, so they
+    are checked on sampled tokens against the oracle run on those tokens."""
+    w = wl.workloads()["c3_mlp_11008"]
+    lins = {l.name: l for l in w.linears}
+    log(f"[mlp full] {w.name}")
+    host_w, dev_w = {}, {}
+    for j, name in enumerate(("gate", "up", "down")):
+        lin = lins[name]
+        W = wl.weight(0, w.cfg_id, j, lin)
+        A, B = wl.adapters(0, w.cfg_id, j, lin)
+        host_w[name] = (W, A, B, lin)
+        dev_w[name] = (q.quantize(dev_f32(W)), dev_bf16(A), dev_bf16(B), lin.alpha)
+    D = lins["gate"].K
+    X = wl.activations(0, w.cfg_id, w.M, D)
+    dY = wl.grad_output(0, w.cfg_id, w.M, D)
+    got = run_block(dev_bf16(X), dev_bf16(dY), dev_w)
+    rows = sample_rows(w.M, 24, seed=7, tile=256)
+    ref_lin = {}
+    for n, (W, A, B, lin) in host_w.items():
+        ref_lin[n] = dict(W_hat=f64(OracleWeight(W).w_bf16()), A=f64(A), B=f64(B),
+                          alpha=lin.alpha, r=lin.r)
+    Yr, saved = oracle.mlp_forward(f64(X[rows]), ref_lin["gate"], ref_lin["up"], ref_lin["down"])
+    dXr, _ = oracle.mlp_backward(f64(dY[rows]), f64(X[rows]), saved, ref_lin["gate"],
+                                 ref_lin["up"], ref_lin["down"])
+    assert_close(host_bf16_f64(got["Y"])[rows], Yr, "Y[sampled tokens]")
+    assert_close(host_bf16_f64(got["dX"])[rows], dXr, "dX[sampled tokens]")
