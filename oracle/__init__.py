@@ -13,6 +13,8 @@ Pages cited (titles as printed on each page):
   [SB] skillbyai "QLoRA: Fine-Tuning on One Consumer GPU"
   [LI] learn-interview-questions "QLoRA (Quantized Low-Rank Adaptation):
        4-bit NormalFloat (NF4) & Paged Optimizers"
+Outside the pages: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+random numbers: as easy as 1, 2, 3", SC 2011) for the dropout mask.
 
 Functions and what pins them (tests/test_oracle_*.py):
   nf4_codebook      three independent inverse-normal routes, equal-probability
@@ -29,14 +31,28 @@ Functions and what pins them (tests/test_oracle_*.py):
   merge             B = 0 reduces to the dequantised base; constant
                     adapters give the closed form W + alpha a b; hand-worked
                     bf16 rounding ties; bf16 rounding against torch
+  philox            the published Philox4x32-10 known-answer vectors; the
+                    same round function at 64-bit width against numpy's
+                    Philox bit generator
+  dropout           keep rate within binomial bounds, p = 0 is the identity,
+                    counter-based (row subsets equal slices), scale exact;
+                    forward/backward with the mask fixed: all-kept reduces to
+                    the plain layer, exact directional derivatives
+  int4 codebook     even spacing, round trip, error bound; NF4 beats it on
+                    Gaussian blocks in error and in code entropy, as the
+                    pages argue
 No function is "parity unpinned".
 """
 from .nf4 import (  # noqa: F401
-    NF4_DELTA, nf4_codebook, dq_codebook, nearest_index, absmax_blocks,
-    quantize_nf4, pack_nibbles, unpack_nibbles, double_quant, dequant_absmax,
+    NF4_DELTA, nf4_codebook, dq_codebook, int4_codebook, nearest_index, absmax_blocks,
+    quantize_nf4, quantize_blocks, pack_nibbles, unpack_nibbles, double_quant, dequant_absmax,
     dequant_nf4, dequant_codes, f32_to_bf16_bits, bf16_bits_to_f64, bits_per_param,
 )
 from .qlora import (  # noqa: F401
     lora_scale, forward, backward, silu_mul_forward, silu_mul_backward,
     mlp_forward, mlp_backward, merge, f64_to_bf16_bits,
+)
+from .dropout import (  # noqa: F401
+    philox, philox4x32_words, dropout_threshold, dropout_scale, dropout_mask, dropout_apply,
+    pack_mask, forward_dropout, backward_dropout,
 )

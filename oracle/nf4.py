@@ -74,6 +74,16 @@ def dq_codebook() -> np.ndarray:
     return (i - np.float32(127.0)) / np.float32(127.0)
 
 
+def int4_codebook() -> np.ndarray:
+    """Uniform 4-bit codebook for the comparison the pages draw with NF4:
+    16 levels spaced evenly over the absmax-normalised range [-1, 1] ([LI] §2,
+    standard uniform INT4 puts its bins at equal linear intervals; [LC] 方法与
+    公式 item 1, uniform INT4 wastes levels in the tails).  Reading: levels
+    -1 + 2 i / 15, i = 0..15, each evaluated in fp64 and rounded once to
+    fp32.  Same packing, blocks and absmax constants as NF4."""
+    return (-1.0 + 2.0 * np.arange(16, dtype=np.float64) / 15.0).astype(np.float32)
+
+
 def nearest_index(values: np.ndarray, levels: np.ndarray) -> np.ndarray:
     """Index of the nearest level, ties to the LOWER index (deterministic).
 
@@ -122,6 +132,13 @@ def quantize_nf4(w: np.ndarray, blocksize: int = 64):
     level.  A block whose absmax is 0 holds only zeros; its codes are the zero
     level (index 7).  Non-finite weights are rejected.
     """
+    return quantize_blocks(w, nf4_codebook(), blocksize)
+
+
+def quantize_blocks(w: np.ndarray, levels: np.ndarray, blocksize: int = 64):
+    """Blockwise absmax quantisation onto any ascending 16-level codebook:
+    n = w / absmax as above (n = 0 in an all-zero block), code = nearest level
+    with ties to the lower index.  quantize_nf4 is this with the NF4 levels."""
     flat = np.asarray(w, dtype=np.float32).reshape(-1)
     if not np.all(np.isfinite(flat)):
         raise ValueError("non-finite weights")
@@ -130,7 +147,7 @@ def quantize_nf4(w: np.ndarray, blocksize: int = 64):
     with np.errstate(divide="ignore", invalid="ignore"):
         n = np.where(per_elem > 0, flat / np.where(per_elem > 0, per_elem, np.float32(1)),
                      np.float32(0)).astype(np.float32)
-    codes = nearest_index(n, nf4_codebook())
+    codes = nearest_index(n, levels)
     return codes, a
 
 
@@ -246,14 +263,16 @@ def dequant_nf4(packed: np.ndarray, codes: np.ndarray, scales: np.ndarray, mean,
     return w_hat.reshape(N, K), wb.reshape(N, K)
 
 
-def dequant_codes(codes4: np.ndarray, a_hat: np.ndarray, blocksize: int = 64):
+def dequant_codes(codes4: np.ndarray, a_hat: np.ndarray, blocksize: int = 64, levels=None):
     """4-bit codes [nblk*blocksize] and the decoded constant of each of their
     blocks [nblk] -> (w_hat fp32, bf16 bits), w_hat = fp32(Q4[code] * a_hat).
+    ``levels`` is the 16-level codebook (default NF4).
 
     Works on any whole-block subset of a weight (blocks are independent)."""
+    lv = nf4_codebook() if levels is None else np.asarray(levels, dtype=np.float32)
     c = np.asarray(codes4, dtype=np.uint8).reshape(-1)
     per_elem = np.repeat(np.asarray(a_hat, dtype=np.float32), blocksize)[:c.size]
-    w_hat = (nf4_codebook()[c] * per_elem).astype(np.float32)
+    w_hat = (lv[c] * per_elem).astype(np.float32)
     return w_hat, f32_to_bf16_bits(w_hat)
 
 
