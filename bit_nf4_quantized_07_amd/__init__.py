@@ -44,6 +44,14 @@ SIGNATURES = {
                                    ctypes.c_size_t, _P]),
     "qlora_linear_bwd_bf16": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _I, _F, _P, _P, _P,
                                    _P, _I, _P, ctypes.c_size_t, _P]),
+    "codebook_quantize": (_I, [_P, _I64, _I64, _I, _P, _P, _P, _P]),
+    "codebook_dequant": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P, _P]),
+    "lora_dropout": (_I, [_P, _I64, _I64, ctypes.c_double, ctypes.c_uint64, _P, _P, _P]),
+    "qlora_linear_fwd_dropout": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F,
+                                      _P, _P, _P, ctypes.c_size_t, _P]),
+    "qlora_linear_bwd_dropout": (_I, [_P, _P, _P, ctypes.c_double, _I64, _I64, _I64, _P, _P, _P,
+                                      _P, _P, _P, _I, _F, _P, _P, _P, _P, _I, _P,
+                                      ctypes.c_size_t, _P]),
     "silu_mul_fwd": (_I, [_P, _P, _I64, _P, _P]),
     "silu_mul_bwd": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "nf4_codebook": (_I, [_P]),
@@ -284,6 +292,104 @@ def linear_bwd(dY, X, qw, A, B, alpha: float, T=None, need_dX: bool = True,
         _check("qlora_linear_bwd_bf16", lib.qlora_linear_bwd_bf16(
             _ptr(dY), _ptr(X), M, K, N, _ptr(qw), _ptr(A), _ptr(B), r, float(alpha), _ptr(T),
             _ptr(dX), _ptr(dA), _ptr(dB), flags, _ptr(ws), wsb, _stream(X.device)))
+    return dX, dA, dB
+
+
+def _levels(levels):
+    vals = [float(v) for v in levels]
+    if len(vals) != 16:
+        raise ValueError("a 4-bit codebook has 16 levels")
+    return (ctypes.c_float * 16)(*vals)
+
+
+def codebook_quantize(W, levels):
+    """Blockwise quantisation of W fp32 [N, K] onto a 16-level codebook (host
+    sequence, ascending) -> (packed uint8 [N*K/2], absmax fp32 [N*K/64])."""
+    torch = _torch()
+    _need_cuda(W)
+    N, K = W.shape
+    packed = torch.empty(N * K // 2, dtype=torch.uint8, device=W.device)
+    absmax = torch.empty(max(N * K // BLOCKSIZE, 1), dtype=torch.float32, device=W.device)
+    lv = _levels(levels)
+    _check("codebook_quantize", load_library().codebook_quantize(
+        _ptr(W), N, K, BLOCKSIZE, ctypes.cast(lv, _P), _ptr(packed), _ptr(absmax),
+        _stream(W.device)))
+    return packed, absmax
+
+
+def quantize_with_codebook(W, levels) -> QuantizedWeight:
+    """codebook_quantize followed by double quantisation of the constants."""
+    packed, absmax = codebook_quantize(W, levels)
+    codes, scales, mean = double_quant(absmax)
+    return QuantizedWeight(packed, codes, scales, mean, W.shape[0], W.shape[1])
+
+
+def codebook_dequant(qw: QuantizedWeight, levels):
+    """-> bf16 [N, K] dequantised with the given 16-level codebook."""
+    torch = _torch()
+    out = torch.empty(qw.N, qw.K, dtype=torch.bfloat16, device=qw.packed.device)
+    lv = _levels(levels)
+    _check("codebook_dequant", load_library().codebook_dequant(
+        _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean), qw.N, qw.K,
+        BLOCKSIZE, DQ_BLOCKSIZE, ctypes.cast(lv, _P), _ptr(out), _stream(out.device)))
+    return out
+
+
+def dropout(X, p: float, seed: int):
+    """LoRA dropout of the adapter input: -> (Xd bf16 [M, K], mask int32
+    [M*K/32], bit i % 32 of word i // 32 = element i kept)."""
+    torch = _torch()
+    _need_cuda(X)
+    M, K = X.shape
+    Xd = torch.empty_like(X)
+    mask = torch.empty(max((M * K + 31) // 32, 4), dtype=torch.int32, device=X.device)
+    _check("lora_dropout", load_library().lora_dropout(
+        _ptr(X), M, K, float(p), int(seed) & (2**64 - 1), _ptr(Xd), _ptr(mask), _stream(X.device)))
+    return Xd, mask[:(M * K + 31) // 32]
+
+
+def linear_fwd_dropout(X, Xd, qw: QuantizedWeight, A, B, alpha: float, save_T: bool = True,
+                       out=None, T_out=None, workspace=None):
+    """Y = X W_hat^T + (alpha/r) (Xd A^T) B^T with Xd the dropped adapter
+    input.  Returns (Y, T = Xd A^T or None)."""
+    torch = _torch()
+    M, K = X.shape
+    r = A.shape[0]
+    _need_cuda(X, Xd, A, B)
+    Y = out if out is not None else torch.empty(M, qw.N, dtype=torch.bfloat16, device=X.device)
+    T = T_out if T_out is not None else (
+        torch.empty(M, r, dtype=torch.bfloat16, device=X.device) if save_T else None)
+    nb = workspace_bytes(M, K, qw.N, r, False)
+    ws, wsb = (workspace.get(nb) if workspace is not None else _ws(X.device, nb))
+    _check("qlora_linear_fwd_dropout", load_library().qlora_linear_fwd_dropout(
+        _ptr(X), _ptr(Xd), M, K, qw.N, _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales),
+        _ptr(qw.mean), _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(T), _ptr(ws), wsb,
+        _stream(X.device)))
+    return Y, T
+
+
+def linear_bwd_dropout(dY, Xd, mask, p: float, qw: QuantizedWeight, A, B, alpha: float, T=None,
+                       need_dX: bool = True, accumulate_into=None, workspace=None):
+    """Backward of linear_fwd_dropout (mask and p from `dropout`).  Returns
+    (dX bf16 or None, dA fp32 [r, K], dB fp32 [N, r])."""
+    torch = _torch()
+    M, K = Xd.shape
+    r = A.shape[0]
+    _need_cuda(dY, Xd, mask, A, B, T)
+    flags = 0
+    if accumulate_into is not None:
+        dX = accumulate_into
+        flags |= BWD_ACCUMULATE_DX
+    else:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=Xd.device) if need_dX else None
+    dA = torch.empty(r, K, dtype=torch.float32, device=Xd.device)
+    dB = torch.empty(qw.N, r, dtype=torch.float32, device=Xd.device)
+    nb = workspace_bytes(M, K, qw.N, r, True)
+    ws, wsb = (workspace.get(nb) if workspace is not None else _ws(Xd.device, nb))
+    _check("qlora_linear_bwd_dropout", load_library().qlora_linear_bwd_dropout(
+        _ptr(dY), _ptr(Xd), _ptr(mask), float(p), M, K, qw.N, _ptr(qw.packed), _ptr(qw.codes),
+        _ptr(qw.scales), _ptr(qw.mean), _ptr(A), _ptr(B), r, float(alpha), _ptr(T), _ptr(dX),
+        _ptr(dA), _ptr(dB), flags, _ptr(ws), wsb, _stream(Xd.device)))
     return dX, dA, dB
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora.so")
 SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "fwd_kernels.hip", "dx_kernels.hip", "adapter_kernels.hip", "gemv_kernels.hip", "elementwise.hip",
-           "merge_kernels.hip", "qlora_api.hip"]
+           "merge_kernels.hip", "dropout_kernels.hip", "qlora_api.hip"]
 ARCH = "gfx950"
 
 COMMON = [

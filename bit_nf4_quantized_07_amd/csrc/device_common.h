@@ -45,14 +45,11 @@ __device__ __forceinline__ float dq_level(int i) {
   return __builtin_fmaf(r, inv, q0);
 }
 
-// Decision threshold between NF4 levels i and i+1: their exact midpoint
+// Decision threshold between 8-bit levels i and i+1: their exact midpoint
 // (exact in fp64) rounded toward -inf, so that for any fp32 n
 // "n > threshold" <=> "n is strictly above the midpoint".  Ties (n equal to
-// a representable midpoint) therefore go to the lower index.
-__device__ __forceinline__ float nf4_threshold(int i) {
-  double m = ((double)nf4_level(i) + (double)nf4_level(i + 1)) * 0.5;
-  return __double2float_rd(m);
-}
+// a representable midpoint) therefore go to the lower index.  The 4-bit
+// codebooks carry thresholds built the same way (Codebook4).
 __device__ __forceinline__ float dq_threshold(int i) {
   double m = ((double)dq_level(i) + (double)dq_level(i + 1)) * 0.5;
   return __double2float_rd(m);

@@ -34,6 +34,8 @@
 //    buffer; raw weight loads run three steps ahead.
 //  * The adapter term s U A is a last contraction over r into the same
 //    accumulators; each lane stores four consecutive features (8 bytes).
+//    With LoRA dropout on the adapter input the term is accumulated apart,
+//    multiplied by mask * 1/(1-p) per element, then added.
 #include <type_traits>
 
 #include "device_common.h"
@@ -65,6 +67,8 @@ struct DxArgs {
   uint16_t* dX;         // [M, K] bf16
   int accumulate;
   int tiles_m, tiles_k, group_m;
+  const uint32_t* mask; // dropout of the adapter input: bit per element of dX, or null
+  float keep_scale;     // 1 / (1 - p) for the kept elements
 };
 
 struct DxWRegs { uint2 p; uint32_t code; float sc; };
@@ -343,33 +347,59 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
 
-  // Adapter term: acc += (s A)^T U^T over r in steps of 16.
+  // Adapter term: (s A)^T U^T over r in steps of 16, into the main
+  // accumulators, or -- with a dropout mask -- into separate ones that are
+  // masked and scaled before they are added.
   const int64_t kf = k0 + 32 * fg + c;   // this lane's feature (operand row)
   const int mw = m0 + kDxWaveM * th;     // first token of this wave
-  for (int r0 = 0; r0 < g.r; r0 += 16) {
-    const int rr = r0 + 8 * h;
-    uint32_t av[4] = {0u, 0u, 0u, 0u};
-    if (kf < K && rr < g.r) {
+  auto adapter_into = [&](f32x16_t (&dst)[4]) {
+    for (int r0 = 0; r0 < g.r; r0 += 16) {
+      const int rr = r0 + 8 * h;
+      uint32_t av[4] = {0u, 0u, 0u, 0u};
+      if (kf < K && rr < g.r) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
-        const float hi = bf16_to_f32(g.A[(int64_t)(rr + 2 * q + 1) * K + kf]) * g.s;
-        av[q] = pack_bf16x2(lo, hi);
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
+          const float hi = bf16_to_f32(g.A[(int64_t)(rr + 2 * q + 1) * K + kf]) * g.s;
+          av[q] = pack_bf16x2(lo, hi);
+        }
+      }
+      const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mw + 32 * i + c;
+        uint4 uv = make_uint4(0, 0, 0, 0);
+        if (m < g.M && rr < g.r) uv = *reinterpret_cast<const uint4*>(g.U + (int64_t)m * g.r + rr);
+        dst[i] = mfma_32x32x16(afr, __builtin_bit_cast(bf16x8_t, uv), dst[i]);
       }
     }
-    const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mw + 32 * i + c;
-      uint4 uv = make_uint4(0, 0, 0, 0);
-      if (m < g.M && rr < g.r) uv = *reinterpret_cast<const uint4*>(g.U + (int64_t)m * g.r + rr);
-      acc[i] = mfma_32x32x16(afr, __builtin_bit_cast(bf16x8_t, uv), acc[i]);
-    }
-  }
+  };
 
   // Accumulator i: lane holds token m = mw + 32 i + c and features
   // 8 (v / 4) + 4 h + (v % 4) of the wave's 32.
   const int64_t kw0 = k0 + 32 * fg;
+  if (g.mask == nullptr) {
+    adapter_into(acc);
+  } else {
+    f32x16_t ad[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ad[i][v] = 0.0f;
+    adapter_into(ad);
+    // The wave's 32 features start at a multiple of 32 and K % 64 == 0, so a
+    // token's 32 mask bits are one word; feature offset 8 (v / 4) + 4 h + v % 4.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mw + 32 * i + c;
+      const uint32_t bits = (m < g.M && kw0 < K) ? g.mask[((int64_t)m * K + kw0) >> 5] : 0u;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int bit = 8 * (v >> 2) + 4 * h + (v & 3);
+        acc[i][v] += ((bits >> bit) & 1u) ? ad[i][v] * g.keep_scale : 0.0f;
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = mw + 32 * i + c;
@@ -394,11 +424,12 @@ bool dx_nf4_supported(int64_t N) { return N % (kDxStepN * kDxUnroll) == 0; }
 
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
                          const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
-                         hipStream_t st) {
+                         hipStream_t st, const uint32_t* mask, float keep_scale) {
   if (!dx_nf4_supported(w.N)) return hipErrorInvalidValue;
   DxArgs g;
   g.dY = dY; g.M = (int)M; g.w = w; g.U = U; g.A = A; g.r = r; g.s = s; g.dX = dX;
   g.accumulate = accumulate ? 1 : 0;
+  g.mask = mask; g.keep_scale = keep_scale;
   g.tiles_m = (int)((M + kDxBM - 1) / kDxBM);
   g.tiles_k = (int)((w.K + kDxBK - 1) / kDxBK);
   g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2,

@@ -781,13 +781,14 @@ static hipError_t compute_T(const uint16_t* X, int64_t M, int64_t K, const uint1
 
 hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                             const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
-                            void* ws, const FwdPlan& plan, hipStream_t st) {
+                            void* ws, const FwdPlan& plan, hipStream_t st, const uint16_t* Xa) {
   const int64_t K = w.K, N = w.N;
   char* base = reinterpret_cast<char*>(ws);
   uint16_t* T = T_out ? T_out : reinterpret_cast<uint16_t*>(base + plan.off_T);
   float* part = reinterpret_cast<float*>(base + plan.off_part);
-  if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st);
-  QLK_TRY(compute_T(X, M, K, A, r, T, st));
+  if (!Xa) Xa = X;
+  if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st, Xa);
+  QLK_TRY(compute_T(Xa, M, K, A, r, T, st));
   GemmArgs g{};
   g.a1 = opnd(X, K, (int)M, M);
   g.b1 = opnd(nullptr, 0, (int)N, 0);
@@ -820,7 +821,8 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
 hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
                             const uint16_t* A, const uint16_t* B, int r, float s,
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,
-                            bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st) {
+                            bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st,
+                            const uint32_t* mask, float keep_scale) {
   const int64_t K = w.K, N = w.N;
   char* base = reinterpret_cast<char*>(ws);
   uint16_t* U = reinterpret_cast<uint16_t*>(base + plan.off_U);
@@ -848,7 +850,27 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     timer_begin(TK_DX_GEMM, st);
     hipError_t e;
     if (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N)) {
-      e = launch_dx_nf4(dY, M, w, U, A, r, s, dX, accumulate_dx, st);
+      e = launch_dx_nf4(dY, M, w, U, A, r, s, dX, accumulate_dx, st, mask, keep_scale);
+    } else if (mask) {
+      // Tile engine with a dropout mask: the masked adapter term is written
+      // (or added) first, then dY W_hat is accumulated on top of it.
+      e = launch_dx_adapter_masked(U, A, M, K, r, s, mask, keep_scale, dX, accumulate_dx, st);
+      if (e == hipSuccess) {
+        g.c2_len = 0;
+        g.accumulate = 1;
+        if (w.bf16) {
+          g.b1 = opnd(w.bf16, K, (int)K, N);
+          e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
+                          LdBF16T<QLK_DX_BN, kBK, false>, LdBF16K<QLK_DX_BM, kBK, false>,
+                          LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
+              g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 2, st);
+        } else {
+          e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
+                          LdNF4T<QLK_DX_BN>, LdBF16K<QLK_DX_BM, kBK, false>,
+                          LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
+              g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 0.52, st);
+        }
+      }
     } else if (w.bf16) {
       g.b1 = opnd(w.bf16, K, (int)K, N);   // transposed load of W [N, K]: rows k, contraction n
       e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,

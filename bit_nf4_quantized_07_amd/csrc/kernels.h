@@ -5,12 +5,28 @@
 
 namespace qlk {
 
-hipError_t launch_nf4_quantize(const float* W, int64_t numel, uint8_t* packed, float* absmax,
-                               hipStream_t st);
+// A 16-level 4-bit codebook (ascending) and its 15 decision thresholds:
+// thr[i] is the exact midpoint of lv[i] and lv[i+1] rounded toward -inf, so
+// that "n > thr[i]" <=> "n lies strictly above the midpoint" (ties go to the
+// lower index).  NF4 is one instance; the uniform INT4 comparison another.
+struct Codebook4 {
+  float lv[16];
+  float thr[15];
+};
+Codebook4 make_codebook(const float* levels16);
+Codebook4 nf4_codebook4();
+
+hipError_t launch_nf4_quantize(const float* W, int64_t numel, const Codebook4& cb, uint8_t* packed,
+                               float* absmax, hipStream_t st);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, float* scales,
                                float* mean, hipStream_t st);
 hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
-                              const float* mean, int64_t numel, uint16_t* out, hipStream_t st);
+                              const float* mean, int64_t numel, const Codebook4& cb, uint16_t* out,
+                              hipStream_t st);
+// LoRA dropout: Xd = bf16(x * scale) where Philox4x32-10 keeps the element,
+// 0 elsewhere; one mask bit per element.  numel % 32 == 0.
+hipError_t launch_lora_dropout(const uint16_t* X, int64_t numel, uint32_t threshold, float scale,
+                               uint64_t seed, uint16_t* Xd, uint32_t* mask, hipStream_t st);
 
 // Base weight [N, K] as stored: NF4 (packed, codes, scales, mean) or, for
 // the unquantised comparison path, plain bf16 (`bf16` non-null, the NF4
@@ -43,9 +59,12 @@ struct BwdPlan {
 FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r);
 BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r);
 
+// Xa: input of the adapter's down projection (the dropout output); null
+// means X itself.
 hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                             const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
-                            void* ws, const FwdPlan& plan, hipStream_t st);
+                            void* ws, const FwdPlan& plan, hipStream_t st,
+                            const uint16_t* Xa = nullptr);
 // Workgroup tile rows walked together by tile_coords (balances the operand
 // footprints each XCD keeps in its L2).
 int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes);
@@ -56,19 +75,30 @@ hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, cons
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
 // dX = dY W_hat (+ s U A) for N a multiple of 256 (else the tile engine runs).
 bool dx_nf4_supported(int64_t N);
+// With a dropout mask (bit per element of dX, row-major), the adapter term
+// becomes mask * keep_scale * s U A.
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
                          const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
-                         hipStream_t st);
+                         hipStream_t st, const uint32_t* mask = nullptr, float keep_scale = 1.0f);
+// dX (+)= bf16(mask * keep_scale * s U A): the adapter term alone, for the
+// tile-engine fallback of the dropout backward.
+hipError_t launch_dx_adapter_masked(const uint16_t* U, const uint16_t* A, int64_t M, int64_t K,
+                                    int r, float s, const uint32_t* mask, float keep_scale,
+                                    uint16_t* dX, bool accumulate, hipStream_t st);
 // out[M, r] (bf16) = S[M, C] W^T with W = [r, C] or, transposed, [C, r].
 hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, bool transposed,
                          int r, uint16_t* out, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
-                       hipStream_t st);
+                       hipStream_t st, const uint16_t* Xa = nullptr);
+// X is the adapter input (the dropout output Xd when mask is non-null): it
+// feeds T (when not given) and dA.  mask/keep_scale: dropout of the adapter
+// input, applied to the adapter term of dX.
 hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
                             const uint16_t* A, const uint16_t* B, int r, float s,
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,
-                            bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st);
+                            bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st,
+                            const uint32_t* mask = nullptr, float keep_scale = 1.0f);
 
 // Measurement hook: events recorded around individual launches.
 enum TimedKernel { TK_NONE = 0, TK_FWD_GEMM = 1, TK_DX_GEMM = 2, TK_GEMV = 3, TK_COUNT = 4 };

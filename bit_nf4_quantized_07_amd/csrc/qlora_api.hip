@@ -85,7 +85,8 @@ qlk::NF4Weight weight_bf16(const uint16_t* W, int64_t N, int64_t K) {
 
 int fwd_common(const uint16_t* X, int64_t M, int64_t K, int64_t N, const qlk::NF4Weight& w,
                const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
-               uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream) {
+               uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream,
+               const uint16_t* Xa = nullptr) {
   if (!Y) return QLORA_ERR_NULL;
   if (!aligned16(Y) || (T_out && !aligned16(T_out))) return QLORA_ERR_ALIGN;
   const qlk::FwdPlan plan = qlk::plan_fwd(M, K, N, r);
@@ -93,13 +94,14 @@ int fwd_common(const uint16_t* X, int64_t M, int64_t K, int64_t N, const qlk::NF
   if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
   const float s = alpha / (float)r;
   return launch_status(qlk::launch_qlora_fwd(X, M, w, A, B, r, s, Y, T_out, workspace, plan,
-                                             as_stream(stream)));
+                                             as_stream(stream), Xa));
 }
 
 int bwd_common(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
                const qlk::NF4Weight& w, const uint16_t* A, const uint16_t* B, int r, float alpha,
                const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               size_t workspace_bytes, void* stream, const uint32_t* mask = nullptr,
+               float keep_scale = 1.0f) {
   if (!dY || !dA || !dB) return QLORA_ERR_NULL;
   if (flags & ~QLORA_BWD_ACCUMULATE_DX) return QLORA_ERR_ARG;
   if (!aligned16(dY) || !aligned16(dA) || !aligned16(dB) || (dX && !aligned16(dX)) ||
@@ -111,7 +113,44 @@ int bwd_common(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int6
   const float s = alpha / (float)r;
   return launch_status(qlk::launch_qlora_bwd(dY, X, M, w, A, B, r, s, T, dX, dA, dB,
                                              (flags & QLORA_BWD_ACCUMULATE_DX) != 0, workspace,
-                                             plan, as_stream(stream)));
+                                             plan, as_stream(stream), mask, keep_scale));
+}
+
+int check_codebook(const float* levels) {
+  if (!levels) return QLORA_ERR_NULL;
+  for (int i = 0; i < 16; ++i)
+    if (!isfinite(levels[i]) || (i > 0 && !(levels[i - 1] < levels[i]))) return QLORA_ERR_ARG;
+  return QLORA_OK;
+}
+
+bool valid_p(double p) { return p >= 0.0 && p < 1.0; }   // false for NaN
+uint32_t dropout_threshold(double p) { return (uint32_t)floor(p * 4294967296.0); }
+float dropout_scale(double p) { return (float)(1.0 / (1.0 - p)); }
+
+int quantize_common(const float* W0, int64_t N, int64_t K, int blocksize, const qlk::Codebook4& cb,
+                    uint8_t* packed, float* absmax, void* stream) {
+  if (!W0 || !packed || !absmax) return QLORA_ERR_NULL;
+  if (blocksize != kBlock) return QLORA_ERR_UNSUPPORTED;
+  int st = check_weight_shape(N, K);
+  if (st) return st;
+  if (N * K / kBlock > (int64_t)0x7fffffff * 32) return QLORA_ERR_SHAPE;
+  if (!aligned16(W0) || !aligned16(packed) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
+  return launch_status(qlk::launch_nf4_quantize(W0, N * K, cb, packed, absmax, as_stream(stream)));
+}
+
+int dequant_common(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                   const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
+                   const qlk::Codebook4& cb, uint16_t* W_bf16, void* stream) {
+  if (!packed || !codes || !scales || !mean || !W_bf16) return QLORA_ERR_NULL;
+  if (blocksize != kBlock || dq_blocksize != kDQBlock) return QLORA_ERR_UNSUPPORTED;
+  int st = check_weight_shape(N, K);
+  if (st) return st;
+  if (N * K / 32 / 256 > 0x7fffffff) return QLORA_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(codes) || !aligned16(scales) || !aligned16(mean) ||
+      !aligned16(W_bf16))
+    return QLORA_ERR_ALIGN;
+  return launch_status(
+      qlk::launch_nf4_dequant(packed, codes, scales, mean, N * K, cb, W_bf16, as_stream(stream)));
 }
 
 }  // namespace
@@ -120,13 +159,14 @@ extern "C" {
 
 int nf4_quantize(const float* W0, int64_t N, int64_t K, int blocksize, uint8_t* packed,
                  float* absmax, void* stream) {
-  if (!W0 || !packed || !absmax) return QLORA_ERR_NULL;
-  if (blocksize != kBlock) return QLORA_ERR_UNSUPPORTED;
-  int st = check_weight_shape(N, K);
+  return quantize_common(W0, N, K, blocksize, qlk::nf4_codebook4(), packed, absmax, stream);
+}
+
+int codebook_quantize(const float* W0, int64_t N, int64_t K, int blocksize, const float* levels,
+                      uint8_t* packed, float* absmax, void* stream) {
+  int st = check_codebook(levels);
   if (st) return st;
-  if (N * K / kBlock > (int64_t)0x7fffffff * 32) return QLORA_ERR_SHAPE;
-  if (!aligned16(W0) || !aligned16(packed) || !aligned16(absmax)) return QLORA_ERR_ALIGN;
-  return launch_status(qlk::launch_nf4_quantize(W0, N * K, packed, absmax, as_stream(stream)));
+  return quantize_common(W0, N, K, blocksize, qlk::make_codebook(levels), packed, absmax, stream);
 }
 
 int double_quant(const float* absmax, int64_t nblocks, int dq_blocksize, uint8_t* codes,
@@ -143,16 +183,28 @@ int double_quant(const float* absmax, int64_t nblocks, int dq_blocksize, uint8_t
 int nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
                 const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
                 uint16_t* W_bf16, void* stream) {
-  if (!packed || !codes || !scales || !mean || !W_bf16) return QLORA_ERR_NULL;
-  if (blocksize != kBlock || dq_blocksize != kDQBlock) return QLORA_ERR_UNSUPPORTED;
-  int st = check_weight_shape(N, K);
+  return dequant_common(packed, codes, scales, mean, N, K, blocksize, dq_blocksize,
+                        qlk::nf4_codebook4(), W_bf16, stream);
+}
+
+int codebook_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                     const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
+                     const float* levels, uint16_t* W_bf16, void* stream) {
+  int st = check_codebook(levels);
   if (st) return st;
-  if (N * K / 32 / 256 > 0x7fffffff) return QLORA_ERR_SHAPE;
-  if (!aligned16(packed) || !aligned16(codes) || !aligned16(scales) || !aligned16(mean) ||
-      !aligned16(W_bf16))
-    return QLORA_ERR_ALIGN;
-  return launch_status(
-      qlk::launch_nf4_dequant(packed, codes, scales, mean, N * K, W_bf16, as_stream(stream)));
+  return dequant_common(packed, codes, scales, mean, N, K, blocksize, dq_blocksize,
+                        qlk::make_codebook(levels), W_bf16, stream);
+}
+
+int lora_dropout(const uint16_t* X, int64_t M, int64_t K, double p, uint64_t seed, uint16_t* Xd,
+                 uint32_t* mask, void* stream) {
+  if (!X || !Xd || !mask) return QLORA_ERR_NULL;
+  if (M <= 0 || K <= 0 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return QLORA_ERR_SHAPE;
+  if (M * K * 2 >= kMaxBufferBytes) return QLORA_ERR_SHAPE;
+  if (!valid_p(p)) return QLORA_ERR_ARG;
+  if (!aligned16(X) || !aligned16(Xd) || !aligned16(mask)) return QLORA_ERR_ALIGN;
+  return launch_status(qlk::launch_lora_dropout(X, M * K, dropout_threshold(p), dropout_scale(p),
+                                                seed, Xd, mask, as_stream(stream)));
 }
 
 int qlora_merge(const uint8_t* packed, const uint8_t* codes, const float* scales,
@@ -188,6 +240,20 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const u
                     T_out, workspace, workspace_bytes, stream);
 }
 
+int qlora_linear_fwd_dropout(const uint16_t* X, const uint16_t* Xd, int64_t M, int64_t K,
+                             int64_t N, const uint8_t* packed, const uint8_t* codes,
+                             const float* scales, const float* mean, const uint16_t* A,
+                             const uint16_t* B, int r, float alpha, uint16_t* Y,
+                             uint16_t* T_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
+  if (st) return st;
+  if (!Xd) return QLORA_ERR_NULL;
+  if (!aligned16(Xd)) return QLORA_ERR_ALIGN;
+  return fwd_common(X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, Y,
+                    T_out, workspace, workspace_bytes, stream, Xd);
+}
+
 int qlora_linear_fwd_bf16(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W,
                           const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
                           uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -206,6 +272,22 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K
   if (st) return st;
   return bwd_common(dY, X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, T,
                     dX, dA, dB, flags, workspace, workspace_bytes, stream);
+}
+
+int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* Xd, const uint32_t* mask,
+                             double p, int64_t M, int64_t K, int64_t N, const uint8_t* packed,
+                             const uint8_t* codes, const float* scales, const float* mean,
+                             const uint16_t* A, const uint16_t* B, int r, float alpha,
+                             const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  // Xd takes the place of X: it is the adapter input that feeds T and dA.
+  int st = check_linear(Xd, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
+  if (st) return st;
+  if (!mask) return QLORA_ERR_NULL;
+  if (!aligned16(mask)) return QLORA_ERR_ALIGN;
+  if (!valid_p(p)) return QLORA_ERR_ARG;
+  return bwd_common(dY, Xd, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, T,
+                    dX, dA, dB, flags, workspace, workspace_bytes, stream, mask, dropout_scale(p));
 }
 
 int qlora_linear_bwd_bf16(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,

@@ -6,6 +6,9 @@
 // blocks of 64 consecutive weights with one absmax constant each; the
 // constants are quantised again to 8 bits around their mean with one fp32
 // scale per 256 constants.
+#include <math.h>
+#include <string.h>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -14,8 +17,10 @@ namespace qlk {
 // ---------------------------------------------------------------------------
 // nf4_quantize: 8 lanes per block of 64, each lane 8 consecutive weights.
 // ---------------------------------------------------------------------------
+// The codebook (NF4, or another 16-level table such as uniform INT4) comes
+// in as a kernel argument with its decision thresholds.
 __global__ void __launch_bounds__(256)
-k_nf4_quantize(const float* __restrict__ W, int64_t nblocks,
+k_nf4_quantize(const float* __restrict__ W, int64_t nblocks, Codebook4 cb,
                uint8_t* __restrict__ packed, float* __restrict__ absmax) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t blk = gid >> 3;
@@ -25,7 +30,7 @@ k_nf4_quantize(const float* __restrict__ W, int64_t nblocks,
 
   float thr[15];
 #pragma unroll
-  for (int i = 0; i < 15; ++i) thr[i] = nf4_threshold(i);
+  for (int i = 0; i < 15; ++i) thr[i] = cb.thr[i];
 
   const float4* src = reinterpret_cast<const float4*>(W + blk * kBlock + sub * 8);
   const float4 a = src[0], b = src[1];
@@ -40,7 +45,8 @@ k_nf4_quantize(const float* __restrict__ W, int64_t nblocks,
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // IEEE division (correctly rounded); an all-zero block maps to level 7.
+    // IEEE division (correctly rounded); an all-zero block has n = 0 (the
+    // NF4 zero level, index 7).
     const float n = (m > 0.0f) ? w[i] / m : 0.0f;
     uint32_t c = 0;
 #pragma unroll
@@ -171,9 +177,14 @@ k_dq_codes(const float* __restrict__ absmax, int64_t nb, const float* __restrict
 __global__ void __launch_bounds__(256)
 k_nf4_dequant(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
               const float* __restrict__ scales, const float* __restrict__ mean,
-              int64_t nwords, uint16_t* __restrict__ out) {
+              int64_t nwords, Codebook4 cb, uint16_t* __restrict__ out) {
   __shared__ float q4[16];
-  if (threadIdx.x < 16) q4[threadIdx.x] = nf4_level(threadIdx.x);
+  if (threadIdx.x < 16) {
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v = (int)threadIdx.x == i ? cb.lv[i] : v;   // no dynamic index
+    q4[threadIdx.x] = v;
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t w0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 256;  // first word of the wave
@@ -201,12 +212,31 @@ k_nf4_dequant(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ co
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_nf4_quantize(const float* W, int64_t numel, uint8_t* packed, float* absmax,
-                               hipStream_t st) {
+Codebook4 make_codebook(const float* levels16) {
+  Codebook4 cb;
+  for (int i = 0; i < 16; ++i) cb.lv[i] = levels16[i];
+  for (int i = 0; i < 15; ++i) {
+    const double m = ((double)cb.lv[i] + (double)cb.lv[i + 1]) * 0.5;   // exact in fp64
+    float t = (float)m;
+    if ((double)t > m) t = nextafterf(t, -INFINITY);                    // round toward -inf
+    cb.thr[i] = t;
+  }
+  return cb;
+}
+
+Codebook4 nf4_codebook4() {
+  float lv[16];
+  for (int i = 0; i < 16; ++i) memcpy(&lv[i], &kNF4Bits[i], 4);
+  return make_codebook(lv);
+}
+
+hipError_t launch_nf4_quantize(const float* W, int64_t numel, const Codebook4& cb, uint8_t* packed,
+                               float* absmax, hipStream_t st) {
   const int64_t nb = numel / kBlock;
   const int64_t threads = nb * 8;
   const int64_t grid = (threads + 255) / 256;
-  hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)grid), dim3(256), 0, st, W, nb, packed, absmax);
+  hipLaunchKernelGGL(k_nf4_quantize, dim3((unsigned)grid), dim3(256), 0, st, W, nb, cb, packed,
+                     absmax);
   return hipGetLastError();
 }
 
@@ -232,11 +262,12 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, 
 }
 
 hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
-                              const float* mean, int64_t numel, uint16_t* out, hipStream_t st) {
+                              const float* mean, int64_t numel, const Codebook4& cb, uint16_t* out,
+                              hipStream_t st) {
   const int64_t nwords = numel / 8;                  // numel % 64 == 0
   const int64_t grid = (nwords + 1023) / 1024;        // 4 waves x 256 words
   hipLaunchKernelGGL(k_nf4_dequant, dim3((unsigned)grid), dim3(256), 0, st, packed, codes, scales,
-                     mean, nwords, out);
+                     mean, nwords, cb, out);
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ extern "C" {
 #define QLORA_ERR_WORKSPACE     -5  /* workspace NULL or smaller than required      */
 #define QLORA_ERR_LAUNCH        -6  /* the HIP runtime refused a launch             */
 #define QLORA_ERR_ARG           -7  /* other invalid argument (alpha not finite,
-                                       unknown flag bits)                            */
+                                       unknown flag bits, p outside [0, 1), a
+                                       codebook not finite and ascending)            */
 
 /* qlora_linear_bwd flag: add the computed dX into the bf16 values already in
  * dX instead of overwriting them (used when two linears share an input, as
@@ -95,6 +96,28 @@ int double_quant(const float* absmax, int64_t nblocks, int dq_blocksize,
 int nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
                 const float* mean, int64_t N, int64_t K, int blocksize,
                 int dq_blocksize, uint16_t* W_bf16, void* stream);
+
+/* ---- other 4-bit codebooks through the same kernels ---------------------- */
+
+/* Blockwise quantisation onto any ascending 16-level codebook, with the NF4
+ * rules (absmax per 64, n = w / absmax, nearest level with ties to the lower
+ * index, n = 0 for an all-zero block).  For the comparison the pages draw
+ * between NF4 and uniform INT4, whose evenly spaced levels waste resolution
+ * where normal weights are dense (learn-interview-questions §2, "4-bit
+ * NormalFloat (NF4) vs. Standard INT4"; llm-compass 方法与公式 item 1).
+ *   levels  HOST memory, 16 finite fp32 values, strictly ascending
+ * Decision thresholds are the exact midpoints rounded toward -inf.  Same
+ * outputs, sizes and rules as nf4_quantize (which is this call with the NF4
+ * levels); QLORA_ERR_ARG for a codebook that is not finite and ascending.
+ * Bit-exact. */
+int codebook_quantize(const float* W0, int64_t N, int64_t K, int blocksize,
+                      const float* levels, uint8_t* packed, float* absmax, void* stream);
+
+/* Dequantisation with the same codebook: W_bf16[i] = RNE_bf16(fp32(
+ * levels[nibble] * a_hat)), a_hat as in nf4_dequant.  Bit-exact. */
+int codebook_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                     const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
+                     const float* levels, uint16_t* W_bf16, void* stream);
 
 /* ---- the linear layer --------------------------------------------------- */
 
@@ -152,6 +175,49 @@ int qlora_linear_bwd_bf16(const uint16_t* dY, const uint16_t* X, int64_t M, int6
                           const uint16_t* W, const uint16_t* A, const uint16_t* B, int r,
                           float alpha, const uint16_t* T, uint16_t* dX, float* dA, float* dB,
                           int flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- LoRA dropout on the adapter input ---------------------------------- */
+
+/* Every training recipe on the pages sets lora_dropout = 0.05 (aigrafen.se
+ * "QLoRA", code block; llm-compass "QLoRA", code under 实现要点; skillbyai
+ * "A QLoRA setup in outline"; learn-interview-questions §3): elements of the
+ * input of A are dropped and the rest scaled by 1/(1-p); the base sees X.
+ *
+ * lora_dropout draws the mask and writes the dropped input:
+ *   element i of the row-major X [M, K] is kept iff word i % 4 of
+ *   Philox4x32-10(counter = (g mod 2^32, g div 2^32, 0, 0),
+ *                 key = (seed mod 2^32, seed div 2^32)),  g = i div 4,
+ *   is >= floor(p * 2^32)  (Salmon et al., "Parallel random numbers: as easy
+ *   as 1, 2, 3", SC 2011; a pure function of (seed, i));
+ *   Xd[i] = kept ? RNE_bf16(fp32(x * fp32(1/(1-p)))) : +0      bf16 [M, K]
+ *   mask[i / 32] bit (i % 32) = kept                           uint32 [M*K/32]
+ * Requires 0 <= p < 1, M >= 1, K % 32 == 0, X and Xd under 2 GiB.  Bit-exact.
+ * Use a fresh seed per step and layer. */
+int lora_dropout(const uint16_t* X, int64_t M, int64_t K, double p, uint64_t seed,
+                 uint16_t* Xd, uint32_t* mask, void* stream);
+
+/* Forward with the dropped adapter input:
+ *   Y = X W_hat^T + s (Xd A^T) B^T,   T_out = Xd A^T
+ * Xd bf16 [M, K] from lora_dropout; everything else as qlora_linear_fwd. */
+int qlora_linear_fwd_dropout(const uint16_t* X, const uint16_t* Xd, int64_t M, int64_t K,
+                             int64_t N, const uint8_t* packed, const uint8_t* codes,
+                             const float* scales, const float* mean, const uint16_t* A,
+                             const uint16_t* B, int r, float alpha, uint16_t* Y,
+                             uint16_t* T_out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Backward of qlora_linear_fwd_dropout, the mask held fixed.  With U = dY B:
+ *   dX = dY W_hat + (s U A) * mask * fp32(1/(1-p))     bf16 [M, K]
+ *   dA = s U^T Xd,   dB = s dY^T (Xd A^T)               fp32
+ * T = Xd A^T from the forward (NULL = recompute from Xd); mask and p as given
+ * to lora_dropout.  Flags, workspace, shape rules and tolerances as in
+ * qlora_linear_bwd. */
+int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* Xd, const uint32_t* mask,
+                             double p, int64_t M, int64_t K, int64_t N, const uint8_t* packed,
+                             const uint8_t* codes, const float* scales, const float* mean,
+                             const uint16_t* A, const uint16_t* B, int r, float alpha,
+                             const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace the forward (is_bwd = 0) or backward (is_bwd = 1)
  * needs for these sizes; 0 means none.  Returns 0 for invalid sizes too. */

@@ -181,3 +181,66 @@ def test_merge_validation():
     assert call(alpha=float("nan")) == q.ERR_ARG
     assert call(B=MIS) == q.ERR_ALIGN
     assert call(out=MIS) == q.ERR_ALIGN
+
+
+def _fl16(vals):
+    return ctypes.cast((ctypes.c_float * 16)(*vals), ctypes.c_void_p)
+
+
+def test_codebook_validation():
+    good = [float(v) for v in oracle.int4_codebook()]
+    bad_order = list(good)
+    bad_order[3], bad_order[4] = bad_order[4], bad_order[3]
+    dup = list(good)
+    dup[5] = dup[4]
+    nan = list(good)
+    nan[0] = float("nan")
+    fq, fd = lib.codebook_quantize, lib.codebook_dequant
+    assert fq(D, 4, 64, 64, None, D, D, None) == q.ERR_NULL
+    for lv in (bad_order, dup, nan):
+        assert fq(D, 4, 64, 64, _fl16(lv), D, D, None) == q.ERR_ARG
+        assert fd(D, D, D, D, 4, 64, 64, 256, _fl16(lv), D, None) == q.ERR_ARG
+    assert fq(None, 4, 64, 64, _fl16(good), D, D, None) == q.ERR_NULL
+    assert fq(D, 4, 100, 64, _fl16(good), D, D, None) == q.ERR_SHAPE
+    assert fq(D, 4, 64, 32, _fl16(good), D, D, None) == q.ERR_UNSUPPORTED
+    assert fq(D, 4, 64, 64, _fl16(good), MIS, D, None) == q.ERR_ALIGN
+    assert fd(D, D, D, D, 4, 64, 64, 256, None, D, None) == q.ERR_NULL
+    assert fd(D, D, D, D, 4, 64, 64, 128, _fl16(good), D, None) == q.ERR_UNSUPPORTED
+    assert fd(D, D, D, D, 4, 64, 64, 256, _fl16(good), MIS, None) == q.ERR_ALIGN
+
+
+def test_dropout_validation():
+    f = lib.lora_dropout
+    assert f(None, 4, 64, 0.05, 1, D, D, None) == q.ERR_NULL
+    assert f(D, 4, 64, 0.05, 1, D, None, None) == q.ERR_NULL
+    assert f(D, 4, 48, 0.05, 1, D, D, None) == q.ERR_SHAPE        # K % 32
+    assert f(D, 0, 64, 0.05, 1, D, D, None) == q.ERR_SHAPE
+    assert f(D, 1 << 18, 1 << 12, 0.05, 1, D, D, None) == q.ERR_SHAPE   # X = 2 GiB
+    for p in (1.0, -0.01, float("nan"), 2.0):
+        assert f(D, 4, 64, p, 1, D, D, None) == q.ERR_ARG
+    assert f(MIS, 4, 64, 0.05, 1, D, D, None) == q.ERR_ALIGN
+    assert f(D, 4, 64, 0.05, 1, D, MIS, None) == q.ERR_ALIGN
+
+
+def test_linear_dropout_validation():
+    ff, fb = lib.qlora_linear_fwd_dropout, lib.qlora_linear_bwd_dropout
+    fwd_ok = [D, D, 64, 256, 256, D, D, D, D, D, D, 16, 32.0, D, D, D, 1 << 30, None]
+    bwd_ok = [D, D, D, 0.05, 64, 256, 256, D, D, D, D, D, D, 16, 32.0, D, D, D, D, 0, D,
+              1 << 30, None]
+
+    def call(f, base, changes):
+        a = list(base)
+        for k, v in changes.items():
+            a[k] = v
+        return f(*a)
+    assert call(ff, fwd_ok, {1: None}) == q.ERR_NULL          # Xd
+    assert call(ff, fwd_ok, {1: MIS}) == q.ERR_ALIGN
+    assert call(ff, fwd_ok, {3: 100}) == q.ERR_SHAPE          # K % 64
+    assert call(ff, fwd_ok, {0: None}) == q.ERR_NULL          # X
+    assert call(fb, bwd_ok, {2: None}) == q.ERR_NULL          # mask
+    assert call(fb, bwd_ok, {2: MIS}) == q.ERR_ALIGN
+    assert call(fb, bwd_ok, {3: 1.0}) == q.ERR_ARG            # p
+    assert call(fb, bwd_ok, {3: float("nan")}) == q.ERR_ARG
+    assert call(fb, bwd_ok, {1: None}) == q.ERR_NULL          # Xd
+    assert call(fb, bwd_ok, {19: 4}) == q.ERR_ARG             # unknown flag
+    assert call(fb, bwd_ok, {20: None}) == q.ERR_WORKSPACE
