@@ -20,11 +20,14 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                    MFMA peak
   lora_bf16_base   the same step with an unquantised bf16 base weight (LoRA
                    versus QLoRA), and the QLoRA / LoRA step-time ratio
+  lora_dropout     the same step with LoRA dropout p = 0.05 on the adapter
+                   input (mask drawn every step), and its ratio to the step
   gemv             the small-M forward (W0 28672x8192, M = 1, 4, 16): bytes
                    the GEMV kernel must move over its average duration vs HBM
-  standalone       the load-time kernels (quantize, double quant, dequant) and the
-                   adapter merge in GB/s, with the merge's error against the
-                   unquantised base
+  standalone       the load-time kernels (quantize, double quant, dequant), the
+                   adapter merge and the dropout kernel in GB/s, with the
+                   merge's error against the unquantised base and the NF4 vs
+                   uniform INT4 reconstruction error of the base weight
   cpu_baseline     the CPU oracle timed on the host cores on a bounded sample
 """
 from __future__ import annotations
@@ -184,6 +187,21 @@ def linear_step(q, d, ws, weight="qw"):
                  dX_out=d["dX"], dA_out=d["dA"], dB_out=d["dB"], workspace=ws)
 
 
+DROPOUT_P = 0.05
+
+
+def dropout_step(q, d, ws, seed):
+    """The step with LoRA dropout on the adapter input: a fresh mask, the
+    forward with the dropped input feeding A, the backward with the mask."""
+    lin = d["lin"]
+    q.dropout(d["X"], DROPOUT_P, seed, Xd_out=d["Xd"], mask_out=d["mask"])
+    q.linear_fwd_dropout(d["X"], d["Xd"], d["qw"], d["A"], d["B"], lin.alpha, out=d["Y"],
+                         T_out=d["T"], workspace=ws)
+    q.linear_bwd_dropout(d["dY"], d["Xd"], d["mask"], DROPOUT_P, d["qw"], d["A"], d["B"],
+                         lin.alpha, T=d["T"], dX_out=d["dX"], dA_out=d["dA"], dB_out=d["dB"],
+                         workspace=ws)
+
+
 def run_linear(args, q, torch, wl, lib, ev):
     """Configuration 2 (default): one linear, fwd + bwd."""
     cfg = wl.workloads()["c2_linear_4096"]
@@ -255,12 +273,27 @@ def run_linear(args, q, torch, wl, lib, ev):
     lora_bf16 = dict(ms_per_step=round(ms_bf16, 4),
                      value=round(flops / (ms_bf16 * 1e-3) / 1e12, 2), unit="TFLOP/s",
                      qlora_step_over_lora_step=round(ms / ms_bf16, 4))
+    # The same step with LoRA dropout p = 0.05 on the adapter input.
+    for d in sets:
+        d["Xd"] = torch.empty_like(d["X"])
+        d["mask"] = torch.empty(M * lin.K // 32, dtype=torch.int32, device="cuda")
+    for i in range(args.warmup):
+        dropout_step(q, sets[i % len(sets)], ws, 1000 + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        dropout_step(q, sets[i % len(sets)], ws, i)
+    torch.cuda.synchronize()
+    ms_drop = (time.perf_counter() - t0) * 1e3 / K
+    lora_dropout = dict(p=DROPOUT_P, ms_per_step=round(ms_drop, 4),
+                        value=round(flops / (ms_drop * 1e-3) / 1e12, 2), unit="TFLOP/s",
+                        step_over_plain_step=round(ms_drop / ms, 4))
     config = dict(workload=cfg.name, M=M, N=lin.N, K=lin.K, r=lin.r, alpha=lin.alpha,
                   blocksize=64, dq_blocksize=256, input_sets=args.sets,
                   step="qlora_linear_fwd + qlora_linear_bwd",
                   flops_per_step=flops)
     return dict(value=value, ms=ms, config=config, roofline=roofline, lora_bf16=lora_bf16,
-                kernels={k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()})
+                lora_dropout=lora_dropout, kernels={k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()})
 
 
 def run_gemv(args, q, torch, wl, lib, ev):
@@ -352,10 +385,21 @@ def run_standalone(args, q, torch, lib, ev):
         w = d["qw"]
         return lib.qlora_merge(ptr(w.packed), ptr(w.codes), ptr(w.scales), ptr(w.mean), N, K, 64,
                                256, ptr(A), ptr(B), r, alpha, ptr(d["out"]), stream)
+    # LoRA dropout of an activation tensor of the default workload (2048 x 4096).
+    Md = 2048
+    for i, d in enumerate(sets):
+        d["X"] = (torch.randn(Md, K, generator=g, device="cuda") ).to(torch.bfloat16)
+        d["Xd"] = torch.empty_like(d["X"])
+        d["mask"] = torch.empty(Md * K // 32, dtype=torch.int32, device="cuda")
+
+    def drop(d):
+        return lib.lora_dropout(ptr(d["X"]), Md, K, 0.05, 12345, ptr(d["Xd"]), ptr(d["mask"]),
+                                stream)
     calls = [("nf4_quantize", quant, N * K * 4 + N * K // 2 + nb * 4),
              ("double_quant", dq, nb * 4 + nb + nsc * 4 + 4),
              ("nf4_dequant", deq, N * K // 2 + nb + nsc * 4 + 4 + N * K * 2),
-             ("qlora_merge", mrg, N * K // 2 + nb + nsc * 4 + 4 + 2 * r * (N + K) + N * K * 2)]
+             ("qlora_merge", mrg, N * K // 2 + nb + nsc * 4 + 4 + 2 * r * (N + K) + N * K * 2),
+             ("lora_dropout", drop, Md * K * 4 + Md * K // 8)]
     out = dict(shape=[N, K], sets=nsets, calls=n)
     for name, fn, nbytes in calls:
         for i in range(10):
@@ -385,6 +429,16 @@ def run_standalone(args, q, torch, lib, ev):
     bf16_path = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16)
     out["qlora_merge"]["rel_err_vs_unquantized"] = float(np.linalg.norm(f64(d["out"]) - exact) / nrm)
     out["qlora_merge"]["rel_err_bf16_base_merge"] = float(np.linalg.norm(f64(bf16_path) - exact) / nrm)
+    # Reconstruction error of the base weight with the NF4 codebook and with
+    # 16 evenly spaced levels (uniform INT4), same blocks and constants.
+    int4 = [float(np.float32(-1.0 + 2.0 * i / 15.0)) for i in range(16)]
+    W64 = f64(d["W"])
+    errs = {}
+    for name, lv in (("nf4", q.codebook()), ("int4_uniform", int4)):
+        deq_w = q.codebook_dequant(q.quantize_with_codebook(d["W"], lv), lv)
+        torch.cuda.synchronize()
+        errs[name] = float(np.linalg.norm(f64(deq_w) - W64) / np.linalg.norm(W64))
+    out["codebook_rel_err"] = errs
     return out
 
 
@@ -694,6 +748,7 @@ def main():
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
                 data="synthetic", config=lin["config"], roofline=lin["roofline"],
                 cpu_baseline=cpu, kernels=lin["kernels"], lora_bf16_base=lin["lora_bf16"],
+                lora_dropout=lin["lora_dropout"],
                 gemv=gemv, standalone=standalone,
                 source_hash=source_hash())
     print(json.dumps(line), flush=True)

@@ -335,14 +335,15 @@ def codebook_dequant(qw: QuantizedWeight, levels):
     return out
 
 
-def dropout(X, p: float, seed: int):
+def dropout(X, p: float, seed: int, Xd_out=None, mask_out=None):
     """LoRA dropout of the adapter input: -> (Xd bf16 [M, K], mask int32
     [M*K/32], bit i % 32 of word i // 32 = element i kept)."""
     torch = _torch()
-    _need_cuda(X)
+    _need_cuda(X, Xd_out, mask_out)
     M, K = X.shape
-    Xd = torch.empty_like(X)
-    mask = torch.empty(max((M * K + 31) // 32, 4), dtype=torch.int32, device=X.device)
+    Xd = Xd_out if Xd_out is not None else torch.empty_like(X)
+    mask = mask_out if mask_out is not None else torch.empty(
+        max((M * K + 31) // 32, 4), dtype=torch.int32, device=X.device)
     _check("lora_dropout", load_library().lora_dropout(
         _ptr(X), M, K, float(p), int(seed) & (2**64 - 1), _ptr(Xd), _ptr(mask), _stream(X.device)))
     return Xd, mask[:(M * K + 31) // 32]
@@ -369,7 +370,8 @@ def linear_fwd_dropout(X, Xd, qw: QuantizedWeight, A, B, alpha: float, save_T: b
 
 
 def linear_bwd_dropout(dY, Xd, mask, p: float, qw: QuantizedWeight, A, B, alpha: float, T=None,
-                       need_dX: bool = True, accumulate_into=None, workspace=None):
+                       need_dX: bool = True, accumulate_into=None, dX_out=None, dA_out=None,
+                       dB_out=None, workspace=None):
     """Backward of linear_fwd_dropout (mask and p from `dropout`).  Returns
     (dX bf16 or None, dA fp32 [r, K], dB fp32 [N, r])."""
     torch = _torch()
@@ -380,10 +382,13 @@ def linear_bwd_dropout(dY, Xd, mask, p: float, qw: QuantizedWeight, A, B, alpha:
     if accumulate_into is not None:
         dX = accumulate_into
         flags |= BWD_ACCUMULATE_DX
+    elif dX_out is not None:
+        dX = dX_out
     else:
         dX = torch.empty(M, K, dtype=torch.bfloat16, device=Xd.device) if need_dX else None
-    dA = torch.empty(r, K, dtype=torch.float32, device=Xd.device)
-    dB = torch.empty(qw.N, r, dtype=torch.float32, device=Xd.device)
+    dA = dA_out if dA_out is not None else torch.empty(r, K, dtype=torch.float32, device=Xd.device)
+    dB = dB_out if dB_out is not None else torch.empty(qw.N, r, dtype=torch.float32,
+                                                       device=Xd.device)
     nb = workspace_bytes(M, K, qw.N, r, True)
     ws, wsb = (workspace.get(nb) if workspace is not None else _ws(Xd.device, nb))
     _check("qlora_linear_bwd_dropout", load_library().qlora_linear_bwd_dropout(
