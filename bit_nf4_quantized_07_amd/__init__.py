@@ -29,6 +29,14 @@ _I64 = ctypes.c_int64
 _I = ctypes.c_int
 _F = ctypes.c_float
 
+class LoraLinearC(ctypes.Structure):
+    """struct qlora_lora_linear of include/qlora.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("mean", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("r", ctypes.c_int), ("alpha", ctypes.c_float)]
+
+
 # name -> (restype, argtypes), mirroring include/qlora.h
 SIGNATURES = {
     "nf4_quantize": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
@@ -52,6 +60,9 @@ SIGNATURES = {
     "qlora_linear_bwd_dropout": (_I, [_P, _P, _P, ctypes.c_double, _I64, _I64, _I64, _P, _P, _P,
                                       _P, _P, _P, _I, _F, _P, _P, _P, _P, _I, _P,
                                       ctypes.c_size_t, _P]),
+    "qlora_mlp_fwd": (_I, [_P, _I64, _I64, _I64, ctypes.POINTER(LoraLinearC),
+                           ctypes.POINTER(LoraLinearC), _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                           _P]),
     "silu_mul_fwd": (_I, [_P, _P, _I64, _P, _P]),
     "silu_mul_bwd": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "nf4_codebook": (_I, [_P]),
@@ -396,6 +407,37 @@ def linear_bwd_dropout(dY, Xd, mask, p: float, qw: QuantizedWeight, A, B, alpha:
         _ptr(qw.scales), _ptr(qw.mean), _ptr(A), _ptr(B), r, float(alpha), _ptr(T), _ptr(dX),
         _ptr(dA), _ptr(dB), flags, _ptr(ws), wsb, _stream(Xd.device)))
     return dX, dA, dB
+
+
+def _lora_linear(qw: QuantizedWeight, A, B, alpha: float) -> LoraLinearC:
+    _need_cuda(A, B)
+    return LoraLinearC(_ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean),
+                       _ptr(A), _ptr(B), A.shape[0], float(alpha))
+
+
+def mlp_fwd(X, gate, up, out=None, workspace=None):
+    """Gate/up projections of a SiLU-gated MLP and the gating in one call.
+    gate, up: (QuantizedWeight [I, K], A, B, alpha).  Returns
+    (G, U, H, Tg, Tu), bf16; `out` may hold preallocated tensors of the same
+    names (a dict)."""
+    torch = _torch()
+    _need_cuda(X)
+    M, K = X.shape
+    qg, qu = gate[0], up[0]
+    I = qg.N
+    out = out or {}
+    mk = lambda n, c: out[n] if n in out else torch.empty(M, c, dtype=torch.bfloat16,
+                                                            device=X.device)
+    G, U, H = mk("G", I), mk("U", I), mk("H", I)
+    Tg, Tu = mk("Tg", gate[1].shape[0]), mk("Tu", up[1].shape[0])
+    nb = max(workspace_bytes(M, K, I, gate[1].shape[0], False),
+             workspace_bytes(M, K, I, up[1].shape[0], False))
+    ws, wsb = (workspace.get(nb) if workspace is not None else _ws(X.device, nb))
+    lg, lu = _lora_linear(*gate), _lora_linear(*up)
+    _check("qlora_mlp_fwd", load_library().qlora_mlp_fwd(
+        _ptr(X), M, K, I, ctypes.byref(lg), ctypes.byref(lu), _ptr(G), _ptr(U), _ptr(H), _ptr(Tg),
+        _ptr(Tu), _ptr(ws), wsb, _stream(X.device)))
+    return G, U, H, Tg, Tu
 
 
 def silu_mul_fwd(G, Up, out=None):

@@ -55,6 +55,12 @@ __device__ __forceinline__ float dq_threshold(int i) {
   return __double2float_rd(m);
 }
 
+// SiLU gating of the MLP glue: silu(g) u = g sigmoid(g) u, evaluated left
+// to right in fp32 (shared by the elementwise kernel and the fused gate/up
+// forward, which therefore give the same bits).
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_mul_f32(float g, float u) { return g * sigmoidf_(g) * u; }
+
 // a_hat = fp32(fp32(Q8[code] * scale) + mean): two separately rounded ops.
 __device__ __forceinline__ float absmax_decode(int code, float scale, float mean) {
 #pragma clang fp contract(off)

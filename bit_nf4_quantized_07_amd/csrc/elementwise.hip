@@ -6,7 +6,6 @@
 
 namespace qlk {
 
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
 __global__ void __launch_bounds__(256)
 k_silu_mul_fwd(const uint16_t* __restrict__ G, const uint16_t* __restrict__ U, int64_t n8,
@@ -21,7 +20,7 @@ k_silu_mul_fwd(const uint16_t* __restrict__ G, const uint16_t* __restrict__ U, i
   for (int q = 0; q < 4; ++q) {
     const float g0 = bf16_to_f32(gw[q] & 0xffffu), g1 = bf16_to_f32(gw[q] >> 16);
     const float u0 = bf16_to_f32(uw[q] & 0xffffu), u1 = bf16_to_f32(uw[q] >> 16);
-    o[q] = pack_bf16x2(g0 * sigmoidf_(g0) * u0, g1 * sigmoidf_(g1) * u1);
+    o[q] = pack_bf16x2(silu_mul_f32(g0, u0), silu_mul_f32(g1, u1));
   }
   reinterpret_cast<uint4*>(H)[i] = make_uint4(o[0], o[1], o[2], o[3]);
 }

@@ -36,6 +36,14 @@
 //    accumulators (the up-projection fused into the base GEMM).
 //  * The accumulator layout gives each lane four consecutive weight rows of
 //    one token, so Y is written 8 bytes at a time.
+//
+// Gated variant (the fused gate/up projections of a SiLU-gated MLP): each
+// wave's weight rows come from one weight, so waves 0-1 take 64 rows of the
+// gate weight and waves 2-3 the same 64 rows of the up weight, each with its
+// own NF4 constants and adapter.  After the main loop the up waves pass their
+// bf16 results through LDS to the gate waves, which write
+// H = silu(G) U (the elementwise kernel's arithmetic on the same bf16 G and
+// U); G and U are written too, for the backward.
 #include <type_traits>
 
 #include "device_common.h"
@@ -65,6 +73,15 @@ struct FwdArgs {
   float s;
   uint16_t* Y;
   int tiles_m, tiles_n, group_m;
+  // gated variant: w/T/B/r/s/Y are the gate projection's (Y = G), these the
+  // up projection's (Y2 = U); H = silu(G) U.
+  NF4Weight w2;
+  const uint16_t* T2;
+  const uint16_t* B2;
+  int r2;
+  float s2;
+  uint16_t* Y2;
+  uint16_t* H;
 };
 
 struct FwdWRegs { uint4 p; uint32_t code; float sc; };   // NF4: 32 weights + block constant
@@ -77,8 +94,9 @@ __device__ __forceinline__ bf16x8_t as_frag(const uint32_t (&d)[4]) {
 
 // BF16W: the base weight is plain bf16 (g.w.bf16) and there is nothing to
 // decode: the same kernel with the dequantisation switched off.
-template <bool BF16W>
+template <bool BF16W, bool GATED = false>
 __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
+  static_assert(!(BF16W && GATED), "the gated variant takes NF4 weights");
   using WRegs = std::conditional_t<BF16W, FwdWRegsB, FwdWRegs>;
   constexpr int kWLoads = BF16W ? 4 : 3;          // weight loads per step
   constexpr int kLoads = 8 + kWLoads;             // global loads per step
@@ -101,9 +119,12 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   int tm, tn;
   tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
   const int m0 = tm * kFwdBM;
-  const int64_t K = g.w.K, N = g.w.N, nkb = K / kBlock;
+  // This wave's weight (the up weight for waves 2-3 of the gated variant).
+  const bool upw = GATED && wave >= 2;
+  const NF4Weight W = upw ? g.w2 : g.w;
+  const int64_t K = W.K, N = W.N, nkb = K / kBlock;
   const int nk = (int)nkb;
-  const float mean = BF16W ? 0.0f : g.w.mean[0];
+  const float mean = BF16W ? 0.0f : W.mean[0];
 
   // X tile loads: wave w, load i fills rows 64 w + 8 i .. +7 (1 KB of LDS);
   // lane L lands at LDS offset 16 L, i.e. row 64 w + 8 i + L / 8, physical
@@ -121,8 +142,10 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   int xrd[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) xrd[t] = c * kXRow + (((4 * h + t) ^ swz(c)) * 8);
-  // Weight row of this lane.
-  const int64_t nrow = (int64_t)tn * kFwdBN + wave * kFwdWaveN + c;
+  // Weight rows of this wave (gated: 64 rows of each weight per tile).
+  const int64_t nw0 = GATED ? (int64_t)tn * (kFwdBN / 2) + (wave & 1) * kFwdWaveN
+                            : (int64_t)tn * kFwdBN + wave * kFwdWaveN;
+  const int64_t nrow = nw0 + c;
   const bool nvalid = nrow < N;
   const uint32_t pbytes = (uint32_t)(N * (K / 2)), cbytes = (uint32_t)(N * nkb);
   const uint32_t sbytes = (uint32_t)(((N * nkb + kDQBlock - 1) / kDQBlock) * 4);
@@ -133,9 +156,9 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   // moves the loads through the scalar offset field.  Eight buffer loads go
   // straight into LDS buffer `buf`.
   const __amdgpu_buffer_rsrc_t rx = rsrc_whole(g.X, xbytes);
-  const __amdgpu_buffer_rsrc_t rp = rsrc_whole(g.w.packed, pbytes);
-  const __amdgpu_buffer_rsrc_t rc = rsrc_whole(g.w.codes, cbytes);
-  const __amdgpu_buffer_rsrc_t rsc = rsrc_whole(g.w.scales, sbytes);
+  const __amdgpu_buffer_rsrc_t rp = rsrc_whole(W.packed, pbytes);
+  const __amdgpu_buffer_rsrc_t rc = rsrc_whole(W.codes, cbytes);
+  const __amdgpu_buffer_rsrc_t rsc = rsrc_whole(W.scales, sbytes);
   // X load j (0..7) of step kb fills rows 64 w + 8 j .. +7 of buffer `buf`;
   // weight load j (0..2) brings the packed bytes, the code, the scale.
   auto load_xj = [&](int j, uint16_t* buf, int kb) {
@@ -145,7 +168,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
         xoff[j], k * (kBlock * 2), 0, 0);
   };
   // bf16 weight: the lane's 32 weights of a step are 64 contiguous bytes.
-  const __amdgpu_buffer_rsrc_t rb = rsrc_whole(g.w.bf16, (uint32_t)(BF16W ? N * K * 2 : 0));
+  const __amdgpu_buffer_rsrc_t rb = rsrc_whole(W.bf16, (uint32_t)(BF16W ? N * K * 2 : 0));
   const uint32_t boff = nvalid ? (uint32_t)((nrow * K + 32 * h) * 2) : kOOB;
   auto load_wj = [&](int j, WRegs& R, int kb) {
     const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
@@ -290,15 +313,19 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
 
   // Adapter term: acc += (s B) T^T over r in steps of 16 (natural order).
-  for (int r0 = 0; r0 < g.r; r0 += 16) {
+  const uint16_t* const Tp = upw ? g.T2 : g.T;
+  const uint16_t* const Bp = upw ? g.B2 : g.B;
+  const int r = upw ? g.r2 : g.r;
+  const float sc = upw ? g.s2 : g.s;
+  for (int r0 = 0; r0 < r; r0 += 16) {
     const int rr = r0 + 8 * h;
     uint4 bv = make_uint4(0, 0, 0, 0);
-    if (nvalid && rr < g.r) {
-      bv = *reinterpret_cast<const uint4*>(g.B + nrow * g.r + rr);
+    if (nvalid && rr < r) {
+      bv = *reinterpret_cast<const uint4*>(Bp + nrow * r + rr);
       uint32_t wv[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        wv[q] = pack_bf16x2(bf16_to_f32(wv[q] & 0xffffu) * g.s, bf16_to_f32(wv[q] >> 16) * g.s);
+        wv[q] = pack_bf16x2(bf16_to_f32(wv[q] & 0xffffu) * sc, bf16_to_f32(wv[q] >> 16) * sc);
       bv = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
     const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, bv);
@@ -306,7 +333,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     for (int i = 0; i < 8; ++i) {
       const int m = m0 + 32 * i + c;
       uint4 tv = make_uint4(0, 0, 0, 0);
-      if (m < g.M && rr < g.r) tv = *reinterpret_cast<const uint4*>(g.T + (int64_t)m * g.r + rr);
+      if (m < g.M && rr < r) tv = *reinterpret_cast<const uint4*>(Tp + (int64_t)m * r + rr);
       acc[i] = mfma_32x32x16(bfr, __builtin_bit_cast(bf16x8_t, tv), acc[i]);
     }
   }
@@ -314,29 +341,82 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   // Accumulator i: lane holds token m = m0 + 32 i + c and weight rows
   // 8 (v / 4) + 4 h + (v % 4) of the wave's 32; four consecutive rows are
   // one 8-byte store.
-  const int64_t nw0 = (int64_t)tn * kFwdBN + wave * kFwdWaveN;
+  uint16_t* const Yp = upw ? g.Y2 : g.Y;
+  uint32_t ob[8][4][2];   // the bf16 results, kept for the gated epilogue
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int m = m0 + 32 * i + c;
-    if (m >= g.M) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t n = nw0 + 8 * q + 4 * h;
-      if (n >= N) continue;   // N % 8 == 0: a group of four is all in or all out
-      uint2 o;
-      o.x = pack_bf16x2(acc[i][4 * q + 0], acc[i][4 * q + 1]);
-      o.y = pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3]);
-      *reinterpret_cast<uint2*>(g.Y + (int64_t)m * N + n) = o;
+      ob[i][q][0] = pack_bf16x2(acc[i][4 * q + 0], acc[i][4 * q + 1]);
+      ob[i][q][1] = pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3]);
+      if (m >= g.M || n >= N) continue;   // N % 8 == 0: a group of four is all in or all out
+      *reinterpret_cast<uint2*>(Yp + (int64_t)m * N + n) = make_uint2(ob[i][q][0], ob[i][q][1]);
+    }
+  }
+  if constexpr (GATED) {
+    // Up waves (2, 3) hand their bf16 results to the gate waves (0, 1) with
+    // the same lane layout through the first X buffer: dword d of lane L of
+    // wave pair p at [d][p][L] (lane-contiguous, conflict-free).
+    uint32_t* const xch = reinterpret_cast<uint32_t*>(xs0);
+    __syncthreads();   // every wave is done with the X buffers
+    if (upw) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            xch[((8 * i + 2 * q + e) * 2 + (wave & 1)) * 64 + lane] = ob[i][q][e];
+    }
+    __syncthreads();
+    if (!upw) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + 32 * i + c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = nw0 + 8 * q + 4 * h;
+          if (m >= g.M || n >= N) continue;
+          uint32_t hv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t gw = ob[i][q][e];
+            const uint32_t uw = xch[((8 * i + 2 * q + e) * 2 + (wave & 1)) * 64 + lane];
+            hv[e] = pack_bf16x2(silu_mul_f32(bf16_to_f32(gw & 0xffffu), bf16_to_f32(uw & 0xffffu)),
+                                silu_mul_f32(bf16_to_f32(gw >> 16), bf16_to_f32(uw >> 16)));
+          }
+          *reinterpret_cast<uint2*>(g.H + (int64_t)m * N + n) = make_uint2(hv[0], hv[1]);
+        }
+      }
     }
   }
 }
 
 bool fwd_nf4_supported(int64_t K) { return (K / kBlock) % kFwdUnroll == 0; }
 
+hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, const uint16_t* Tg,
+                            const uint16_t* Bg, int rg, float sg, const NF4Weight& wu,
+                            const uint16_t* Tu, const uint16_t* Bu, int ru, float su, uint16_t* G,
+                            uint16_t* U, uint16_t* H, hipStream_t st) {
+  if (!fwd_nf4_supported(wg.K) || wg.K != wu.K || wg.N != wu.N || wg.bf16 || wu.bf16)
+    return hipErrorInvalidValue;
+  FwdArgs g{};
+  g.X = X; g.M = (int)M; g.w = wg; g.T = Tg; g.B = Bg; g.r = rg; g.s = sg; g.Y = G;
+  g.w2 = wu; g.T2 = Tu; g.B2 = Bu; g.r2 = ru; g.s2 = su; g.Y2 = U; g.H = H;
+  g.tiles_m = (int)((M + kFwdBM - 1) / kFwdBM);
+  g.tiles_n = (int)((wg.N + kFwdBN / 2 - 1) / (kFwdBN / 2));
+  g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * wg.K * 2,
+                        (double)kFwdBN * wg.K * 0.52);
+  hipLaunchKernelGGL((k_fwd_nf4<false, true>), dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
   if (!fwd_nf4_supported(w.K)) return hipErrorInvalidValue;
-  FwdArgs g;
+  FwdArgs g{};
   g.X = X; g.M = (int)M; g.w = w; g.T = T; g.B = B; g.r = r; g.s = s; g.Y = Y;
   g.tiles_m = (int)((M + kFwdBM - 1) / kFwdBM);
   g.tiles_n = (int)((w.N + kFwdBN - 1) / kFwdBN);

@@ -818,6 +818,26 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   return e;
 }
 
+hipError_t launch_mlp_fwd(const uint16_t* X, int64_t M, const LoraLinear& gate,
+                          const LoraLinear& up, uint16_t* G, uint16_t* U, uint16_t* H,
+                          uint16_t* Tg, uint16_t* Tu, void* ws, size_t ws_bytes, hipStream_t st) {
+  const int64_t K = gate.w.K, I = gate.w.N;
+  if (M > kGemvMaxM && fwd_nf4_supported(K) && !QLK_FWD_TILE_ENGINE) {
+    QLK_TRY(compute_T(X, M, K, gate.A, gate.r, Tg, st));
+    QLK_TRY(compute_T(X, M, K, up.A, up.r, Tu, st));
+    timer_begin(TK_FWD_GEMM, st);
+    const hipError_t e = launch_fwd_gated(X, M, gate.w, Tg, gate.B, gate.r, gate.s, up.w, Tu, up.B,
+                                          up.r, up.s, G, U, H, st);
+    timer_end(TK_FWD_GEMM, st);
+    return e;
+  }
+  const FwdPlan pg = plan_fwd(M, K, I, gate.r), pu = plan_fwd(M, K, I, up.r);
+  if (ws_bytes < pg.bytes || ws_bytes < pu.bytes) return hipErrorInvalidValue;
+  QLK_TRY(launch_qlora_fwd(X, M, gate.w, gate.A, gate.B, gate.r, gate.s, G, Tg, ws, pg, st));
+  QLK_TRY(launch_qlora_fwd(X, M, up.w, up.A, up.B, up.r, up.s, U, Tu, ws, pu, st));
+  return launch_silu_mul_fwd(G, U, M * I, H, st);
+}
+
 hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
                             const uint16_t* A, const uint16_t* B, int r, float s,
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,

@@ -73,6 +73,25 @@ int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes
 bool fwd_nf4_supported(int64_t K);
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
+// Fused gate/up projections of a SiLU-gated MLP (M > kGemvMaxM, K / 64 a
+// multiple of 4, both weights [I, K]): G = X Wg^T + sg Tg Bg^T,
+// U = X Wu^T + su Tu Bu^T, H = silu(G) U, all bf16 [M, I]; Tg, Tu precomputed.
+hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, const uint16_t* Tg,
+                            const uint16_t* Bg, int rg, float sg, const NF4Weight& wu,
+                            const uint16_t* Tu, const uint16_t* Bu, int ru, float su, uint16_t* G,
+                            uint16_t* U, uint16_t* H, hipStream_t st);
+// The gated MLP's gate/up forward: the fused kernel where it applies, else
+// two layer forwards and the elementwise gating.
+struct LoraLinear {
+  NF4Weight w;
+  const uint16_t* A;
+  const uint16_t* B;
+  int r;
+  float s;
+};
+hipError_t launch_mlp_fwd(const uint16_t* X, int64_t M, const LoraLinear& gate,
+                          const LoraLinear& up, uint16_t* G, uint16_t* U, uint16_t* H,
+                          uint16_t* Tg, uint16_t* Tu, void* ws, size_t ws_bytes, hipStream_t st);
 // dX = dY W_hat (+ s U A) for N a multiple of 256 (else the tile engine runs).
 bool dx_nf4_supported(int64_t N);
 // With a dropout mask (bit per element of dX, row-major), the adapter term

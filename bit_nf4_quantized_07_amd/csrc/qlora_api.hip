@@ -300,6 +300,30 @@ int qlora_linear_bwd_bf16(const uint16_t* dY, const uint16_t* X, int64_t M, int6
                     workspace, workspace_bytes, stream);
 }
 
+int qlora_mlp_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t I,
+                  const qlora_lora_linear* gate, const qlora_lora_linear* up, uint16_t* G,
+                  uint16_t* U, uint16_t* H, uint16_t* Tg, uint16_t* Tu, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!gate || !up) return QLORA_ERR_NULL;
+  const qlora_lora_linear* lin[2] = {gate, up};
+  qlk::LoraLinear L[2];
+  for (int j = 0; j < 2; ++j) {
+    const qlora_lora_linear& l = *lin[j];
+    int st = check_linear(X, M, K, I, l.packed, l.codes, l.scales, l.mean, l.A, l.B, l.r, l.alpha);
+    if (st) return st;
+    L[j].w = weight(l.packed, l.codes, l.scales, l.mean, I, K);
+    L[j].A = l.A; L[j].B = l.B; L[j].r = l.r; L[j].s = l.alpha / (float)l.r;
+    const size_t need = qlk::plan_fwd(M, K, I, l.r).bytes;
+    if (workspace_bytes < need || (need && !workspace)) return QLORA_ERR_WORKSPACE;
+  }
+  if (!G || !U || !H || !Tg || !Tu) return QLORA_ERR_NULL;
+  if (!aligned16(G) || !aligned16(U) || !aligned16(H) || !aligned16(Tg) || !aligned16(Tu) ||
+      (workspace && !aligned16(workspace)))
+    return QLORA_ERR_ALIGN;
+  return launch_status(qlk::launch_mlp_fwd(X, M, L[0], L[1], G, U, H, Tg, Tu, workspace,
+                                           workspace_bytes, as_stream(stream)));
+}
+
 int silu_mul_fwd(const uint16_t* G, const uint16_t* Up, int64_t n, uint16_t* H, void* stream) {
   if (!G || !Up || !H) return QLORA_ERR_NULL;
   if (n <= 0 || n % 8 != 0 || n / 8 / 256 > 0x7fffffff) return QLORA_ERR_SHAPE;

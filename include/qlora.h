@@ -223,6 +223,41 @@ int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* Xd, const uint3
  * needs for these sizes; 0 means none.  Returns 0 for invalid sizes too. */
 size_t qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int r, int is_bwd);
 
+/* ---- fused gate/up projections of a SiLU-gated MLP ---------------------- */
+
+/* One QLoRA linear of the MLP: NF4 base [I, K] as nf4_quantize + double_quant
+ * store it (device pointers), bf16 adapters A [r, K] and B [I, r] (device),
+ * r and alpha as in qlora_linear_fwd.  Passed by HOST pointer. */
+typedef struct qlora_lora_linear {
+  const uint8_t* packed;
+  const uint8_t* codes;
+  const float* scales;
+  const float* mean;
+  const uint16_t* A;
+  const uint16_t* B;
+  int r;
+  float alpha;
+} qlora_lora_linear;
+
+/* The gate and up projections of a SiLU-gated MLP with LoRA on both (the
+ * pages put adapters on gate_proj and up_proj as on every linear, aigrafen.se
+ * "QLoRA", code block, target_modules) and the gating, in one pass over X:
+ *   G = X Wg^T + sg (X Ag^T) Bg^T,   U = X Wu^T + su (X Au^T) Bu^T,
+ *   H = silu(G) * U,   silu(g) = g / (1 + exp(-g))
+ *   X  bf16 [M, K];   G, U, H  bf16 [M, I];   Tg, Tu  bf16 [M, rg], [M, ru]
+ * G, U, Tg and Tu are what the backward needs.  G and U are bit-identical to
+ * qlora_linear_fwd on each projection and H to silu_mul_fwd(G, U).  For
+ * M > 16 and K % 256 == 0 one kernel computes G and U tile by tile and writes
+ * H from the same tile (no second pass over G and U); other shapes run the
+ * two layer forwards and the elementwise gating.
+ * Requires the shape rules of qlora_linear_fwd for each projection (I plays
+ * N), both weights [I, K], and workspace_bytes >= qlora_workspace_bytes(M, K,
+ * I, r, 0) for both r. */
+int qlora_mlp_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t I,
+                  const qlora_lora_linear* gate, const qlora_lora_linear* up,
+                  uint16_t* G, uint16_t* U, uint16_t* H, uint16_t* Tg, uint16_t* Tu,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- serving: fold the adapter into the base ---------------------------- */
 
 /* W_merged = RNE_bf16( w_hat_bf16 + s (B A) ),  s = fp32(alpha / r).

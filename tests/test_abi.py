@@ -244,3 +244,25 @@ def test_linear_dropout_validation():
     assert call(fb, bwd_ok, {1: None}) == q.ERR_NULL          # Xd
     assert call(fb, bwd_ok, {19: 4}) == q.ERR_ARG             # unknown flag
     assert call(fb, bwd_ok, {20: None}) == q.ERR_WORKSPACE
+
+
+def test_mlp_fwd_validation():
+    f = lib.qlora_mlp_fwd
+    good = q.LoraLinearC(D, D, D, D, D, D, 16, 32.0)
+
+    def call(gate=good, up=good, M=64, K=256, I=512, G=D, U=D, H=D, Tg=D, Tu=D, ws=D,
+             wsb=1 << 30):
+        gp = None if gate is None else ctypes.byref(gate)
+        upp = None if up is None else ctypes.byref(up)
+        return f(D, M, K, I, gp, upp, G, U, H, Tg, Tu, ws, wsb, None)
+    assert call(gate=None) == q.ERR_NULL
+    assert call(up=None) == q.ERR_NULL
+    assert call(up=q.LoraLinearC(D, D, D, D, D, D, 12, 32.0)) == q.ERR_SHAPE     # r % 8
+    assert call(gate=q.LoraLinearC(D, None, D, D, D, D, 16, 32.0)) == q.ERR_NULL
+    assert call(up=q.LoraLinearC(D, D, D, D, D, D, 16, float("inf"))) == q.ERR_ARG
+    assert call(K=100) == q.ERR_SHAPE
+    assert call(I=12) == q.ERR_SHAPE
+    assert call(H=None) == q.ERR_NULL
+    assert call(Tu=None) == q.ERR_NULL
+    assert call(U=MIS) == q.ERR_ALIGN
+    assert call(M=4, ws=None, wsb=0) == q.ERR_WORKSPACE      # small M needs workspace

@@ -90,8 +90,8 @@ def run_block(X, dY, lins):
     return dict(Y=Y, dX=dX, dA=dict(gate=dAg, up=dAu, down=dAd), dB=dict(gate=dBg, up=dBu, down=dBd))
 
 
-def make_block(seed, M, D, I, r, alpha):
-    shapes = dict(gate=(I, D), up=(I, D), down=(D, I))
+def make_block(seed, M, D, I, r, alpha, with_down=True):
+    shapes = dict(gate=(I, D), up=(I, D), down=(D, I)) if with_down else dict(gate=(I, D), up=(I, D))
     host_w, dev_w = {}, {}
     for j, (name, (N, K)) in enumerate(shapes.items()):
         lin = wl.Linear(name, N, K, r, alpha)
@@ -150,3 +150,71 @@ def test_mlp_block_config3_sampled_tokens():
                                  ref_lin["up"], ref_lin["down"])
     assert_close(host_bf16_f64(got["Y"])[rows], Yr, "Y[sampled tokens]")
     assert_close(host_bf16_f64(got["dX"])[rows], dXr, "dX[sampled tokens]")
+
+
+def composed_gate_up(X, gl, ul):
+    """The reference composition on the GPU: two layer forwards and the
+    elementwise gating (separate launches)."""
+    G, Tg = q.linear_fwd(X, *gl)
+    U, Tu = q.linear_fwd(X, *ul)
+    return G, U, q.silu_mul_fwd(G, U), Tg, Tu
+
+
+@pytest.mark.parametrize("M,K,I,r", [
+    (300, 512, 704, 16),     # fused kernel, ragged last token tile and a partial row tile
+    (256, 1024, 128, 64),    # fused, two row tiles
+    (40, 256, 200, 16),      # fused, last row tile 8 of 64 rows
+    (8, 512, 256, 16),       # M <= 16: the small-M forwards and the elementwise gating
+    (100, 320, 264, 8),      # K % 256 != 0: tile-engine forwards and the elementwise gating
+])
+def test_fused_gate_up_equals_the_composition(M, K, I, r):
+    """G and U must be bit-identical to the layer forward on each projection
+    and H to silu_mul_fwd(G, U); then G, U and H against the oracle."""
+    t = pytest.importorskip("torch")
+    log(f"[mlp fused] M={M} K={K} I={I} r={r}")
+    _, _, host_w, dev_w = make_block(61, M, K, I, r, 2.0 * r, with_down=False)
+    X = wl.activations(61, 101, M, K)
+    Xd = dev_bf16(X)
+    G, U, H, Tg, Tu = q.mlp_fwd(Xd, dev_w["gate"], dev_w["up"])
+    G0, U0, H0, Tg0, Tu0 = composed_gate_up(Xd, dev_w["gate"], dev_w["up"])
+    t.cuda.synchronize()
+    for name, a, b in (("G", G, G0), ("U", U, U0), ("H", H, H0), ("Tg", Tg, Tg0), ("Tu", Tu, Tu0)):
+        assert np.array_equal(host_bf16_bits(a), host_bf16_bits(b)), name
+    ref = {}
+    for n in ("gate", "up"):
+        W, A, B = host_w[n]
+        ref[n], _ = oracle.forward(f64(X), f64(OracleWeight(W).w_bf16()), f64(A), f64(B),
+                                   2.0 * r, r)
+    assert_close(host_bf16_f64(G), ref["gate"], "G")
+    assert_close(host_bf16_f64(U), ref["up"], "U")
+    assert_close(host_bf16_f64(H), oracle.silu_mul_forward(ref["gate"], ref["up"]), "H")
+
+
+@pytest.mark.timeout(400)
+def test_fused_gate_up_config3_full_shape():
+    """c3's gate/up at full size (4096 tokens, 11008 x 4096, r = 64): bit-exact
+    against the composition, and H on sampled tokens against the oracle."""
+    t = pytest.importorskip("torch")
+    w = wl.workloads()["c3_mlp_11008"]
+    lins = {l.name: l for l in w.linears}
+    dev_w, host_w = {}, {}
+    for j, name in enumerate(("gate", "up")):
+        lin = lins[name]
+        W = wl.weight(0, w.cfg_id, j, lin)
+        A, B = wl.adapters(0, w.cfg_id, j, lin)
+        host_w[name] = (W, A, B, lin)
+        dev_w[name] = (q.quantize(dev_f32(W)), dev_bf16(A), dev_bf16(B), lin.alpha)
+    X = wl.activations(0, w.cfg_id, w.M, lins["gate"].K)
+    Xd = dev_bf16(X)
+    G, U, H, Tg, Tu = q.mlp_fwd(Xd, dev_w["gate"], dev_w["up"])
+    G0, U0, H0, _, _ = composed_gate_up(Xd, dev_w["gate"], dev_w["up"])
+    t.cuda.synchronize()
+    for name, a, b in (("G", G, G0), ("U", U, U0), ("H", H, H0)):
+        assert np.array_equal(host_bf16_bits(a), host_bf16_bits(b)), name
+    rows = sample_rows(w.M, 16, seed=11, tile=256)
+    ref = {}
+    for n, (W, A, B, lin) in host_w.items():
+        ref[n], _ = oracle.forward(f64(X[rows]), f64(OracleWeight(W).w_bf16()), f64(A), f64(B),
+                                   lin.alpha, lin.r)
+    assert_close(host_bf16_f64(H)[rows], oracle.silu_mul_forward(ref["gate"], ref["up"]),
+                 "H[sampled tokens]")
