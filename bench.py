@@ -24,6 +24,8 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                    input (mask drawn every step), and its ratio to the step
   gemv             the small-M forward (W0 28672x8192, M = 1, 4, 16): bytes
                    the GEMV kernel must move over its average duration vs HBM
+  mlp_gate_up      the 11008-wide MLP's gate/up projections (4096 tokens):
+                   the fused forward vs the composition, and the backward
   standalone       the load-time kernels (quantize, double quant, dequant), the
                    adapter merge and the dropout kernel in GB/s, with the
                    merge's error against the unquantised base and the NF4 vs
@@ -70,8 +72,8 @@ def source_hash(files=None) -> str:
 
 # bench timer name -> (kernel symbol in profiler output, source file, workload)
 PROFILED = {
-    "dx_gemm": ("k_dx_nf4", "dx_kernels.hip", "c2_linear_4096"),
-    "fwd_gemm": ("k_fwd_nf4", "fwd_kernels.hip", "c2_linear_4096"),
+    "dx_gemm": ("k_dx_nf4<false>", "dx_kernels.hip", "c2_linear_4096"),
+    "fwd_gemm": ("k_fwd_nf4<false, false>", "fwd_kernels.hip", "c2_linear_4096"),
     "gemv": ("k_gemv_dma", "gemv_kernels.hip", "c4_gemv_28672x8192"),
 }
 
@@ -257,6 +259,14 @@ def run_linear(args, q, torch, wl, lib, ev):
                     traffic=traffic_for(dom, units),
                     avg_us=round(kd["avg_us"], 2))
     value = flops / (ms * 1e-3) / 1e12
+    config = dict(workload=cfg.name, M=M, N=lin.N, K=lin.K, r=lin.r, alpha=lin.alpha,
+                  blocksize=64, dq_blocksize=256, input_sets=args.sets,
+                  step="qlora_linear_fwd + qlora_linear_bwd",
+                  flops_per_step=flops)
+    kernels = {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()}
+    if args.no_variants:
+        return dict(value=value, ms=ms, config=config, roofline=roofline, lora_bf16=None,
+                    lora_dropout=None, kernels=kernels)
     # The same step with an unquantised bf16 base (the dequantised weight, so
     # the values are identical): LoRA on a bf16 base versus QLoRA, the
     # comparison the pages quantify as 20-40 % slower per step.
@@ -288,12 +298,8 @@ def run_linear(args, q, torch, wl, lib, ev):
     lora_dropout = dict(p=DROPOUT_P, ms_per_step=round(ms_drop, 4),
                         value=round(flops / (ms_drop * 1e-3) / 1e12, 2), unit="TFLOP/s",
                         step_over_plain_step=round(ms_drop / ms, 4))
-    config = dict(workload=cfg.name, M=M, N=lin.N, K=lin.K, r=lin.r, alpha=lin.alpha,
-                  blocksize=64, dq_blocksize=256, input_sets=args.sets,
-                  step="qlora_linear_fwd + qlora_linear_bwd",
-                  flops_per_step=flops)
     return dict(value=value, ms=ms, config=config, roofline=roofline, lora_bf16=lora_bf16,
-                lora_dropout=lora_dropout, kernels={k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()})
+                lora_dropout=lora_dropout, kernels=kernels)
 
 
 def run_gemv(args, q, torch, wl, lib, ev):
@@ -337,6 +343,67 @@ def run_gemv(args, q, torch, wl, lib, ev):
         if M == 1:
             out["M1"]["traffic"] = traffic_for("gemv", dict(workload=cfg.name))
     return dict(workload=cfg.name, N=lin.N, K=lin.K, r=lin.r, peak_GBps=PEAK_HBM_GBPS, **out)
+
+
+def run_mlp(args, q, torch, wl, lib, ev):
+    """The gate/up projections of the 11008-wide MLP (4096 tokens, 11008 x
+    4096 NF4 weights, r = 64): the fused forward (qlora_mlp_fwd: one kernel
+    writes G, U and H) against the composition (two layer forwards and the
+    elementwise gating), and the backward (qlora_mlp_bwd) from dH."""
+    cfg = wl.workloads()["c3_mlp_11008"]
+    lins = {l.name: l for l in cfg.linears}
+    M, K, I = cfg.M, lins["gate"].K, lins["gate"].N
+    dev_bf16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    lin_args = {}
+    for j, name in enumerate(("gate", "up")):
+        lin = lins[name]
+        W = wl.weight(0, cfg.cfg_id, j, lin)
+        A, B = wl.adapters(0, cfg.cfg_id, j, lin)
+        lin_args[name] = (q.quantize(torch.from_numpy(W).cuda()), dev_bf16(A), dev_bf16(B),
+                          lin.alpha)
+        del W
+    X = dev_bf16(wl.activations(0, cfg.cfg_id, M, K))
+    dH = dev_bf16(wl.grad_output(0, cfg.cfg_id, M, I))
+    ws = q.Workspace("cuda")
+    out = {n: torch.empty(M, I, dtype=torch.bfloat16, device="cuda") for n in ("G", "U", "H")}
+    out["Tg"] = torch.empty(M, lins["gate"].r, dtype=torch.bfloat16, device="cuda")
+    out["Tu"] = torch.empty(M, lins["up"].r, dtype=torch.bfloat16, device="cuda")
+    G2 = torch.empty_like(out["G"])
+    U2 = torch.empty_like(out["U"])
+    H2 = torch.empty_like(out["H"])
+
+    def fused():
+        q.mlp_fwd(X, lin_args["gate"], lin_args["up"], out=out, workspace=ws)
+
+    def composed():
+        q.linear_fwd(X, *lin_args["gate"], out=G2, T_out=out["Tg"], workspace=ws)
+        q.linear_fwd(X, *lin_args["up"], out=U2, T_out=out["Tu"], workspace=ws)
+        q.silu_mul_fwd(G2, U2, out=H2)
+
+    def backward():
+        q.mlp_bwd(dH, X, lin_args["gate"], lin_args["up"], out["G"], out["U"], out["Tg"],
+                  out["Tu"], workspace=ws)
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 3)):
+            fn()
+        torch.cuda.synchronize()
+        n = max(args.steps // 2, 5)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+    ms_f, ms_c, ms_b = timed(fused), timed(composed), timed(backward)
+    r = lins["gate"].r
+    flops = 2 * (2.0 * M * I * K + 2.0 * M * r * (I + K))        # two forwards
+    bflops = 2 * (2.0 * M * I * K + 4.0 * M * r * (I + K))       # dX, dA, dB of both
+    return dict(workload=cfg.name, M=M, K=K, I=I, r=r,
+                fwd_fused_ms=round(ms_f, 4), fwd_composed_ms=round(ms_c, 4),
+                fwd_fused_tflops=round(flops / (ms_f * 1e-3) / 1e12, 1),
+                composed_over_fused=round(ms_c / ms_f, 4),
+                bwd_ms=round(ms_b, 4),
+                bwd_tflops=round(bflops / (ms_b * 1e-3) / 1e12, 1))
 
 
 def run_standalone(args, q, torch, lib, ev):
@@ -538,7 +605,7 @@ COUNTER_SETS = {
     "f": "FETCH_SIZE",
     "w": "WRITE_SIZE",
 }
-SHORT_RUN = "--steps 3 --warmup 1 --no-cpu-baseline --no-standalone"
+SHORT_RUN = "--steps 3 --warmup 1 --no-cpu-baseline --no-standalone --no-mlp --no-variants"
 
 
 def profile_commands(out: str) -> dict:
@@ -690,12 +757,15 @@ def summarize(out: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standalone", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the bf16-base and dropout steps (counter runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--profile-commands", metavar="OUT",
@@ -733,6 +803,11 @@ def main():
         err("[bench] small-M forward ...")
         gemv = run_gemv(args, q, torch, wl, lib, ev)
         err(f"[bench] gemv {gemv}")
+    mlp = None
+    if not args.no_mlp:
+        err("[bench] MLP gate/up ...")
+        mlp = run_mlp(args, q, torch, wl, lib, ev)
+        err(f"[bench] mlp {mlp}")
     standalone = None
     if not args.no_standalone:
         err("[bench] standalone quantize / double quant / dequant ...")
@@ -749,7 +824,7 @@ def main():
                 data="synthetic", config=lin["config"], roofline=lin["roofline"],
                 cpu_baseline=cpu, kernels=lin["kernels"], lora_bf16_base=lin["lora_bf16"],
                 lora_dropout=lin["lora_dropout"],
-                gemv=gemv, standalone=standalone,
+                gemv=gemv, mlp_gate_up=mlp, standalone=standalone,
                 source_hash=source_hash())
     print(json.dumps(line), flush=True)
 

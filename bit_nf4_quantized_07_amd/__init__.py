@@ -63,6 +63,9 @@ SIGNATURES = {
     "qlora_mlp_fwd": (_I, [_P, _I64, _I64, _I64, ctypes.POINTER(LoraLinearC),
                            ctypes.POINTER(LoraLinearC), _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                            _P]),
+    "qlora_mlp_bwd": (_I, [_P, _P, _I64, _I64, _I64, ctypes.POINTER(LoraLinearC),
+                           ctypes.POINTER(LoraLinearC), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                           _P, _I, _P, ctypes.c_size_t, _P]),
     "silu_mul_fwd": (_I, [_P, _P, _I64, _P, _P]),
     "silu_mul_bwd": (_I, [_P, _P, _P, _I64, _P, _P, _P]),
     "nf4_codebook": (_I, [_P]),
@@ -438,6 +441,33 @@ def mlp_fwd(X, gate, up, out=None, workspace=None):
         _ptr(X), M, K, I, ctypes.byref(lg), ctypes.byref(lu), _ptr(G), _ptr(U), _ptr(H), _ptr(Tg),
         _ptr(Tu), _ptr(ws), wsb, _stream(X.device)))
     return G, U, H, Tg, Tu
+
+
+def mlp_bwd(dH, X, gate, up, G, U, Tg, Tu, accumulate_into=None, workspace=None):
+    """Backward of mlp_fwd from dH.  Returns (dX, (dAg, dBg), (dAu, dBu), dG, dU)."""
+    torch = _torch()
+    _need_cuda(dH, X, G, U, Tg, Tu)
+    M, K = X.shape
+    qg, qu = gate[0], up[0]
+    I = qg.N
+    dG, dU = torch.empty_like(G), torch.empty_like(U)
+    flags = 0
+    if accumulate_into is not None:
+        dX = accumulate_into
+        flags |= BWD_ACCUMULATE_DX
+    else:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+    f32 = lambda *s: torch.empty(*s, dtype=torch.float32, device=X.device)
+    rg, ru = gate[1].shape[0], up[1].shape[0]
+    dAg, dBg, dAu, dBu = f32(rg, K), f32(I, rg), f32(ru, K), f32(I, ru)
+    nb = max(workspace_bytes(M, K, I, rg, True), workspace_bytes(M, K, I, ru, True))
+    ws, wsb = (workspace.get(nb) if workspace is not None else _ws(X.device, nb))
+    lg, lu = _lora_linear(*gate), _lora_linear(*up)
+    _check("qlora_mlp_bwd", load_library().qlora_mlp_bwd(
+        _ptr(dH), _ptr(X), M, K, I, ctypes.byref(lg), ctypes.byref(lu), _ptr(G), _ptr(U),
+        _ptr(Tg), _ptr(Tu), _ptr(dG), _ptr(dU), _ptr(dX), _ptr(dAg), _ptr(dBg), _ptr(dAu),
+        _ptr(dBu), flags, _ptr(ws), wsb, _stream(X.device)))
+    return dX, (dAg, dBg), (dAu, dBu), dG, dU
 
 
 def silu_mul_fwd(G, Up, out=None):

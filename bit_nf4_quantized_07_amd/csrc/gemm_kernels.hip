@@ -922,4 +922,17 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
   return hipGetLastError();
 }
 
+hipError_t launch_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, const LoraLinear& gate,
+                          const LoraLinear& up, const uint16_t* G, const uint16_t* U,
+                          const uint16_t* Tg, const uint16_t* Tu, uint16_t* dG, uint16_t* dU,
+                          uint16_t* dX, float* dAg, float* dBg, float* dAu, float* dBu,
+                          bool accumulate_dx, void* ws, hipStream_t st) {
+  const int64_t K = gate.w.K, I = gate.w.N;
+  QLK_TRY(launch_silu_mul_bwd(dH, G, U, M * I, dG, dU, st));
+  QLK_TRY(launch_qlora_bwd(dG, X, M, gate.w, gate.A, gate.B, gate.r, gate.s, Tg, dX, dAg, dBg,
+                           accumulate_dx, ws, plan_bwd(M, K, I, gate.r), st));
+  return launch_qlora_bwd(dU, X, M, up.w, up.A, up.B, up.r, up.s, Tu, dX, dAu, dBu, true, ws,
+                          plan_bwd(M, K, I, up.r), st);
+}
+
 }  // namespace qlk

@@ -92,6 +92,13 @@ struct LoraLinear {
 hipError_t launch_mlp_fwd(const uint16_t* X, int64_t M, const LoraLinear& gate,
                           const LoraLinear& up, uint16_t* G, uint16_t* U, uint16_t* H,
                           uint16_t* Tg, uint16_t* Tu, void* ws, size_t ws_bytes, hipStream_t st);
+// Its backward from dH: dG, dU by the elementwise gating backward, then the
+// two layer backwards, the second accumulating into dX.
+hipError_t launch_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, const LoraLinear& gate,
+                          const LoraLinear& up, const uint16_t* G, const uint16_t* U,
+                          const uint16_t* Tg, const uint16_t* Tu, uint16_t* dG, uint16_t* dU,
+                          uint16_t* dX, float* dAg, float* dBg, float* dAu, float* dBu,
+                          bool accumulate_dx, void* ws, hipStream_t st);
 // dX = dY W_hat (+ s U A) for N a multiple of 256 (else the tile engine runs).
 bool dx_nf4_supported(int64_t N);
 // With a dropout mask (bit per element of dX, row-major), the adapter term

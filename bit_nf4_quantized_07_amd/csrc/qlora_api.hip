@@ -324,6 +324,34 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t I,
                                            workspace_bytes, as_stream(stream)));
 }
 
+int qlora_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, int64_t K, int64_t I,
+                  const qlora_lora_linear* gate, const qlora_lora_linear* up, const uint16_t* G,
+                  const uint16_t* U, const uint16_t* Tg, const uint16_t* Tu, uint16_t* dG,
+                  uint16_t* dU, uint16_t* dX, float* dAg, float* dBg, float* dAu, float* dBu,
+                  int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gate || !up) return QLORA_ERR_NULL;
+  const qlora_lora_linear* lin[2] = {gate, up};
+  qlk::LoraLinear L[2];
+  for (int j = 0; j < 2; ++j) {
+    const qlora_lora_linear& l = *lin[j];
+    int st = check_linear(X, M, K, I, l.packed, l.codes, l.scales, l.mean, l.A, l.B, l.r, l.alpha);
+    if (st) return st;
+    L[j].w = weight(l.packed, l.codes, l.scales, l.mean, I, K);
+    L[j].A = l.A; L[j].B = l.B; L[j].r = l.r; L[j].s = l.alpha / (float)l.r;
+    if (workspace_bytes < qlk::plan_bwd(M, K, I, l.r).bytes || !workspace)
+      return QLORA_ERR_WORKSPACE;
+  }
+  if (!dH || !G || !U || !Tg || !Tu || !dG || !dU || !dX || !dAg || !dBg || !dAu || !dBu)
+    return QLORA_ERR_NULL;
+  if (flags & ~QLORA_BWD_ACCUMULATE_DX) return QLORA_ERR_ARG;
+  const void* ptrs[] = {dH, G, U, Tg, Tu, dG, dU, dX, dAg, dBg, dAu, dBu, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return QLORA_ERR_ALIGN;
+  return launch_status(qlk::launch_mlp_bwd(dH, X, M, L[0], L[1], G, U, Tg, Tu, dG, dU, dX, dAg,
+                                           dBg, dAu, dBu, (flags & QLORA_BWD_ACCUMULATE_DX) != 0,
+                                           workspace, as_stream(stream)));
+}
+
 int silu_mul_fwd(const uint16_t* G, const uint16_t* Up, int64_t n, uint16_t* H, void* stream) {
   if (!G || !Up || !H) return QLORA_ERR_NULL;
   if (n <= 0 || n % 8 != 0 || n / 8 / 256 > 0x7fffffff) return QLORA_ERR_SHAPE;

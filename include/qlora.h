@@ -258,6 +258,24 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t I,
                   uint16_t* G, uint16_t* U, uint16_t* H, uint16_t* Tg, uint16_t* Tu,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of qlora_mlp_fwd from dH = dL/dH, in one call:
+ *   dG = dH * U * sig(G) * (1 + G (1 - sig(G))),  dU = dH * silu(G)   (silu_mul_bwd)
+ *   dX = dG Wg + sg (dG Bg) Ag + dU Wu + su (dU Bu) Au          bf16 [M, K]
+ *   dAg, dBg, dAu, dBu as qlora_linear_bwd gives them for each projection.
+ * G, U, Tg, Tu are the forward's; dG and dU (bf16 [M, I], caller-owned) are
+ * written on the way, since they feed three products each (the dX GEMM, U =
+ * dY B and dB).  The gate's dX is written (or, with QLORA_BWD_ACCUMULATE_DX,
+ * added) and the up projection's is added to it; the results are those of
+ * silu_mul_bwd followed by the two qlora_linear_bwd calls.  Shape rules as
+ * qlora_mlp_fwd; workspace_bytes >= qlora_workspace_bytes(M, K, I, r, 1) for
+ * both r. */
+int qlora_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, int64_t K, int64_t I,
+                  const qlora_lora_linear* gate, const qlora_lora_linear* up,
+                  const uint16_t* G, const uint16_t* U, const uint16_t* Tg, const uint16_t* Tu,
+                  uint16_t* dG, uint16_t* dU, uint16_t* dX, float* dAg, float* dBg,
+                  float* dAu, float* dBu, int flags, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* ---- serving: fold the adapter into the base ---------------------------- */
 
 /* W_merged = RNE_bf16( w_hat_bf16 + s (B A) ),  s = fp32(alpha / r).

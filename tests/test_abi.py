@@ -266,3 +266,22 @@ def test_mlp_fwd_validation():
     assert call(Tu=None) == q.ERR_NULL
     assert call(U=MIS) == q.ERR_ALIGN
     assert call(M=4, ws=None, wsb=0) == q.ERR_WORKSPACE      # small M needs workspace
+
+
+def test_mlp_bwd_validation():
+    f = lib.qlora_mlp_bwd
+    good = q.LoraLinearC(D, D, D, D, D, D, 16, 32.0)
+
+    def call(gate=good, up=good, K=256, I=512, dH=D, dX=D, dAu=D, flags=0, ws=D, wsb=1 << 30):
+        gp = None if gate is None else ctypes.byref(gate)
+        upp = None if up is None else ctypes.byref(up)
+        return f(dH, D, 64, K, I, gp, upp, D, D, D, D, D, D, dX, D, D, dAu, D, flags, ws, wsb, None)
+    assert call(gate=None) == q.ERR_NULL
+    assert call(up=q.LoraLinearC(D, D, D, D, D, D, 264, 32.0)) == q.ERR_SHAPE
+    assert call(K=96) == q.ERR_SHAPE
+    assert call(dH=None) == q.ERR_NULL
+    assert call(dAu=None) == q.ERR_NULL
+    assert call(flags=2) == q.ERR_ARG
+    assert call(dX=MIS) == q.ERR_ALIGN
+    assert call(ws=None) == q.ERR_WORKSPACE
+    assert call(wsb=16) == q.ERR_WORKSPACE

@@ -218,3 +218,35 @@ def test_fused_gate_up_config3_full_shape():
                                    lin.alpha, lin.r)
     assert_close(host_bf16_f64(H)[rows], oracle.silu_mul_forward(ref["gate"], ref["up"]),
                  "H[sampled tokens]")
+
+
+@pytest.mark.parametrize("M,K,I,r", [(300, 512, 704, 16), (40, 256, 200, 16), (8, 512, 256, 16)])
+def test_mlp_backward_equals_the_composition(M, K, I, r):
+    """qlora_mlp_bwd gives the bits of silu_mul_bwd followed by the two layer
+    backwards (the up projection accumulating into dX); then against the
+    oracle."""
+    t = pytest.importorskip("torch")
+    log(f"[mlp bwd] M={M} K={K} I={I} r={r}")
+    _, _, host_w, dev_w = make_block(62, M, K, I, r, 2.0 * r, with_down=False)
+    X = wl.activations(62, 102, M, K)
+    dHh = wl.grad_output(62, 102, M, I)
+    Xd, dH = dev_bf16(X), dev_bf16(dHh)
+    G, U, H, Tg, Tu = q.mlp_fwd(Xd, dev_w["gate"], dev_w["up"])
+    dX, (dAg, dBg), (dAu, dBu), dG, dU = q.mlp_bwd(dH, Xd, dev_w["gate"], dev_w["up"], G, U, Tg, Tu)
+    dG0, dU0 = q.silu_mul_bwd(dH, G, U)
+    dX0, dAg0, dBg0 = q.linear_bwd(dG0, Xd, *dev_w["gate"], T=Tg)
+    _, dAu0, dBu0 = q.linear_bwd(dU0, Xd, *dev_w["up"], T=Tu, accumulate_into=dX0)
+    t.cuda.synchronize()
+    for name, a, b in (("dG", dG, dG0), ("dU", dU, dU0), ("dX", dX, dX0)):
+        assert np.array_equal(host_bf16_bits(a), host_bf16_bits(b)), name
+    for name, a, b in (("dAg", dAg, dAg0), ("dBg", dBg, dBg0), ("dAu", dAu, dAu0), ("dBu", dBu, dBu0)):
+        assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32)), name
+    ref_w = {n: (f64(OracleWeight(W).w_bf16()), f64(A), f64(B)) for n, (W, A, B) in host_w.items()}
+    Gr, _ = oracle.forward(f64(X), *ref_w["gate"], 2.0 * r, r)
+    Ur, _ = oracle.forward(f64(X), *ref_w["up"], 2.0 * r, r)
+    dGr, dUr = oracle.silu_mul_backward(f64(dHh), Gr, Ur)
+    dXg, dAgr, dBgr = oracle.backward(dGr, f64(X), *ref_w["gate"], 2.0 * r, r)
+    dXu, dAur, dBur = oracle.backward(dUr, f64(X), *ref_w["up"], 2.0 * r, r)
+    assert_close(host_bf16_f64(dX), dXg + dXu, "dX")
+    for name, got, ref in (("dAg", dAg, dAgr), ("dBg", dBg, dBgr), ("dAu", dAu, dAur), ("dBu", dBu, dBur)):
+        assert_close(host(got).astype(np.float64), ref, name)
