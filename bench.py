@@ -72,7 +72,7 @@ def source_hash(files=None) -> str:
 
 # bench timer name -> (kernel symbol in profiler output, source file, workload)
 PROFILED = {
-    "dx_gemm": ("k_dx_nf4<false>", "dx_kernels.hip", "c2_linear_4096"),
+    "dx_gemm": ("k_dx_nf4<true>", "dx_kernels.hip", "c2_linear_4096"),
     "fwd_gemm": ("k_fwd_nf4<false, false>", "fwd_kernels.hip", "c2_linear_4096"),
     "gemv": ("k_gemv_dma", "gemv_kernels.hip", "c4_gemv_28672x8192"),
 }
@@ -126,7 +126,10 @@ def algorithmic_bytes(kernel: str, M=None) -> int:
     M, N, K, r = 2048, 4096, 4096, 16
     if kernel == "fwd_gemm":    # X, weight, T, B -> Y
         return 2 * M * K + weight_bytes(N, K) + 2 * M * r + 2 * N * r + 2 * M * N
-    return 2 * M * N + weight_bytes(N, K) + 2 * M * r + 2 * r * K + 2 * M * K   # dY, weight, U, A -> dX
+    if kernel == "dequant":     # the backward's one-off dequantisation: NF4 + DQ -> bf16
+        return weight_bytes(N, K) + 2 * N * K
+    # dY, the once-dequantised bf16 weight, U, A -> dX
+    return 2 * M * N + 2 * N * K + 2 * M * r + 2 * r * K + 2 * M * K
 
 
 def gemv_bytes(M, N, K, r):
@@ -228,7 +231,8 @@ def run_linear(args, q, torch, wl, lib, ev):
     # library on the launch stream around the two GEMMs.  An event record
     # between two kernels breaks their back-to-back dispatch, so it is kept
     # out of the pass that gives the step time.
-    evs = {k: (ev.create(K), ev.create(K)) for k in (q.KERNEL_FWD_GEMM, q.KERNEL_DX_GEMM)}
+    evs = {k: (ev.create(K), ev.create(K))
+           for k in (q.KERNEL_FWD_GEMM, q.KERNEL_DX_GEMM, q.KERNEL_DX_DEQUANT)}
     torch.cuda.synchronize()
     for i in range(K):
         for k, (a, b) in evs.items():
@@ -239,18 +243,23 @@ def run_linear(args, q, torch, wl, lib, ev):
         lib.qlora_set_kernel_timer(k, None, None)
     flops = linear_flops(M, lin.N, lin.K, lin.r)
     kern = {}
-    names = {q.KERNEL_FWD_GEMM: "fwd_gemm", q.KERNEL_DX_GEMM: "dx_gemm"}
+    names = {q.KERNEL_FWD_GEMM: "fwd_gemm", q.KERNEL_DX_GEMM: "dx_gemm",
+             q.KERNEL_DX_DEQUANT: "dx_dequant"}
     kflops = {q.KERNEL_FWD_GEMM: 2.0 * M * lin.N * (lin.K + lin.r),
               q.KERNEL_DX_GEMM: 2.0 * M * lin.K * (lin.N + lin.r)}
     for k, (a, b) in evs.items():
         d = [ev.elapsed_ms(a[i], b[i]) for i in range(K)]
         avg = float(np.mean(d))
-        kern[names[k]] = dict(avg_us=avg * 1e3, median_us=float(np.median(d)) * 1e3,
-                              min_us=float(np.min(d)) * 1e3,
-                              flops_per_launch=kflops[k],
-                              tflops=kflops[k] / (avg * 1e-3) / 1e12)
+        e = dict(avg_us=avg * 1e3, median_us=float(np.median(d)) * 1e3,
+                 min_us=float(np.min(d)) * 1e3)
+        if k in kflops:
+            e.update(flops_per_launch=kflops[k], tflops=kflops[k] / (avg * 1e-3) / 1e12)
+        else:   # the backward's one-off dequantisation: bytes moved
+            nbytes = algorithmic_bytes("dequant")
+            e.update(bytes_per_launch=nbytes, GBps=nbytes / (avg * 1e-3) / 1e9)
+        kern[names[k]] = e
         ev.destroy(a + b)
-    dom = max(kern, key=lambda n: kern[n]["avg_us"])
+    dom = max((names[k] for k in kflops), key=lambda n: kern[n]["avg_us"])
     kd = kern[dom]
     units = dict(workload=cfg.name)
     roofline = dict(bound="mfma", kernel=dom, achieved=round(kd["tflops"], 2),

@@ -75,7 +75,7 @@ SIGNATURES = {
     "qlora_set_kernel_timer": (_I, [_I, _P, _P]),
 }
 
-KERNEL_FWD_GEMM, KERNEL_DX_GEMM, KERNEL_GEMV = 1, 2, 3
+KERNEL_FWD_GEMM, KERNEL_DX_GEMM, KERNEL_GEMV, KERNEL_DX_DEQUANT = 1, 2, 3, 4
 
 _lib = None
 

@@ -655,6 +655,12 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r) {
   p.m_splits_b = actual_splits(M, choose_splits((int64_t)ceil_div(N, 128) * rt, M));
   p.off_part_b = p.off_part + align256((size_t)p.m_splits_a * r * K * 4);
   p.bytes = p.off_part_b + align256((size_t)p.m_splits_b * N * r * 4);
+  // Large M: the dequantised weight (bf16, 2 N K bytes, addressed with 32-bit
+  // buffer offsets) is reused by every token tile of the dX kernel.
+  p.dequant_dx = M >= kDequantDxMinM && dx_nf4_supported(N) && N * K * 2 < ((int64_t)1 << 31) &&
+                 !QLK_DX_TILE_ENGINE;
+  p.off_wbf16 = p.bytes;
+  if (p.dequant_dx) p.bytes += align256((size_t)N * K * 2);
   return p;
 }
 
@@ -867,10 +873,22 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     g.P = (int)M; g.Q = (int)K;
     g.c1_len = (int)N; g.c1_split = (int)N; g.c2_len = r;
     g.out = dX; g.ldo = K; g.accumulate = accumulate_dx ? 1 : 0;
+    NF4Weight wx = w;
+    if (!w.bf16 && plan.dequant_dx) {
+      // Dequantise once (the standalone kernel: the same bits as the in-tile
+      // decode) and run the dX kernel on the bf16 copy, so that the M / 256
+      // token tiles do not each decode the whole weight again.
+      uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
+      timer_begin(TK_DX_DEQUANT, st);
+      QLK_TRY(launch_nf4_dequant(w.packed, w.codes, w.scales, w.mean, N * K, nf4_codebook4(), wb,
+                                 st));
+      timer_end(TK_DX_DEQUANT, st);
+      wx.bf16 = wb;
+    }
     timer_begin(TK_DX_GEMM, st);
     hipError_t e;
     if (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N)) {
-      e = launch_dx_nf4(dY, M, w, U, A, r, s, dX, accumulate_dx, st, mask, keep_scale);
+      e = launch_dx_nf4(dY, M, wx, U, A, r, s, dX, accumulate_dx, st, mask, keep_scale);
     } else if (mask) {
       // Tile engine with a dropout mask: the masked adapter term is written
       // (or added) first, then dY W_hat is accumulated on top of it.

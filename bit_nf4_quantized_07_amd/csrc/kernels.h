@@ -55,7 +55,13 @@ struct FwdPlan {
 struct BwdPlan {
   int u_splits, t_splits, m_splits_a, m_splits_b;
   size_t off_U, off_T, off_part, off_part_b, bytes;   // dA partials at off_part, dB at off_part_b
+  // dX on a bf16 copy of the weight dequantised once per call (at off_wbf16)
+  // instead of decoding every tile in each of the M / 256 token tiles.
+  bool dequant_dx;
+  size_t off_wbf16;
 };
+// Token count from which the backward dequantises the NF4 weight once.
+constexpr int64_t kDequantDxMinM = 1024;
 FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r);
 BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r);
 
@@ -127,7 +133,8 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
                             const uint32_t* mask = nullptr, float keep_scale = 1.0f);
 
 // Measurement hook: events recorded around individual launches.
-enum TimedKernel { TK_NONE = 0, TK_FWD_GEMM = 1, TK_DX_GEMM = 2, TK_GEMV = 3, TK_COUNT = 4 };
+enum TimedKernel { TK_NONE = 0, TK_FWD_GEMM = 1, TK_DX_GEMM = 2, TK_GEMV = 3, TK_DX_DEQUANT = 4,
+                   TK_COUNT = 5 };
 void set_kernel_timer(int kernel, hipEvent_t start, hipEvent_t stop);
 void timer_begin(int kernel, hipStream_t st);
 void timer_end(int kernel, hipStream_t st);

@@ -151,7 +151,12 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
  * T is the X A^T saved by the forward (bf16 [M, r]); NULL = recompute it.
  * flags: 0 or QLORA_BWD_ACCUMULATE_DX.  The reductions over M run in a fixed
  * order, so repeated calls give identical bits.  Same shape rules and
- * tolerances as the forward; workspace >= qlora_workspace_bytes(..., 1). */
+ * tolerances as the forward; workspace >= qlora_workspace_bytes(..., 1).
+ * For M >= 1024 (and N % 256 == 0, 2 N K < 2 GiB) the weight is dequantised
+ * once per call into the workspace (2 N K bytes of it) and dX runs on that
+ * bf16 copy (the pages' dequantise-then-matmul, llm-compass 直觉与动机): the
+ * same bits as decoding in every tile, without decoding it again for every
+ * 256 tokens. */
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
                      const uint8_t* packed, const uint8_t* codes, const float* scales,
                      const float* mean, const uint16_t* A, const uint16_t* B,
@@ -313,7 +318,8 @@ int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int6
 #define QLORA_KERNEL_FWD_GEMM   1  /* fused dequant GEMM  Y = X W_hat^T + s T B^T     */
 #define QLORA_KERNEL_DX_GEMM    2  /* fused dequant GEMM  dX = dY W_hat + s U A       */
 #define QLORA_KERNEL_GEMV       3  /* small-M dequant GEMV forward                    */
-#define QLORA_KERNEL_COUNT      4
+#define QLORA_KERNEL_DX_DEQUANT 4  /* the backward's one-off dequantisation (M >= 1024) */
+#define QLORA_KERNEL_COUNT      5
 
 /* While set, each launch of `kernel` is bracketed by hipEventRecord(ev_start)
  * and hipEventRecord(ev_stop) on the stream of the call that launches it

@@ -134,12 +134,16 @@ def test_workspace_sizes():
     assert lib.qlora_workspace_bytes(16, 256, 256, 5, 1) == 0
     # the backward needs room for U and T at least
     assert lib.qlora_workspace_bytes(2048, 4096, 4096, 16, 1) >= 2 * 2048 * 16 * 2
+    # from 1024 tokens on it also holds the once-dequantised bf16 weight
+    big, small = lib.qlora_workspace_bytes(1024, 4096, 4096, 16, 1), lib.qlora_workspace_bytes(1023, 4096, 4096, 16, 1)
+    assert big - small >= 2 * 4096 * 4096
+    assert small < 2 * 4096 * 4096
 
 
 def test_kernel_timer_validation():
     assert lib.qlora_set_kernel_timer(0, None, None) == q.ERR_ARG
-    assert lib.qlora_set_kernel_timer(4, None, None) == q.ERR_ARG
-    for k in (1, 2, 3):
+    assert lib.qlora_set_kernel_timer(5, None, None) == q.ERR_ARG
+    for k in (1, 2, 3, 4):
         assert lib.qlora_set_kernel_timer(k, None, None) == q.OK
 
 

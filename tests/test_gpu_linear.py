@@ -157,6 +157,33 @@ def test_gemv_matches_tiled_path(M):
     assert_close(gb["Y"][:M], ref["Y"], f"tiled rows M{M}")
 
 
+@pytest.mark.parametrize("N,K", [(512, 768), (1024, 320)])
+def test_dequant_once_dx_equals_in_tile_decode(N, K):
+    """From 1024 tokens the backward dequantises the weight once and runs the
+    dX kernel on the bf16 copy; below, every tile decodes the NF4 bytes.  dX
+    rows depend on their own dY row only, so the first 512 rows of a
+    1024-token backward must equal a 512-token backward of those rows bit for
+    bit (dA, dB sum over tokens and differ)."""
+    t = pytest.importorskip("torch")
+    case = wl.linear_case(12, 1024, N, K, 16, 32.0)
+    qw = q.quantize(dev_f32(case["W"]))
+    X, A, B, dY = (dev_bf16(case[k]) for k in ("X", "A", "B", "dY"))
+    for mask_p in (None, 0.05):
+        if mask_p is None:
+            dX_big, _, _ = q.linear_bwd(dY, X, qw, A, B, 32.0)
+            dX_small, _, _ = q.linear_bwd(dY[:512].contiguous(), X[:512].contiguous(), qw, A, B, 32.0)
+        else:
+            Xd, mask = q.dropout(X, mask_p, 77)
+            dX_big, _, _ = q.linear_bwd_dropout(dY, Xd, mask, mask_p, qw, A, B, 32.0)
+            dX_small, _, _ = q.linear_bwd_dropout(dY[:512].contiguous(), Xd[:512].contiguous(),
+                                                  mask[:512 * K // 32].contiguous(), mask_p, qw, A,
+                                                  B, 32.0)
+        t.cuda.synchronize()
+        a = dX_big[:512].contiguous().view(t.int16).cpu().numpy()
+        b = dX_small.view(t.int16).cpu().numpy()
+        assert np.array_equal(a, b), f"dropout={mask_p}"
+
+
 # ---------------------------- full-size configs ------------------------------
 
 def _full_linear(cfg, idx, M=None, rows=48):
