@@ -75,6 +75,7 @@ PROFILED = {
     "dx_gemm": ("k_dx_nf4<true>", "dx_kernels.hip", "c2_linear_4096"),
     "fwd_gemm": ("k_fwd_nf4<false, false>", "fwd_kernels.hip", "c2_linear_4096"),
     "gemv": ("k_gemv_dma", "gemv_kernels.hip", "c4_gemv_28672x8192"),
+    "dx_dequant": ("k_nf4_dequant", "quant_kernels.hip", "c2_linear_4096"),
 }
 
 
@@ -126,7 +127,7 @@ def algorithmic_bytes(kernel: str, M=None) -> int:
     M, N, K, r = 2048, 4096, 4096, 16
     if kernel == "fwd_gemm":    # X, weight, T, B -> Y
         return 2 * M * K + weight_bytes(N, K) + 2 * M * r + 2 * N * r + 2 * M * N
-    if kernel == "dequant":     # the backward's one-off dequantisation: NF4 + DQ -> bf16
+    if kernel in ("dequant", "dx_dequant"):   # the backward's one-off dequantisation: NF4 + DQ -> bf16
         return weight_bytes(N, K) + 2 * N * K
     # dY, the once-dequantised bf16 weight, U, A -> dX
     return 2 * M * N + 2 * N * K + 2 * M * r + 2 * r * K + 2 * M * K
@@ -672,8 +673,10 @@ def summarize(out: str):
     rows = _csv(os.path.join(out, "kt", "kt_kernel_stats.csv"))
     md = ["# Kernel statistics of the default bench run", "",
           "The default `bench.py` run: the 2048 x 4096 x 4096 linear layer (r = 16) forward and "
-          "backward (warm-up, timed pass, event pass), the 28672 x 8192 small-M forward at "
-          "M = 1, 4, 16, and the standalone quantize / double-quant / dequant calls.", "",
+          "backward (warm-up, timed pass, event pass; then the same step on a bf16 base and "
+          "with LoRA dropout), the 28672 x 8192 small-M forward at M = 1, 4, 16, the "
+          "11008-wide MLP gate/up forward (fused and composed) and backward, and the "
+          "standalone quantize / double-quant / dequant / merge / dropout calls.", "",
           head, "```", cmds["kt"], "```", "",
           "| calls | total us | avg us | min us | max us | % | kernel |",
           "|---:|---:|---:|---:|---:|---:|---|"]
@@ -683,6 +686,24 @@ def summarize(out: str):
         md.append("| %s | %.1f | %.2f | %.2f | %.2f | %.2f | `%s` |" % (
             r["Calls"], float(r["TotalDurationNs"]) / 1e3, float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"]), name))
+    # The profiled kernels run on several shapes in the default run (the
+    # forward kernel also on the MLP's 4096 x 11008 x 4096 projections): their
+    # dispatches by launch shape, from the per-dispatch trace.
+    trace = _csv(os.path.join(out, "kt", "kt_kernel_trace.csv"))
+    md += ["", "Profiled kernels by launch shape (grid in work-items; from the per-dispatch trace "
+           "`kt_kernel_trace.csv` of the same run):", "",
+           "| kernel | grid | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
+    for key, (sym, src, wk) in PROFILED.items():
+        by = {}
+        for r in trace:
+            if sym in r["Kernel_Name"]:
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                by.setdefault(int(r["Grid_Size_X"]), []).append(us)
+        for grid, ds in sorted(by.items(), key=lambda kv: -len(kv[1])):
+            md.append("| `%s` (%s) | %d | %d | %.2f | %.2f | %.2f |" % (
+                sym, key, grid, len(ds), float(np.mean(ds)), float(np.min(ds)), float(np.max(ds))))
+    md += ["", "On the 2048 x 4096 x 4096 layer the forward kernel runs 256 workgroups of 256 "
+           "work-items (grid 65536) and the dX kernel 256 of 512 (grid 131072)."]
     with open(os.path.join(prof, "kernel_stats_default_bench.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
 
