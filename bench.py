@@ -75,7 +75,7 @@ PROFILED = {
     "dx_gemm": ("k_dx_nf4<true>", "dx_kernels.hip", "c2_linear_4096"),
     "fwd_gemm": ("k_fwd_nf4<false, false>", "fwd_kernels.hip", "c2_linear_4096"),
     "gemv": ("k_gemv_dma", "gemv_kernels.hip", "c4_gemv_28672x8192"),
-    "dx_dequant": ("k_nf4_dequant", "quant_kernels.hip", "c2_linear_4096"),
+    "dx_prep": ("k_rank16_and_dequant", "adapter_kernels.hip+dequant_block.h", "c2_linear_4096"),
 }
 
 
@@ -127,8 +127,10 @@ def algorithmic_bytes(kernel: str, M=None) -> int:
     M, N, K, r = 2048, 4096, 4096, 16
     if kernel == "fwd_gemm":    # X, weight, T, B -> Y
         return 2 * M * K + weight_bytes(N, K) + 2 * M * r + 2 * N * r + 2 * M * N
-    if kernel in ("dequant", "dx_dequant"):   # the backward's one-off dequantisation: NF4 + DQ -> bf16
+    if kernel == "dequant":     # the one-off dequantisation: NF4 + DQ -> bf16
         return weight_bytes(N, K) + 2 * N * K
+    if kernel == "dx_prep":     # U = dY B next to the dequantisation: dY, B -> U; NF4 + DQ -> bf16
+        return 2 * M * N + 2 * N * r + 2 * M * r + weight_bytes(N, K) + 2 * N * K
     # dY, the once-dequantised bf16 weight, U, A -> dX
     return 2 * M * N + 2 * N * K + 2 * M * r + 2 * r * K + 2 * M * K
 
@@ -152,7 +154,7 @@ def traffic_for(kernel: str, launch_units: dict):
     k = t.get("kernels", {}).get(kernel)
     if not k or k.get("workload") != launch_units.get("workload"):
         return None
-    if k.get("source_hash") != source_hash([PROFILED[kernel][1]]):
+    if k.get("source_hash") != source_hash(PROFILED[kernel][1].split("+")):
         return None
     return k.get("hbm_bytes_per_launch")
 
@@ -245,7 +247,7 @@ def run_linear(args, q, torch, wl, lib, ev):
     flops = linear_flops(M, lin.N, lin.K, lin.r)
     kern = {}
     names = {q.KERNEL_FWD_GEMM: "fwd_gemm", q.KERNEL_DX_GEMM: "dx_gemm",
-             q.KERNEL_DX_DEQUANT: "dx_dequant"}
+             q.KERNEL_DX_DEQUANT: "dx_prep"}
     kflops = {q.KERNEL_FWD_GEMM: 2.0 * M * lin.N * (lin.K + lin.r),
               q.KERNEL_DX_GEMM: 2.0 * M * lin.K * (lin.N + lin.r)}
     for k, (a, b) in evs.items():
@@ -255,8 +257,8 @@ def run_linear(args, q, torch, wl, lib, ev):
                  min_us=float(np.min(d)) * 1e3)
         if k in kflops:
             e.update(flops_per_launch=kflops[k], tflops=kflops[k] / (avg * 1e-3) / 1e12)
-        else:   # the backward's one-off dequantisation: bytes moved
-            nbytes = algorithmic_bytes("dequant")
+        else:   # U = dY B and the backward's one-off dequantisation, one launch: bytes moved
+            nbytes = algorithmic_bytes("dx_prep")
             e.update(bytes_per_launch=nbytes, GBps=nbytes / (avg * 1e-3) / 1e9)
         kern[names[k]] = e
         ev.destroy(a + b)
@@ -743,7 +745,7 @@ def summarize(out: str):
                                                fetch_kib=round(fk, 1), write_kib=round(wk_, 1),
                                                hbm_bytes_per_launch=int(hbm),
                                                algorithmic_bytes_per_launch=int(alg),
-                                               source_hash=source_hash([src]))
+                                               source_hash=source_hash(src.split("+")))
     with open(os.path.join(prof, "traffic.json"), "w") as fh:
         json.dump(traffic, fh, indent=1)
     with open(os.path.join(prof, "traffic_gemms_gemv.md"), "w") as fh:

@@ -13,6 +13,9 @@
 // workgroup keep enough loads in flight to stream S), and the NW partial sums
 // are added through LDS in a fixed order, so the bf16 result is written by
 // the same kernel and is bit-reproducible.
+#include <type_traits>
+
+#include "dequant_block.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -21,14 +24,15 @@ namespace qlk {
 constexpr int kRankRows = 16;
 constexpr int kRankMaxTiles = 16;   // r <= 256
 
+// One workgroup's share; `blk` is its index in the rank-r grid.
 template <bool WT, int RT, int NW>
-__global__ void __launch_bounds__(NW * 64)
-k_rank16(const uint16_t* __restrict__ S, int M, int64_t C, const uint16_t* __restrict__ W, int r,
-         int rows, uint16_t* __restrict__ out) {
+__device__ __forceinline__ void rank16_block(const uint16_t* __restrict__ S, int M, int64_t C,
+                                             const uint16_t* __restrict__ W, int r, int rows,
+                                             uint16_t* __restrict__ out, int blk) {
   __shared__ float red[NW - 1][kRankRows][RT * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, grp = lane >> 4;
-  const int m0 = blockIdx.x * rows;
+  const int m0 = blk * rows;
   const int m = m0 + row;
   const bool mvalid = row < rows && m < M;
   const int64_t nsteps = (C + 31) / 32;
@@ -89,6 +93,33 @@ k_rank16(const uint16_t* __restrict__ S, int M, int64_t C, const uint16_t* __res
   }
 }
 
+template <bool WT, int RT, int NW>
+__global__ void __launch_bounds__(NW * 64)
+k_rank16(const uint16_t* __restrict__ S, int M, int64_t C, const uint16_t* __restrict__ W, int r,
+         int rows, uint16_t* __restrict__ out) {
+  rank16_block<WT, RT, NW>(S, M, C, W, r, rows, out, blockIdx.x);
+}
+
+// The backward's U = dY B and its one-off dequantisation of the weight are
+// independent and each too short to fill the device for long: one launch
+// runs both, the first `rank_blocks` workgroups computing U and the rest
+// dequantising (each workgroup does one or the other, so the barriers inside
+// each body see all of its threads).
+template <int RT, int NW>
+__global__ void __launch_bounds__(NW * 64)
+k_rank16_and_dequant(const uint16_t* __restrict__ S, int M, int64_t C,
+                     const uint16_t* __restrict__ W, int r, int rows, uint16_t* __restrict__ out,
+                     int rank_blocks, const uint8_t* __restrict__ packed,
+                     const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+                     const float* __restrict__ mean, int64_t nwords, Codebook4 cb,
+                     uint16_t* __restrict__ wout) {
+  if ((int)blockIdx.x < rank_blocks)
+    rank16_block<true, RT, NW>(S, M, C, W, r, rows, out, blockIdx.x);
+  else
+    nf4_dequant_block(packed, codes, scales, mean, nwords, cb, wout,
+                      (int64_t)blockIdx.x - rank_blocks);
+}
+
 template <bool WT>
 static hipError_t rank16_dispatch(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, int r,
                                   uint16_t* out, hipStream_t st) {
@@ -102,6 +133,34 @@ static hipError_t rank16_dispatch(const uint16_t* S, int64_t M, int64_t C, const
   else if (tiles <= 4) hipLaunchKernelGGL((k_rank16<WT, 4, 8>), grid, dim3(512), 0, st, S, (int)M, C, W, r, rows, out);
   else if (tiles <= 8) hipLaunchKernelGGL((k_rank16<WT, 8, 4>), grid, dim3(256), 0, st, S, (int)M, C, W, r, rows, out);
   else hipLaunchKernelGGL((k_rank16<WT, kRankMaxTiles, 4>), grid, dim3(256), 0, st, S, (int)M, C, W, r, rows, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W,
+                                     int r, uint16_t* out, const NF4Weight& w, uint16_t* wout,
+                                     hipStream_t st) {
+  const int rows = (M + kRankRows - 1) / kRankRows < 256 ? 8 : kRankRows;
+  const int rank_blocks = (int)((M + rows - 1) / rows);
+  const int64_t nwords = w.N * w.K / 8;
+  const Codebook4 cb = nf4_codebook4();
+  const int tiles = (r + 15) / 16;
+  auto go = [&](auto rt, auto nw) {
+    constexpr int RT = decltype(rt)::value, NW = decltype(nw)::value;
+    const int64_t dq_blocks = (nwords + NW * 256 - 1) / (NW * 256);
+    hipLaunchKernelGGL((k_rank16_and_dequant<RT, NW>), dim3((unsigned)(rank_blocks + dq_blocks)),
+                       dim3(NW * 64), 0, st, S, (int)M, C, W, r, rows, out, rank_blocks, w.packed,
+                       w.codes, w.scales, w.mean, nwords, cb, wout);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+  if (tiles <= 1) go(I1(), I16());
+  else if (tiles <= 2) go(I2(), I16());
+  else if (tiles <= 4) go(I4(), I8());
+  else if (tiles <= 8) go(I8(), I4());
+  else go(std::integral_constant<int, kRankMaxTiles>(), I4());
   return hipGetLastError();
 }
 

@@ -860,8 +860,22 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     QLK_TRY(compute_T(X, M, K, A, r, Tw, st));
     T = Tw;
   }
-  // U = dY B (B [N, r] read transposed), in one pass over dY.
-  QLK_TRY(launch_rank16(dY, M, N, B, true, r, U, st));
+  // U = dY B (B [N, r] read transposed), in one pass over dY; for large M
+  // together with the one-off dequantisation of the weight for dX (one
+  // launch, the two run side by side): the dX kernel then runs on the bf16
+  // copy (the standalone kernel's arithmetic: the same bits as the in-tile
+  // decode), so that the M / 256 token tiles do not each decode the whole
+  // weight again.
+  NF4Weight wx = w;
+  if (dX && !w.bf16 && plan.dequant_dx) {
+    uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
+    timer_begin(TK_DX_DEQUANT, st);
+    QLK_TRY(launch_rank16_and_dequant(dY, M, N, B, r, U, w, wb, st));
+    timer_end(TK_DX_DEQUANT, st);
+    wx.bf16 = wb;
+  } else {
+    QLK_TRY(launch_rank16(dY, M, N, B, true, r, U, st));
+  }
   // dX = dY W_hat + s U A.
   if (dX) {
     GemmArgs g{};
@@ -873,18 +887,6 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     g.P = (int)M; g.Q = (int)K;
     g.c1_len = (int)N; g.c1_split = (int)N; g.c2_len = r;
     g.out = dX; g.ldo = K; g.accumulate = accumulate_dx ? 1 : 0;
-    NF4Weight wx = w;
-    if (!w.bf16 && plan.dequant_dx) {
-      // Dequantise once (the standalone kernel: the same bits as the in-tile
-      // decode) and run the dX kernel on the bf16 copy, so that the M / 256
-      // token tiles do not each decode the whole weight again.
-      uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
-      timer_begin(TK_DX_DEQUANT, st);
-      QLK_TRY(launch_nf4_dequant(w.packed, w.codes, w.scales, w.mean, N * K, nf4_codebook4(), wb,
-                                 st));
-      timer_end(TK_DX_DEQUANT, st);
-      wx.bf16 = wb;
-    }
     timer_begin(TK_DX_GEMM, st);
     hipError_t e;
     if (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N)) {

@@ -117,6 +117,12 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
 hipError_t launch_dx_adapter_masked(const uint16_t* U, const uint16_t* A, int64_t M, int64_t K,
                                     int r, float s, const uint32_t* mask, float keep_scale,
                                     uint16_t* dX, bool accumulate, hipStream_t st);
+// U = S B (B [C, r] read transposed, as launch_rank16 with transposed = true)
+// and the dequantisation of w into wout (bf16 [N, K], as launch_nf4_dequant),
+// in one launch.
+hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W,
+                                     int r, uint16_t* out, const NF4Weight& w, uint16_t* wout,
+                                     hipStream_t st);
 // out[M, r] (bf16) = S[M, C] W^T with W = [r, C] or, transposed, [C, r].
 hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, bool transposed,
                          int r, uint16_t* out, hipStream_t st);

@@ -318,7 +318,8 @@ int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int6
 #define QLORA_KERNEL_FWD_GEMM   1  /* fused dequant GEMM  Y = X W_hat^T + s T B^T     */
 #define QLORA_KERNEL_DX_GEMM    2  /* fused dequant GEMM  dX = dY W_hat + s U A       */
 #define QLORA_KERNEL_GEMV       3  /* small-M dequant GEMV forward                    */
-#define QLORA_KERNEL_DX_DEQUANT 4  /* the backward's one-off dequantisation (M >= 1024) */
+#define QLORA_KERNEL_DX_DEQUANT 4  /* the backward's one-off dequantisation (M >= 1024),
+                                       launched together with U = dY B                 */
 #define QLORA_KERNEL_COUNT      5
 
 /* While set, each launch of `kernel` is bracketed by hipEventRecord(ev_start)
