@@ -464,17 +464,18 @@ struct Tile {
   }
 };
 
+// One workgroup of the tile engine: tile index `bx` (walked by tile_coords),
+// contraction split `z`; smem holds two stages of this tile shape, q4 / q8
+// the decode tables.
 template <int BM, int BN, int BK, int WGM, int WGN, class LA1, class LB1, class LA2, class LB2, int EPI>
-__global__ void __launch_bounds__(kThreads) k_gemm(GemmArgs g) {
+__device__ __forceinline__ void gemm_block(const GemmArgs& g, int bx, int z, uint16_t* smem,
+                                           float* q4, float* q8) {
   using T = Tile<BM, BN, BK, WGM, WGN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
-  __shared__ float q4[16];
-  __shared__ float q8[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   int tp, tq;
-  tile_coords(blockIdx.x, g.tiles_p, g.tiles_q, g.group_p, tp, tq);
-  const int p0 = tp * BM, q0 = tq * BN, z = blockIdx.z;
+  tile_coords(bx, g.tiles_p, g.tiles_q, g.group_p, tp, tq);
+  const int p0 = tp * BM, q0 = tq * BN;
   if (tid < 16) q4[tid] = nf4_level(tid);
   q8[tid] = dq_level(tid);
   Dec d;
@@ -519,6 +520,50 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmArgs g) {
         }
       }
     }
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, class LA1, class LB1, class LA2, class LB2, int EPI>
+__global__ void __launch_bounds__(kThreads) k_gemm(GemmArgs g) {
+  using T = Tile<BM, BN, BK, WGM, WGN>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+  __shared__ float q4[16];
+  __shared__ float q8[256];
+  gemm_block<BM, BN, BK, WGM, WGN, LA1, LB1, LA2, LB2, EPI>(g, blockIdx.x, blockIdx.z, smem, q4, q8);
+}
+
+constexpr int kPairBK = 64;   // contraction step of the paired skinny products (kBK below)
+
+// Tile shape and loaders of one tile-engine product, for k_gemm_pair.
+template <int BM_, int BN_, class LA_, class LB_>
+struct GemmShape {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WGM = (BN == 32) ? 4 : (BM == 32 ? 1 : 2);
+  static constexpr int WGN = 4 / WGM;
+  using LA = LA_;
+  using LB = LB_;
+};
+
+// Two independent tile-engine products in one launch (the backward's dA and
+// dB partials): blocks [0, blocks1) run the first, the rest the second, with
+// (tile, split) = (b mod tiles, b div tiles) of each.  The two share the
+// stage buffer, sized for the larger tile.
+template <class G1, class G2>
+__global__ void __launch_bounds__(kThreads) k_gemm_pair(GemmArgs g1, int blocks1, GemmArgs g2) {
+  constexpr int S1 = Tile<G1::BM, G1::BN, kPairBK, G1::WGM, G1::WGN>::STAGE;
+  constexpr int S2 = Tile<G2::BM, G2::BN, kPairBK, G2::WGM, G2::WGN>::STAGE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (S1 > S2 ? S1 : S2)];
+  __shared__ float q4[16];
+  __shared__ float q8[256];
+  const int b = blockIdx.x;
+  if (b < blocks1) {
+    const int tiles = g1.tiles_p * g1.tiles_q;
+    gemm_block<G1::BM, G1::BN, kPairBK, G1::WGM, G1::WGN, typename G1::LA, typename G1::LB, LdNone,
+               LdNone, EPI_F32_PARTIAL>(g1, b % tiles, b / tiles, smem, q4, q8);
+  } else {
+    const int c = b - blocks1, tiles = g2.tiles_p * g2.tiles_q;
+    gemm_block<G2::BM, G2::BN, kPairBK, G2::WGM, G2::WGN, typename G2::LA, typename G2::LB, LdNone,
+               LdNone, EPI_F32_PARTIAL>(g2, c % tiles, c / tiles, smem, q4, q8);
+  }
 }
 
 // Fixed-order reduction of split partials: out = scale * sum_z part[z].
@@ -581,6 +626,7 @@ static inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b)
 static inline int r_tile(int r) { return r <= 32 ? 32 : (r <= 64 ? 64 : 128); }
 
 constexpr int kBK = 64;
+static_assert(kBK == kPairBK, "paired products use the engine's contraction step");
 
 // dX tile (rows of dX x columns of dX).
 #ifndef QLK_DX_BM
@@ -776,6 +822,49 @@ static hipError_t skinny(int rt, const Operand& a, const Operand& b, int P, int 
   }
 }
 
+// The backward's two adapter-gradient products in one launch: dA partials
+// (rows j of U^T, columns k of X^T) and dB partials (rows n of dY^T, columns
+// j of T^T), both contracting over the M tokens in `splits` slices.
+static GemmArgs skinny_args(const Operand& a, const Operand& b, int P, int Q, int64_t C, int splits,
+                            float* part, int BM, int BN) {
+  GemmArgs g{};
+  g.a1 = a; g.b1 = b; g.P = P; g.Q = Q;
+  g.c1_len = (int)C;
+  g.c1_split = split_len(C, splits);
+  g.c2_len = 0;
+  g.out = part; g.ldo = Q;
+  g.tiles_p = ceil_div(P, BM);
+  g.tiles_q = ceil_div(Q, BN);
+  g.group_p = group_for(g.tiles_p, g.tiles_q, 1.0, 1.0);
+  return g;
+}
+
+template <int RT>
+static hipError_t skinny_pair_rt(const Operand& aa, const Operand& ba, int Pa, int Qa, int splits_a,
+                                 float* part_a, const Operand& ab, const Operand& bb, int Pb, int Qb,
+                                 int splits_b, float* part_b, int64_t C, hipStream_t st) {
+  using GA = GemmShape<RT, 128, LdBF16T<RT, kBK, false>, LdBF16T<128, kBK, false>>;
+  using GB = GemmShape<128, RT, LdBF16T<128, kBK, false>, LdBF16T<RT, kBK, false>>;
+  const GemmArgs ga = skinny_args(aa, ba, Pa, Qa, C, splits_a, part_a, GA::BM, GA::BN);
+  const GemmArgs gb = skinny_args(ab, bb, Pb, Qb, C, splits_b, part_b, GB::BM, GB::BN);
+  const int blocks_a = ga.tiles_p * ga.tiles_q * actual_splits(C, splits_a);
+  const int blocks_b = gb.tiles_p * gb.tiles_q * actual_splits(C, splits_b);
+  hipLaunchKernelGGL((k_gemm_pair<GA, GB>), dim3((unsigned)(blocks_a + blocks_b)), dim3(kThreads), 0,
+                     st, ga, blocks_a, gb);
+  return hipGetLastError();
+}
+
+static hipError_t skinny_pair(int rt, const Operand& aa, const Operand& ba, int Pa, int Qa,
+                              int splits_a, float* part_a, const Operand& ab, const Operand& bb,
+                              int Pb, int Qb, int splits_b, float* part_b, int64_t C,
+                              hipStream_t st) {
+  if (rt == 32)
+    return skinny_pair_rt<32>(aa, ba, Pa, Qa, splits_a, part_a, ab, bb, Pb, Qb, splits_b, part_b, C, st);
+  if (rt == 64)
+    return skinny_pair_rt<64>(aa, ba, Pa, Qa, splits_a, part_a, ab, bb, Pb, Qb, splits_b, part_b, C, st);
+  return skinny_pair_rt<128>(aa, ba, Pa, Qa, splits_a, part_a, ab, bb, Pb, Qb, splits_b, part_b, C, st);
+}
+
 #define QLK_TRY(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
 
 // T = X A^T (bf16 [M, r]) through split partials + fixed-order reduction.
@@ -926,12 +1015,12 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     timer_end(TK_DX_GEMM, st);
     QLK_TRY(e);
   }
-  // dA = s U^T X: rows j (U^T, transposed), cols k (X^T, transposed), contraction m.
-  QLK_TRY((skinny<1, 1, true>(rt, opnd(U, r, r, M), opnd(X, K, (int)K, M), r, (int)K, M, plan.m_splits_a,
-                              part, st)));
-  // dB = s dY^T T: rows n (dY^T), cols j (T^T), contraction m.
-  QLK_TRY((skinny<1, 1, false>(rt, opnd(dY, N, (int)N, M), opnd(T, r, r, M), (int)N, r, M,
-                               plan.m_splits_b, part_b, st)));
+  // dA = s U^T X: rows j (U^T, transposed), cols k (X^T, transposed), and
+  // dB = s dY^T T: rows n (dY^T), cols j (T^T), both contracting over m: one
+  // launch for the partials of both.
+  QLK_TRY(skinny_pair(rt, opnd(U, r, r, M), opnd(X, K, (int)K, M), r, (int)K, plan.m_splits_a, part,
+                      opnd(dY, N, (int)N, M), opnd(T, r, r, M), (int)N, r, plan.m_splits_b, part_b,
+                      M, st));
   // Both fixed-order split reductions in one launch.
   const int64_t na = (int64_t)r * K, nb = N * r;
   const int blocks_a = (int)((na / 4 + kRedCols - 1) / kRedCols);
