@@ -25,8 +25,6 @@ constexpr uint32_t kNF4Bits[16] = {
 
 constexpr int kBlock = 64;      // weights per absmax constant
 constexpr int kDQBlock = 256;   // constants per second-level scale
-constexpr int kZeroCode4 = 7;   // index of the exact zero level
-constexpr int kZeroCode8 = 127;
 
 __device__ __forceinline__ float nf4_level(int i) { return __uint_as_float(kNF4Bits[i]); }
 
@@ -161,18 +159,6 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t
 constexpr uint32_t kOOB = 0x80000000u;       // offset beyond any accepted buffer
 constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
 
-// All arguments are wave-uniform.  The remaining size is a saturating
-// subtraction, which exists only as a vector instruction; readfirstlane brings
-// it back to a scalar register, so the resource stays in scalar registers and
-// the load needs no per-lane resource loop.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base, uint32_t bytes,
-                                                          uint32_t shift) {
-  shift = __builtin_amdgcn_readfirstlane(shift);
-  const uint32_t rem = __builtin_amdgcn_readfirstlane(shift < bytes ? bytes - shift : 0u);
-  return __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(reinterpret_cast<const char*>(base) + shift), (short)0, (int)rem,
-      kRsrcWord3);
-}
 // A resource over a whole array, built once per kernel.  Loads then add a
 // wave-uniform byte offset in the instruction's scalar offset field, so a
 // K-step costs one scalar add instead of a new resource.  Out-of-range lanes
@@ -196,9 +182,6 @@ __device__ __forceinline__ uint32_t bload8s(__amdgpu_buffer_rsrc_t r, uint32_t v
 }
 __device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
-__device__ __forceinline__ uint2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
 }
 __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);

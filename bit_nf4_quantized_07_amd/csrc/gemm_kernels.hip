@@ -571,35 +571,6 @@ __global__ void __launch_bounds__(kThreads) k_gemm_pair(GemmArgs g1, int blocks1
 // 16 lanes per group: lane g sums the splits z = g, g+16, g+32, ... with
 // 16-byte loads, and the 16 lane sums are then added in the order g = 0..15.
 constexpr int kRedCols = 16, kRedLanes = 16;
-__global__ void __launch_bounds__(256)
-k_reduce_splits(const float* __restrict__ part, int splits, int64_t n, float scale,
-                float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16) {
-  __shared__ float4 red[kRedLanes][kRedCols];
-  const int tid = threadIdx.x, col = tid % kRedCols, g = tid / kRedCols;
-  const int64_t n4 = n / 4;
-  const int64_t i4 = (int64_t)blockIdx.x * kRedCols + col;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (i4 < n4) {
-    const float4* p = reinterpret_cast<const float4*>(part) + i4;
-#pragma unroll 2
-    for (int z = g; z < splits; z += kRedLanes) {
-      const float4 v = p[(int64_t)z * n4];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-  }
-  red[g][col] = acc;
-  __syncthreads();
-  if (g != 0 || i4 >= n4) return;
-  float4 t = red[0][col];
-#pragma unroll
-  for (int q = 1; q < kRedLanes; ++q) {
-    const float4 v = red[q][col];
-    t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
-  }
-  t.x *= scale; t.y *= scale; t.z *= scale; t.w *= scale;
-  if (out_f32) reinterpret_cast<float4*>(out_f32)[i4] = t;
-  if (out_bf16) reinterpret_cast<uint2*>(out_bf16)[i4] = make_uint2(pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w));
-}
 
 // ---------------------------- measurement hook ------------------------------
 
@@ -737,9 +708,8 @@ static hipError_t launch_gemm(GemmArgs g, int splits, double a_tile_bytes, doubl
   return hipGetLastError();
 }
 
-// Both split reductions of the backward (dA and dB) in one launch: blocks
-// [0, blocks of dA) take dA, the rest dB; each block runs the same fixed
-// order as k_reduce_splits.
+// Both split reductions of the backward (dA and dB) in one launch, in the
+// fixed order above: blocks [0, blocks of dA) take dA, the rest dB.
 __global__ void __launch_bounds__(256)
 k_reduce_splits2(const float* __restrict__ part_a, int splits_a, int64_t n_a, float* __restrict__ out_a,
                  const float* __restrict__ part_b, int splits_b, int64_t n_b, float* __restrict__ out_b,
@@ -775,51 +745,12 @@ k_reduce_splits2(const float* __restrict__ part_a, int splits_a, int64_t n_a, fl
   reinterpret_cast<float4*>(out)[i4] = t;
 }
 
-static hipError_t launch_reduce(const float* part, int splits, int64_t n, float scale, float* of,
-                                uint16_t* ob, hipStream_t st) {
-  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n / 4 + kRedCols - 1) / kRedCols)), dim3(256), 0, st, part,
-                     splits, n, scale, of, ob);
-  return hipGetLastError();
-}
-
 // `src_rows` x `ld` is the whole source matrix (for its byte size).
 static Operand opnd(const uint16_t* p, int64_t ld, int rows, int64_t src_rows, float scale = 1.0f) {
   Operand o;
   o.p = p; o.ld = ld; o.rows = rows; o.scale = scale;
   o.bytes = (uint32_t)(src_rows * ld * 2);
   return o;
-}
-
-// C[P, Q] partial products over a split contraction, both operands bf16.
-// AK/BKIND: 0 = contraction contiguous (K-major), 1 = transposed (MN-major).
-template <int BM, int BN, int AK, int BKIND>
-static hipError_t skinny_partials(const Operand& a, const Operand& b, int P, int Q, int64_t C,
-                                  int splits, float* part, hipStream_t st) {
-  GemmArgs g{};
-  g.a1 = a; g.b1 = b; g.P = P; g.Q = Q;
-  g.c1_len = (int)C;
-  g.c1_split = split_len(C, splits);
-  g.c2_len = 0;
-  g.out = part; g.ldo = Q;
-  using LA = typename std::conditional<AK == 0, LdBF16K<BM, kBK, false>, LdBF16T<BM, kBK, false>>::type;
-  using LB = typename std::conditional<BKIND == 0, LdBF16K<BN, kBK, false>, LdBF16T<BN, kBK, false>>::type;
-  return launch_gemm<BM, BN, kBK, LA, LB, LdNone, LdNone, EPI_F32_PARTIAL>(
-      g, actual_splits(C, splits), 1.0, 1.0, st);
-}
-
-// Dispatch on the adapter-rank tile (32, 64 or 128).
-template <int AK, int BKIND, bool R_ON_P>
-static hipError_t skinny(int rt, const Operand& a, const Operand& b, int P, int Q, int64_t C,
-                         int splits, float* part, hipStream_t st) {
-  if (R_ON_P) {
-    if (rt == 32) return skinny_partials<32, 128, AK, BKIND>(a, b, P, Q, C, splits, part, st);
-    if (rt == 64) return skinny_partials<64, 128, AK, BKIND>(a, b, P, Q, C, splits, part, st);
-    return skinny_partials<128, 128, AK, BKIND>(a, b, P, Q, C, splits, part, st);
-  } else {
-    if (rt == 32) return skinny_partials<128, 32, AK, BKIND>(a, b, P, Q, C, splits, part, st);
-    if (rt == 64) return skinny_partials<128, 64, AK, BKIND>(a, b, P, Q, C, splits, part, st);
-    return skinny_partials<128, 128, AK, BKIND>(a, b, P, Q, C, splits, part, st);
-  }
 }
 
 // The backward's two adapter-gradient products in one launch: dA partials
