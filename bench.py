@@ -26,6 +26,8 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                    the GEMV kernel must move over its average duration vs HBM
   mlp_gate_up      the 11008-wide MLP's gate/up projections (4096 tokens):
                    the fused forward vs the composition, and the backward
+  blocks           whole workloads forward + backward: the 11008-wide MLP
+                   block and the 65B-shaped decoder layer (TFLOP/s)
   standalone       the load-time kernels (quantize, double quant, dequant), the
                    adapter merge and the dropout kernel in GB/s, with the
                    merge's error against the unquantised base and the NF4 vs
@@ -418,6 +420,86 @@ def run_mlp(args, q, torch, wl, lib, ev):
                 bwd_tflops=round(bflops / (ms_b * 1e-3) / 1e12, 1))
 
 
+def _linears(q, torch, wl, cfg, names):
+    """Quantised base weights and adapters of the named linears of a workload."""
+    dev_bf16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    out = {}
+    for j, lin in enumerate(cfg.linears):
+        if lin.name in names:
+            W = wl.weight(0, cfg.cfg_id, j, lin)
+            A, B = wl.adapters(0, cfg.cfg_id, j, lin)
+            out[lin.name] = (q.quantize(torch.from_numpy(W).cuda()), dev_bf16(A), dev_bf16(B),
+                             lin.alpha)
+            del W
+    return out
+
+
+def run_blocks(args, q, torch, wl):
+    """Whole workloads, forward and backward, in TFLOP/s of 4MNK + 6Mr(N+K)
+    per linear:
+      c3: the 11008-wide SiLU-gated MLP block (fused gate/up forward, down
+          projection, down backward, gating backward, gate/up backward);
+      c5: the 65B-shaped decoder layer: q, k, v (one input, dX accumulated),
+          o (its own input, standing in for the attention output; the
+          attention core is not part of the method) and the 22016-wide MLP
+          block.  Inputs and output gradients ~ N(0, 1)."""
+    dev_bf16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    res = {}
+    ws = q.Workspace("cuda")
+
+    def mlp_block(L, X, dY):
+        G, U, H, Tg, Tu = q.mlp_fwd(X, L["gate"], L["up"], workspace=ws)
+        _, Td = q.linear_fwd(H, *L["down"], workspace=ws)
+        dH, _, _ = q.linear_bwd(dY, H, *L["down"], T=Td, workspace=ws)
+        q.mlp_bwd(dH, X, L["gate"], L["up"], G, U, Tg, Tu, workspace=ws)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    def flops(cfg):
+        return sum(linear_flops(cfg.M, l.N, l.K, l.r) for l in cfg.linears)
+
+    c3 = wl.workloads()["c3_mlp_11008"]
+    L3 = _linears(q, torch, wl, c3, ("gate", "up", "down"))
+    X3 = dev_bf16(wl.activations(0, c3.cfg_id, c3.M, 4096))
+    dY3 = dev_bf16(wl.grad_output(0, c3.cfg_id, c3.M, 4096))
+    ms = timed(lambda: mlp_block(L3, X3, dY3), 5)
+    res["c3_mlp_block"] = dict(ms_per_step=round(ms, 4), gflop=round(flops(c3) / 1e9, 2),
+                               tflops=round(flops(c3) / (ms * 1e-3) / 1e12, 1),
+                               frac_bf16_peak=round(flops(c3) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    del L3, X3, dY3
+
+    c5 = wl.workloads()["c5_decoder_8192"]
+    L5 = _linears(q, torch, wl, c5, ("q", "k", "v", "o", "gate", "up", "down"))
+    M, d = c5.M, 8192
+    X = dev_bf16(wl.activations(0, c5.cfg_id, M, d))
+    Xo = dev_bf16(wl.activations(0, c5.cfg_id, M, d, sub=3))
+    Xm = dev_bf16(wl.activations(0, c5.cfg_id, M, d, sub=4))
+    dYs = {n: dev_bf16(wl.grad_output(0, c5.cfg_id, M, d, sub=i))
+           for i, n in enumerate(("q", "k", "v", "o", "mlp"))}
+
+    def layer():
+        dX = None
+        for n in ("q", "k", "v"):
+            _, T = q.linear_fwd(X, *L5[n], workspace=ws)
+            dX, _, _ = q.linear_bwd(dYs[n], X, *L5[n], T=T, accumulate_into=dX, workspace=ws)
+        _, T = q.linear_fwd(Xo, *L5["o"], workspace=ws)
+        q.linear_bwd(dYs["o"], Xo, *L5["o"], T=T, workspace=ws)
+        mlp_block(L5, Xm, dYs["mlp"])
+    ms = timed(layer, 3)
+    res["c5_decoder_layer"] = dict(ms_per_step=round(ms, 4), gflop=round(flops(c5) / 1e9, 2),
+                                   tflops=round(flops(c5) / (ms * 1e-3) / 1e12, 1),
+                                   frac_bf16_peak=round(flops(c5) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    return res
+
+
 def run_standalone(args, q, torch, lib, ev):
     """The load-time kernels and the adapter merge on the default workload's
     weight shape (4096 x 4096, r = 16), event-timed per call over 8 rotated
@@ -617,7 +699,8 @@ COUNTER_SETS = {
     "f": "FETCH_SIZE",
     "w": "WRITE_SIZE",
 }
-SHORT_RUN = "--steps 3 --warmup 1 --no-cpu-baseline --no-standalone --no-mlp --no-variants"
+SHORT_RUN = ("--steps 3 --warmup 1 --no-cpu-baseline --no-standalone --no-mlp --no-variants "
+             "--no-blocks")
 
 
 def profile_commands(out: str) -> dict:
@@ -796,6 +879,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-standalone", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
+    ap.add_argument("--no-blocks", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the bf16-base and dropout steps (counter runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -840,6 +924,11 @@ def main():
         err("[bench] MLP gate/up ...")
         mlp = run_mlp(args, q, torch, wl, lib, ev)
         err(f"[bench] mlp {mlp}")
+    blocks = None
+    if not args.no_blocks:
+        err("[bench] MLP block and decoder layer ...")
+        blocks = run_blocks(args, q, torch, wl)
+        err(f"[bench] blocks {blocks}")
     standalone = None
     if not args.no_standalone:
         err("[bench] standalone quantize / double quant / dequant ...")
@@ -856,7 +945,7 @@ def main():
                 data="synthetic", config=lin["config"], roofline=lin["roofline"],
                 cpu_baseline=cpu, kernels=lin["kernels"], lora_bf16_base=lin["lora_bf16"],
                 lora_dropout=lin["lora_dropout"],
-                gemv=gemv, mlp_gate_up=mlp, standalone=standalone,
+                gemv=gemv, mlp_gate_up=mlp, blocks=blocks, standalone=standalone,
                 source_hash=source_hash())
     print(json.dumps(line), flush=True)
 
