@@ -713,6 +713,11 @@ def profile_commands(out: str) -> dict:
         extra = " --copy-calib" if k in ("f", "w") else ""
         cmds[k] = (f"rocprofv3 --pmc {ctr} --output-format csv -d {out}/{k} -o {k} "
                    f"-- python3 {me} {SHORT_RUN}{extra}")
+    # MFMA busy of the GEMMs on every workload shape: the same counters as p2
+    # over a run that also executes the MLP block and the decoder layer.
+    cmds["p2b"] = (f"rocprofv3 --pmc {COUNTER_SETS['p2']} --output-format csv -d {out}/p2b -o p2b "
+                   f"-- python3 {me} --steps 1 --warmup 1 --no-cpu-baseline --no-standalone "
+                   f"--no-mlp --no-variants --no-gemv")
     return cmds
 
 
@@ -865,6 +870,40 @@ def summarize(out: str):
                 div(_med(ag, "SQ_WAIT_INST_ANY"), wc), div(_med(ag, "SQ_WAIT_INST_LDS"), wc),
                 div(_med(ag, "SQ_LDS_BANK_CONFLICT"), _med(ag, "SQ_ACTIVE_INST_LDS"))))
     md += ["", "VALU instructions exclude the MFMAs (SQ_INSTS_VALU counts both)."]
+    # MFMA busy by launch shape over the run with the whole workloads
+    p2b = os.path.join(out, "p2b", "p2b_counter_collection.csv")
+    if os.path.exists(p2b):
+        md += ["", "MFMA busy of the GEMM kernels by launch shape, from a run that also executes "
+               "the 11008-wide MLP block (c3) and the 65B-shaped decoder layer (c5):", "",
+               "```", cmds["p2b"], "```", "",
+               "| kernel | grid (work-items) | workload | dispatches | clock GHz | MFMA busy |",
+               "|---|---:|---|---:|---:|---:|"]
+        shapes = {("k_fwd_nf4<false, false>", 65536): "c2 forward",
+                  ("k_dx_nf4<true>", 131072): "c2 dX",
+                  ("k_fwd_nf4<false, true>", 704512): "c3 gate/up (fused)",
+                  ("k_fwd_nf4<false, false>", 131072): "c3 down forward",
+                  ("k_dx_nf4<true>", 262144): "c3 gate/up dX",
+                  ("k_dx_nf4<true>", 704512): "c3 down dX",
+                  ("k_fwd_nf4<false, false>", 262144): "c5 q/k/v/o and down forward",
+                  ("k_fwd_nf4<false, true>", 1409024): "c5 gate/up (fused)",
+                  ("k_dx_nf4<true>", 1409024): "c5 down dX",
+                  ("k_dx_nf4<true>", 524288): "c5 q/k/v/o and gate/up dX"}
+        groups = {}
+        for r in _csv(p2b):
+            name = r["Kernel_Name"]
+            for sym in ("k_fwd_nf4<false, false>", "k_fwd_nf4<false, true>", "k_dx_nf4<true>"):
+                if sym in name:
+                    key = (sym, int(r["Grid_Size"]))
+                    d = groups.setdefault(key, {}).setdefault(
+                        int(r["Dispatch_Id"]), dict(_ns=int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+                    d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for (sym, grid), dd in sorted(groups.items()):
+            ds = list(dd.values())
+            gui = _med(ds, "GRBM_GUI_ACTIVE") / 8
+            busy = _med(ds, "SQ_VALU_MFMA_BUSY_CYCLES") / 1024 / gui
+            md.append("| `%s` | %d | %s | %d | %.2f | %.1f %% |" % (
+                sym, grid, shapes.get((sym, grid), "other"), len(ds), gui / _med(ds, "_ns"),
+                100 * busy))
     with open(os.path.join(prof, "counters_gemms_gemv.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
 
