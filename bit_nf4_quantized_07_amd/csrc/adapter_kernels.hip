@@ -8,11 +8,16 @@
 // W(j, c) = A[j][c] (contraction contiguous) or B[c][j] (transposed).
 // One workgroup owns 16 rows of S (or 8, with the MFMA's other 8 rows zero,
 // when 16-row tiles would leave CUs idle) and all r outputs; its NW waves take every
-// NW-th 32-wide slice of the contraction (v_mfma_f32_16x16x32_bf16, operands
-// loaded straight from memory, S read once in total; many waves per
-// workgroup keep enough loads in flight to stream S), and the NW partial sums
-// are added through LDS in a fixed order, so the bf16 result is written by
-// the same kernel and is bit-reproducible.
+// NW-th 64-wide slice of the contraction (v_mfma_f32_16x16x32_bf16, S read
+// once in total), and the NW partial sums are added through LDS in a fixed
+// order, so the bf16 result is written by the same kernel and is
+// bit-reproducible.  A wave issues the loads of several slices before their
+// MFMAs (branch-free: out-of-range pieces are loaded from a valid address and
+// replaced by zeros), so that many loads are in flight per wave.  W(j, c) =
+// B[c][j] is loaded as rows of B (16 bytes per lane, coalesced) and
+// transposed through a 1 KB slice of LDS per wave by the transposing LDS
+// read; r and C are multiples of 8, so every 16-byte piece is wholly inside
+// or wholly outside the operands.
 #include <type_traits>
 
 #include "dequant_block.h"
@@ -24,47 +29,109 @@ namespace qlk {
 constexpr int kRankRows = 16;
 constexpr int kRankMaxTiles = 16;   // r <= 256
 
+// Contraction slices whose loads one wave issues together (registers:
+// 8 (1 + RT) per slice).
+// The transposed case keeps to 64 VGPRs at r <= 16, so that its combined
+// launch with the dequantisation still runs two workgroups per CU.
+template <bool WT, int RT>
+constexpr int rank_batch() { return RT <= 1 ? (WT ? 2 : 4) : (RT <= 2 ? 2 : 1); }
+
+// v if ok, else zeros (component-wise: a select of the struct would go
+// through private memory).
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
 // One workgroup's share; `blk` is its index in the rank-r grid.
+//
+// A slice is 64 contraction indices, two MFMAs.  Lane (row, grp) loads the
+// 16 contiguous indices 16 grp .. 16 grp + 15 of the slice (two 16-byte
+// loads), so that the four lanes of a row cover its 128 bytes and every
+// cache line fetched is used whole; MFMA h takes indices 16 grp + 8 h .. +7
+// of every lane, the same permutation of the slice for both operands.
 template <bool WT, int RT, int NW>
 __device__ __forceinline__ void rank16_block(const uint16_t* __restrict__ S, int M, int64_t C,
                                              const uint16_t* __restrict__ W, int r, int rows,
                                              uint16_t* __restrict__ out, int blk) {
+  constexpr int kB = rank_batch<WT, RT>();
   __shared__ float red[NW - 1][kRankRows][RT * 16];
+  // WT: one 64 (c) x 16 (j) slice of B per wave, row-major.
+  __shared__ __attribute__((aligned(16))) uint16_t slab[WT ? NW : 1][64 * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, grp = lane >> 4;
   const int m0 = blk * rows;
   const int m = m0 + row;
   const bool mvalid = row < rows && m < M;
-  const int64_t nsteps = (C + 31) / 32;
+  const int64_t nsteps = (C + 63) / 64;
   const uint16_t* srow = S + (int64_t)(mvalid ? m : 0) * C;
+  // WT: lane L loads rows c0 + L / 2 and c0 + 32 + L / 2 of the slice,
+  // columns 8 (L % 2) .. +7, and reads back column `row` of rows
+  // 16 grp + 8 h .. +7 for MFMA h (transposing reads of four rows each).
+  const int wrow = lane >> 1, wcol = 8 * (lane & 1);
+  uint16_t* const my = slab[WT ? wave : 0];
+  const int rd = (16 * grp + (row >> 2)) * 16 + 4 * (row & 3);
 
   f32x4_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-#pragma unroll 8
-  for (int64_t ks = wave; ks < nsteps; ks += NW) {
-    const int64_t k = ks * 32 + 8 * grp;   // this lane's 8 contraction indices
-    const bool kvalid = k < C;             // C % 8 == 0: a group of 8 is all in or all out
-    uint4 av = make_uint4(0, 0, 0, 0);
-    if (mvalid && kvalid) av = *reinterpret_cast<const uint4*>(srow + k);
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+  for (int64_t base = wave; base < nsteps; base += (int64_t)NW * kB) {
+    uint4 xv[kB][2], wv[kB][RT][2];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int j = 16 * t + row;
-      uint4 bv = make_uint4(0, 0, 0, 0);
-      if (j < r && kvalid) {
-        if (!WT) {
-          bv = *reinterpret_cast<const uint4*>(W + (int64_t)j * C + k);
-        } else {
-          uint32_t w[4];
+    for (int b = 0; b < kB; ++b) {
+      const int64_t ks = base + (int64_t)NW * b;
+      const bool sv = ks < nsteps;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            w[q] = (uint32_t)W[(k + 2 * q) * r + j] | ((uint32_t)W[(k + 2 * q + 1) * r + j] << 16);
-          bv = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int h = 0; h < 2; ++h) {
+        const int64_t k = ks * 64 + 16 * grp + 8 * h;   // 8 contraction indices
+        const bool kvalid = sv && k < C;
+        const uint4 v = *reinterpret_cast<const uint4*>(srow + (kvalid ? k : 0));
+        xv[b][h] = keep_if(mvalid && kvalid, v);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          if (!WT) {
+            const int j = 16 * t + row;
+            const bool ok = kvalid && j < r;
+            const uint4 w = *reinterpret_cast<const uint4*>(W + (ok ? (int64_t)j * C + k : 0));
+            wv[b][t][h] = keep_if(ok, w);
+          } else {
+            const int64_t c = ks * 64 + 32 * h + wrow;
+            const int j = 16 * t + wcol;
+            const bool ok = sv && c < C && j < r;
+            const uint4 w = *reinterpret_cast<const uint4*>(W + (ok ? c * r + j : 0));
+            wv[b][t][h] = keep_if(ok, w);
+          }
         }
       }
-      acc[t] = mfma_16x16x32(a, __builtin_bit_cast(bf16x8_t, bv), acc[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch before the first MFMA
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        bf16x8_t bop[2];
+        if (!WT) {
+          bop[0] = __builtin_bit_cast(bf16x8_t, wv[b][t][0]);
+          bop[1] = __builtin_bit_cast(bf16x8_t, wv[b][t][1]);
+        } else {
+          // A wave's LDS operations run in issue order: the stores are
+          // complete before the reads, which complete before the next stores.
+          *reinterpret_cast<uint4*>(my + wrow * 16 + wcol) = wv[b][t][0];
+          *reinterpret_cast<uint4*>(my + (32 + wrow) * 16 + wcol) = wv[b][t][1];
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const v4s_t lo = lds_read_tr16(my + rd + 8 * h * 16);
+            const v4s_t hi = lds_read_tr16(my + rd + (8 * h + 4) * 16);
+            typedef short v8s_t __attribute__((ext_vector_type(8)));
+            const v8s_t bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            bop[h] = __builtin_bit_cast(bf16x8_t, bv);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[t] = mfma_16x16x32(__builtin_bit_cast(bf16x8_t, xv[b][h]), bop[h], acc[t]);
+      }
     }
   }
 
