@@ -566,11 +566,10 @@ __global__ void __launch_bounds__(kThreads) k_gemm_pair(GemmArgs g1, int blocks1
   }
 }
 
-// Fixed-order reduction of split partials: out = scale * sum_z part[z].
-// n is a multiple of 4.  A workgroup covers 16 groups of four outputs with
-// 16 lanes per group: lane g sums the splits z = g, g+16, g+32, ... with
-// 16-byte loads, and the 16 lane sums are then added in the order g = 0..15.
-constexpr int kRedCols = 16, kRedLanes = 16;
+// Fixed-order reduction of split partials: out = scale * sum_z part[z],
+// summed in the order z = 0, 1, ..., splits - 1.  n is a multiple of 4; one
+// thread per four outputs (coalesced 16-byte loads, eight splits in flight).
+constexpr int kRedThreads = 64;
 
 // ---------------------------- measurement hook ------------------------------
 
@@ -710,35 +709,23 @@ static hipError_t launch_gemm(GemmArgs g, int splits, double a_tile_bytes, doubl
 
 // Both split reductions of the backward (dA and dB) in one launch, in the
 // fixed order above: blocks [0, blocks of dA) take dA, the rest dB.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRedThreads)
 k_reduce_splits2(const float* __restrict__ part_a, int splits_a, int64_t n_a, float* __restrict__ out_a,
                  const float* __restrict__ part_b, int splits_b, int64_t n_b, float* __restrict__ out_b,
                  int blocks_a, float scale) {
-  __shared__ float4 red[kRedLanes][kRedCols];
   const bool first = (int)blockIdx.x < blocks_a;
   const float* part = first ? part_a : part_b;
   const int splits = first ? splits_a : splits_b;
   const int64_t n4 = (first ? n_a : n_b) / 4;
   float* out = first ? out_a : out_b;
   const int64_t blk = first ? blockIdx.x : blockIdx.x - blocks_a;
-  const int tid = threadIdx.x, col = tid % kRedCols, g = tid / kRedCols;
-  const int64_t i4 = blk * kRedCols + col;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (i4 < n4) {
-    const float4* p = reinterpret_cast<const float4*>(part) + i4;
-#pragma unroll 2
-    for (int z = g; z < splits; z += kRedLanes) {
-      const float4 v = p[(int64_t)z * n4];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-  }
-  red[g][col] = acc;
-  __syncthreads();
-  if (g != 0 || i4 >= n4) return;
-  float4 t = red[0][col];
-#pragma unroll
-  for (int q = 1; q < kRedLanes; ++q) {
-    const float4 v = red[q][col];
+  const int64_t i4 = blk * kRedThreads + threadIdx.x;
+  if (i4 >= n4) return;
+  const float4* p = reinterpret_cast<const float4*>(part) + i4;
+  float4 t = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+  for (int z = 0; z < splits; ++z) {
+    const float4 v = p[(int64_t)z * n4];
     t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
   }
   t.x *= scale; t.y *= scale; t.z *= scale; t.w *= scale;
@@ -954,9 +941,9 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
                       M, st));
   // Both fixed-order split reductions in one launch.
   const int64_t na = (int64_t)r * K, nb = N * r;
-  const int blocks_a = (int)((na / 4 + kRedCols - 1) / kRedCols);
-  const int blocks_b = (int)((nb / 4 + kRedCols - 1) / kRedCols);
-  hipLaunchKernelGGL(k_reduce_splits2, dim3((unsigned)(blocks_a + blocks_b)), dim3(256), 0, st, part,
+  const int blocks_a = (int)((na / 4 + kRedThreads - 1) / kRedThreads);
+  const int blocks_b = (int)((nb / 4 + kRedThreads - 1) / kRedThreads);
+  hipLaunchKernelGGL(k_reduce_splits2, dim3((unsigned)(blocks_a + blocks_b)), dim3(kRedThreads), 0, st, part,
                      actual_splits(M, plan.m_splits_a), na, dA, part_b, actual_splits(M, plan.m_splits_b),
                      nb, dB, blocks_a, s);
   return hipGetLastError();
