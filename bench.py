@@ -74,8 +74,8 @@ def source_hash(files=None) -> str:
 
 # bench timer name -> (kernel symbol in profiler output, source file, workload)
 PROFILED = {
-    "dx_gemm": ("k_dx_nf4<true>", "dx_kernels.hip", "c2_linear_4096"),
-    "fwd_gemm": ("k_fwd_nf4<false, false>", "fwd_kernels.hip", "c2_linear_4096"),
+    "dx_gemm": ("k_dx_nf4<true, false>", "dx_kernels.hip", "c2_linear_4096"),
+    "fwd_gemm": ("k_fwd_nf4<false>", "fwd_kernels.hip", "c2_linear_4096"),
     "gemv": ("k_gemv_dma", "gemv_kernels.hip", "c4_gemv_28672x8192"),
     "dx_prep": ("k_rank16_and_dequant", "adapter_kernels.hip+dequant_block.h", "c2_linear_4096"),
 }
@@ -878,20 +878,20 @@ def summarize(out: str):
                "```", cmds["p2b"], "```", "",
                "| kernel | grid (work-items) | workload | dispatches | clock GHz | MFMA busy |",
                "|---|---:|---|---:|---:|---:|"]
-        shapes = {("k_fwd_nf4<false, false>", 65536): "c2 forward",
-                  ("k_dx_nf4<true>", 131072): "c2 dX",
-                  ("k_fwd_nf4<false, true>", 704512): "c3 gate/up (fused)",
-                  ("k_fwd_nf4<false, false>", 131072): "c3 down forward",
-                  ("k_dx_nf4<true>", 262144): "c3 gate/up dX",
-                  ("k_dx_nf4<true>", 704512): "c3 down dX",
-                  ("k_fwd_nf4<false, false>", 262144): "c5 q/k/v/o and down forward",
-                  ("k_fwd_nf4<false, true>", 1409024): "c5 gate/up (fused)",
-                  ("k_dx_nf4<true>", 1409024): "c5 down dX",
-                  ("k_dx_nf4<true>", 524288): "c5 q/k/v/o and gate/up dX"}
+        shapes = {("k_fwd_nf4<false>", 65536): "c2 forward",
+                  ("k_dx_nf4<true, false>", 131072): "c2 dX",
+                  ("k_fwd_nf4<true>", 704512): "c3 gate/up (fused)",
+                  ("k_fwd_nf4<false>", 131072): "c3 down forward",
+                  ("k_dx_nf4<true, false>", 262144): "c3 gate/up dX",
+                  ("k_dx_nf4<true, false>", 704512): "c3 down dX",
+                  ("k_fwd_nf4<false>", 262144): "c5 q/k/v/o and down forward",
+                  ("k_fwd_nf4<true>", 1409024): "c5 gate/up (fused)",
+                  ("k_dx_nf4<true, false>", 1409024): "c5 down dX",
+                  ("k_dx_nf4<true, false>", 524288): "c5 q/k/v/o and gate/up dX"}
         groups = {}
         for r in _csv(p2b):
             name = r["Kernel_Name"]
-            for sym in ("k_fwd_nf4<false, false>", "k_fwd_nf4<false, true>", "k_dx_nf4<true>"):
+            for sym in ("k_fwd_nf4<false>", "k_fwd_nf4<true>", "k_dx_nf4<true, false>"):
                 if sym in name:
                     key = (sym, int(r["Grid_Size"]))
                     d = groups.setdefault(key, {}).setdefault(

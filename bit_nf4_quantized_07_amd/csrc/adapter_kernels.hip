@@ -30,11 +30,13 @@ constexpr int kRankRows = 16;
 constexpr int kRankMaxTiles = 16;   // r <= 256
 
 // Contraction slices whose loads one wave issues together (registers:
-// 8 (1 + RT) per slice).
-// The transposed case keeps to 64 VGPRs at r <= 16, so that its combined
-// launch with the dequantisation still runs two workgroups per CU.
-template <bool WT, int RT>
-constexpr int rank_batch() { return RT <= 1 ? (WT ? 2 : 4) : (RT <= 2 ? 2 : 1); }
+// 8 (1 + RT) per slice).  In the launch shared with the dequantisation the
+// batch is smaller, so that the kernel keeps to 64 VGPRs at r <= 16 and runs
+// two 1024-thread workgroups per CU for the dequantising workgroups.
+template <int RT>
+constexpr int rank_batch() { return RT <= 1 ? 4 : (RT <= 2 ? 2 : 1); }
+template <int RT>
+constexpr int rank_batch_shared() { return RT <= 1 ? 2 : 1; }
 
 // v if ok, else zeros (component-wise: a select of the struct would go
 // through private memory).
@@ -49,11 +51,10 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
 // loads), so that the four lanes of a row cover its 128 bytes and every
 // cache line fetched is used whole; MFMA h takes indices 16 grp + 8 h .. +7
 // of every lane, the same permutation of the slice for both operands.
-template <bool WT, int RT, int NW>
+template <bool WT, int RT, int NW, int kB>
 __device__ __forceinline__ void rank16_block(const uint16_t* __restrict__ S, int M, int64_t C,
                                              const uint16_t* __restrict__ W, int r, int rows,
                                              uint16_t* __restrict__ out, int blk) {
-  constexpr int kB = rank_batch<WT, RT>();
   __shared__ float red[NW - 1][kRankRows][RT * 16];
   // WT: one 64 (c) x 16 (j) slice of B per wave, row-major.
   __shared__ __attribute__((aligned(16))) uint16_t slab[WT ? NW : 1][64 * 16];
@@ -164,7 +165,7 @@ template <bool WT, int RT, int NW>
 __global__ void __launch_bounds__(NW * 64)
 k_rank16(const uint16_t* __restrict__ S, int M, int64_t C, const uint16_t* __restrict__ W, int r,
          int rows, uint16_t* __restrict__ out) {
-  rank16_block<WT, RT, NW>(S, M, C, W, r, rows, out, blockIdx.x);
+  rank16_block<WT, RT, NW, rank_batch<RT>()>(S, M, C, W, r, rows, out, blockIdx.x);
 }
 
 // The backward's U = dY B and its one-off dequantisation of the weight are
@@ -181,7 +182,7 @@ k_rank16_and_dequant(const uint16_t* __restrict__ S, int M, int64_t C,
                      const float* __restrict__ mean, int64_t nwords, Codebook4 cb,
                      uint16_t* __restrict__ wout) {
   if ((int)blockIdx.x < rank_blocks)
-    rank16_block<true, RT, NW>(S, M, C, W, r, rows, out, blockIdx.x);
+    rank16_block<true, RT, NW, rank_batch_shared<RT>()>(S, M, C, W, r, rows, out, blockIdx.x);
   else
     nf4_dequant_block(packed, codes, scales, mean, nwords, cb, wout,
                       (int64_t)blockIdx.x - rank_blocks);

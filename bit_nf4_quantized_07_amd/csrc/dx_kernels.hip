@@ -36,6 +36,14 @@
 //    accumulators; each lane stores four consecutive features (8 bytes).
 //    With LoRA dropout on the adapter input the term is accumulated apart,
 //    multiplied by mask * 1/(1-p) per element, then added.
+//
+// NT: the same kernel computes the forward Y = X W_hat^T + s T B^T on a bf16
+// weight (the weight dequantised once per call, or a bf16 base).  There the
+// contraction runs over the weight's columns, so the weight tile of a step
+// (128 rows x 64 columns) has the token tile's shape: it is loaded into LDS
+// like the token tile (rows of 128 bytes, the same swizzle) and its MFMA
+// operand is read like the token operand, with no transpose.  The adapter
+// term takes rows of s B straight from memory.
 #include <type_traits>
 
 #include "device_common.h"
@@ -79,8 +87,9 @@ __device__ __forceinline__ int wswz(int n) { return ((n & 3) << 2) | ((n >> 2) &
 // weight tile is copied into LDS by buffer loads that write LDS directly (two
 // per wave, the same swizzled layout the decode writes), with nothing to
 // decode -- the same kernel with the dequantisation switched off.
-template <bool BF16W>
+template <bool BF16W, bool NT = false>
 __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
+  static_assert(BF16W || !NT, "the forward form takes a bf16 weight");
   __shared__ __attribute__((aligned(16))) uint16_t dy0[kDyTile];
   __shared__ __attribute__((aligned(16))) uint16_t dy1[kDyTile];
   __shared__ __attribute__((aligned(16))) uint16_t dy2[kDyTile];
@@ -98,7 +107,9 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   tile_coords(blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
   const int m0 = tm * kDxBM;
   const int64_t k0 = (int64_t)tk * kDxBK;
-  const int64_t N = g.w.N, K = g.w.K, nkb = K / kBlock;
+  // N: contraction length; K: output features (dX columns, or Y columns and
+  // weight rows in the forward form).
+  const int64_t N = NT ? g.w.K : g.w.N, K = NT ? g.w.N : g.w.K, nkb = K / kBlock;
   const int nsteps = (int)(N / kDxStepN);
   const float mean = BF16W ? 0.0f : g.w.mean[0];
   const float qlev = nf4_level(lane & 15);   // source of the level lookups
@@ -165,18 +176,30 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   // 8 w + 4 i + L / 16, physical piece L % 16, i.e. logical piece
   // (L % 16) ^ wswz(row).
   const __amdgpu_buffer_rsrc_t rwb = rsrc_whole(g.w.bf16, (uint32_t)(BF16W ? N * K * 2 : 0));
+  // NT: load i of wave w fills weight rows 16 w + 8 i .. +7 of the tile
+  // (rows of 64 contraction values, 128 bytes); lane L lands at row
+  // 16 w + 8 i + L / 8, physical piece L % 8, holding logical piece
+  // (L % 8) ^ swz(row) -- the token tile's layout.
   uint32_t wboff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = 8 * wave + 4 * i + (lane >> 4);
-    const int64_t col = k0 + 8 * ((lane & 15) ^ wswz(row));
-    wboff[i] = col < K ? (uint32_t)(((int64_t)row * K + col) * 2) : kOOB;
+    if constexpr (NT) {
+      const int row = 16 * wave + 8 * i + (lane >> 3);
+      const int piece = (lane & 7) ^ swz(row);
+      const int64_t f = k0 + row;
+      wboff[i] = f < K ? (uint32_t)((f * N + piece * 8) * 2) : kOOB;
+    } else {
+      const int row = 8 * wave + 4 * i + (lane >> 4);
+      const int64_t col = k0 + 8 * ((lane & 15) ^ wswz(row));
+      wboff[i] = col < K ? (uint32_t)(((int64_t)row * K + col) * 2) : kOOB;
+    }
   }
   auto load_wbi = [&](int i, uint16_t* buf, int kb) {
-    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(kb) * kDxStepN * (uint32_t)K * 2u;
+    const uint32_t kbs = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
+    const uint32_t soff = NT ? kbs * (kDxStepN * 2) : kbs * kDxStepN * (uint32_t)K * 2u;
+    uint16_t* const dst = NT ? buf + (16 * wave + 8 * i) * kDxStepN : buf + (8 * wave + 4 * i) * kDxBK;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rwb, (__attribute__((address_space(3))) void*)(buf + (8 * wave + 4 * i) * kDxBK), 16,
-        wboff[i], soff, 0, 0);
+        rwb, (__attribute__((address_space(3))) void*)dst, 16, wboff[i], soff, 0, 0);
   };
   auto word = [](const DxWRegs& R, int t) -> uint32_t { return t == 0 ? R.p.x : R.p.y; };
   // NF4 level of the nibble at bits b .. b+3 of w.  ds_bpermute reads lane
@@ -212,6 +235,8 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
       wrd[t][half] = n * kDxBK + phys * 8 + (col & 7);
     }
   auto wfrag = [&](const uint16_t* buf, int t) -> bf16x8_t {
+    // NT: weight row 32 fg + c, whose swizzle equals that of row c
+    if constexpr (NT) return *reinterpret_cast<const bf16x8_t*>(buf + 32 * fg * kDxStepN + yrd[t]);
     const v4s_t lo = lds_read_tr16(buf + wrd[t][0]);
     const v4s_t hi = lds_read_tr16(buf + wrd[t][1]);
     typedef short v8s_t __attribute__((ext_vector_type(8)));
@@ -356,7 +381,14 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     for (int r0 = 0; r0 < g.r; r0 += 16) {
       const int rr = r0 + 8 * h;
       uint32_t av[4] = {0u, 0u, 0u, 0u};
-      if (kf < K && rr < g.r) {
+      if (NT && kf < K && rr < g.r) {
+        // s B, B = g.A here ([K, r]): eight consecutive r of weight row kf
+        const uint4 bv = *reinterpret_cast<const uint4*>(g.A + kf * g.r + rr);
+        const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          av[q] = pack_bf16x2(bf16_to_f32(bw[q] & 0xffffu) * g.s, bf16_to_f32(bw[q] >> 16) * g.s);
+      } else if (!NT && kf < K && rr < g.r) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
@@ -378,7 +410,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   // Accumulator i: lane holds token m = mw + 32 i + c and features
   // 8 (v / 4) + 4 h + (v % 4) of the wave's 32.
   const int64_t kw0 = k0 + 32 * fg;
-  if (g.mask == nullptr) {
+  if (NT || g.mask == nullptr) {
     adapter_into(acc);
   } else {
     f32x16_t ad[4];
@@ -438,6 +470,23 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
     hipLaunchKernelGGL(k_dx_nf4<true>, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
   else
     hipLaunchKernelGGL(k_dx_nf4<false>, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
+  return hipGetLastError();
+}
+
+// Forward on a bf16 weight wb ([N, K]): Y = X wb^T + s T B^T.
+hipError_t launch_fwd_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N, int64_t K,
+                           const uint16_t* T, const uint16_t* B, int r, float s, uint16_t* Y,
+                           hipStream_t st) {
+  if (!dx_nf4_supported(K)) return hipErrorInvalidValue;
+  DxArgs g{};
+  g.dY = X; g.M = (int)M; g.U = T; g.A = B; g.r = r; g.s = s; g.dX = Y;
+  g.w.N = N; g.w.K = K; g.w.bf16 = wb;
+  g.accumulate = 0;
+  g.mask = nullptr; g.keep_scale = 1.0f;
+  g.tiles_m = (int)((M + kDxBM - 1) / kDxBM);
+  g.tiles_k = (int)((N + kDxBK - 1) / kDxBK);
+  g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * K * 2, (double)kDxBK * K * 2);
+  hipLaunchKernelGGL((k_dx_nf4<true, true>), dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
   return hipGetLastError();
 }
 

@@ -44,8 +44,6 @@
 // bf16 results through LDS to the gate waves, which write
 // H = silu(G) U (the elementwise kernel's arithmetic on the same bf16 G and
 // U); G and U are written too, for the backward.
-#include <type_traits>
-
 #include "device_common.h"
 #include "kernels.h"
 
@@ -85,20 +83,16 @@ struct FwdArgs {
 };
 
 struct FwdWRegs { uint4 p; uint32_t code; float sc; };   // NF4: 32 weights + block constant
-struct FwdWRegsB { uint4 p[4]; };                          // bf16: 32 weights
 struct FwdBFrag { uint32_t d[4][4]; };   // [MFMA step][dword]
 
 __device__ __forceinline__ bf16x8_t as_frag(const uint32_t (&d)[4]) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
-// BF16W: the base weight is plain bf16 (g.w.bf16) and there is nothing to
-// decode: the same kernel with the dequantisation switched off.
-template <bool BF16W, bool GATED = false>
+template <bool GATED = false>
 __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
-  static_assert(!(BF16W && GATED), "the gated variant takes NF4 weights");
-  using WRegs = std::conditional_t<BF16W, FwdWRegsB, FwdWRegs>;
-  constexpr int kWLoads = BF16W ? 4 : 3;          // weight loads per step
+  using WRegs = FwdWRegs;
+  constexpr int kWLoads = 3;                      // weight loads per step
   constexpr int kLoads = 8 + kWLoads;             // global loads per step
   // Tables first (low LDS addresses fit the instructions' offset field),
   // then the X buffers as four separate objects, so that the compiler can
@@ -124,7 +118,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   const NF4Weight W = upw ? g.w2 : g.w;
   const int64_t K = W.K, N = W.N, nkb = K / kBlock;
   const int nk = (int)nkb;
-  const float mean = BF16W ? 0.0f : W.mean[0];
+  const float mean = W.mean[0];
 
   // X tile loads: wave w, load i fills rows 64 w + 8 i .. +7 (1 KB of LDS);
   // lane L lands at LDS offset 16 L, i.e. row 64 w + 8 i + L / 8, physical
@@ -167,21 +161,14 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
         rx, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * j) * kXRow), 16,
         xoff[j], k * (kBlock * 2), 0, 0);
   };
-  // bf16 weight: the lane's 32 weights of a step are 64 contiguous bytes.
-  const __amdgpu_buffer_rsrc_t rb = rsrc_whole(W.bf16, (uint32_t)(BF16W ? N * K * 2 : 0));
-  const uint32_t boff = nvalid ? (uint32_t)((nrow * K + 32 * h) * 2) : kOOB;
   auto load_wj = [&](int j, WRegs& R, int kb) {
     const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
-    if constexpr (BF16W) {
-      R.p[j] = bload128s(rb, boff == kOOB ? kOOB : boff + 16u * j, k * (kBlock * 2));
-    } else {
-      if (j == 0)
-        R.p = bload128s(rp, poff, k * (kBlock / 2));
-      else if (j == 1)
-        R.code = bload8s(rc, coff, k);
-      else
-        R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + k) / kDQBlock) * 4u));
-    }
+    if (j == 0)
+      R.p = bload128s(rp, poff, k * (kBlock / 2));
+    else if (j == 1)
+      R.code = bload8s(rc, coff, k);
+    else
+      R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + k) / kDQBlock) * 4u));
   };
   auto load_x = [&](uint16_t* buf, int kb) {
 #pragma unroll
@@ -236,7 +223,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   }
   // Only step 0's loads must have arrived (those of steps 1 and 2 may still
   // be in flight) before the barrier publishes X(0).
-  if constexpr (!BF16W) decode_all(wr[0], bf[0]);
+  decode_all(wr[0], bf[0]);
   __builtin_amdgcn_s_waitcnt(wait_vm(2 * kLoads, 0));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -260,8 +247,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     // not queue 44 loads at the address unit before their first MFMA.
     const int kload = min(kb + 3, nk - 1);
     uint16_t* const xload = xbuf[(P + 3) % kXBufs];
-    float q8v = 0.0f;
-    if constexpr (!BF16W) q8v = q8[wdec.code];
+    const float q8v = q8[wdec.code];
     float ah = 0.0f;
     float lh[16], ll[16];
     uint32_t nh[4], nl[4];
@@ -269,15 +255,12 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
       const int t = u / 8, i = u % 8;
-      if constexpr (BF16W)
-        acc[i] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, wr[P].p[t]), a[t & 1][i], acc[i]);
-      else
-        acc[i] = mfma_32x32x16(as_frag(bc.d[t]), a[t & 1][i], acc[i]);
+      acc[i] = mfma_32x32x16(as_frag(bc.d[t]), a[t & 1][i], acc[i]);
       if (u < 8) load_xj(u, xload, kload);
       else if (u < 8 + kWLoads) load_wj(u - 8, wload, kload);
       if (t < 3) a[(t + 1) & 1][i] = xfrag(xcur, i, t + 1);
       else a[0][i] = xfrag(xnext, i, 0);
-      if constexpr (!BF16W) {
+      {
         if (u < 16) {
           if (u % 4 == 0) {
             nh[u / 4] = hi4(word(wdec, u / 4));
@@ -409,23 +392,20 @@ hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, c
   g.tiles_n = (int)((wg.N + kFwdBN / 2 - 1) / (kFwdBN / 2));
   g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * wg.K * 2,
                         (double)kFwdBN * wg.K * 0.52);
-  hipLaunchKernelGGL((k_fwd_nf4<false, true>), dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
+  hipLaunchKernelGGL(k_fwd_nf4<true>, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
-  if (!fwd_nf4_supported(w.K)) return hipErrorInvalidValue;
+  if (!fwd_nf4_supported(w.K) || w.bf16) return hipErrorInvalidValue;
   FwdArgs g{};
   g.X = X; g.M = (int)M; g.w = w; g.T = T; g.B = B; g.r = r; g.s = s; g.Y = Y;
   g.tiles_m = (int)((M + kFwdBM - 1) / kFwdBM);
   g.tiles_n = (int)((w.N + kFwdBN - 1) / kFwdBN);
   g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * w.K * 2,
-                        (double)kFwdBN * w.K * (w.bf16 ? 2.0 : 0.52));
-  if (w.bf16)
-    hipLaunchKernelGGL(k_fwd_nf4<true>, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
-  else
-    hipLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
+                        (double)kFwdBN * w.K * 0.52);
+  hipLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -802,6 +802,13 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   if (!Xa) Xa = X;
   if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st, Xa);
   QLK_TRY(compute_T(Xa, M, K, A, r, T, st));
+  // A bf16 base: the dX kernel's forward form.
+  if (w.bf16 && dx_nf4_supported(K) && !QLK_FWD_TILE_ENGINE) {
+    timer_begin(TK_FWD_GEMM, st);
+    const hipError_t e = launch_fwd_bf16(X, M, w.bf16, N, K, T, B, r, s, Y, st);
+    timer_end(TK_FWD_GEMM, st);
+    return e;
+  }
   GemmArgs g{};
   g.a1 = opnd(X, K, (int)M, M);
   g.b1 = opnd(nullptr, 0, (int)N, 0);

@@ -123,6 +123,11 @@ hipError_t launch_dx_adapter_masked(const uint16_t* U, const uint16_t* A, int64_
 hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W,
                                      int r, uint16_t* out, const NF4Weight& w, uint16_t* wout,
                                      hipStream_t st);
+// Y = X wb^T + s T B^T on a bf16 base weight wb [N, K] (the dX kernel in its
+// forward form), for K a multiple of 256.
+hipError_t launch_fwd_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N, int64_t K,
+                           const uint16_t* T, const uint16_t* B, int r, float s, uint16_t* Y,
+                           hipStream_t st);
 // out[M, r] (bf16) = S[M, C] W^T with W = [r, C] or, transposed, [C, r].
 hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, bool transposed,
                          int r, uint16_t* out, hipStream_t st);

@@ -169,9 +169,11 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K
  * QLoRA, where QLoRA trains 20-40 % slower per step because of the
  * dequantisation in every forward pass (aigrafen.se "QLoRA", paragraph
  * "Priset"; llm-compass "QLoRA", 与 baseline 对比 table, row 训练速度).  The
- * same kernels run with the dequantisation switched off; everything else
- * (adapter branch, reductions, tolerances, workspace size) is as in
- * qlora_linear_fwd / qlora_linear_bwd, with W_hat = W.  Requires W under
+ * backward runs the same kernels with the dequantisation switched off, the
+ * forward (K a multiple of 256, more than 16 tokens) the dX kernel's forward
+ * form, a bf16 GEMM; everything else (adapter branch, reductions,
+ * tolerances, workspace size) is as in qlora_linear_fwd / qlora_linear_bwd,
+ * with W_hat = W.  Requires W under
  * 2 GiB (2 N K bytes) in addition to their shape rules. */
 int qlora_linear_fwd_bf16(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint16_t* W,
                           const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
