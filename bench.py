@@ -908,6 +908,30 @@ def summarize(out: str):
         fh.write("\n".join(md) + "\n")
 
 
+def library_gemm(torch, args, M=2048, N=4096, K=4096):
+    """Context only, not part of the path: the vendor library's bf16 GEMM on
+    the same contraction shapes with a plain bf16 weight (nothing to decode).
+    X W^T is the forward's contraction, dY W the dX kernel's."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+    X = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    W = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    dY = torch.randn(M, N, device="cuda", dtype=torch.bfloat16, generator=g)
+    out = {"shape": [M, N, K], "op": "torch.matmul (hipBLASLt), bf16 operands"}
+    for name, f in (("X_Wt", lambda: X @ W.t()), ("dY_W", lambda: dY @ W)):
+        for _ in range(args.warmup):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        out[name] = {"avg_us": round(us, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -923,6 +947,9 @@ def main():
                     help="skip the bf16-base and dropout steps (counter runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on plain bf16 operands of the "
+                         "2048 x 4096 x 4096 layer's two contractions, for context")
     ap.add_argument("--profile-commands", metavar="OUT",
                     help="print the rocprofv3 runs behind profiles/ (one per line) and exit")
     ap.add_argument("--summarize", metavar="OUT",
@@ -973,6 +1000,9 @@ def main():
         err("[bench] standalone quantize / double quant / dequant ...")
         standalone = run_standalone(args, q, torch, lib, ev)
         err(f"[bench] standalone {standalone}")
+    library = library_gemm(torch, args) if args.library_gemm else None
+    if library:
+        err(f"[bench] library bf16 GEMM {library}")
     cpu = None
     if not args.no_cpu_baseline:
         err("[bench] CPU oracle baseline ...")
@@ -986,6 +1016,8 @@ def main():
                 lora_dropout=lin["lora_dropout"],
                 gemv=gemv, mlp_gate_up=mlp, blocks=blocks, standalone=standalone,
                 source_hash=source_hash())
+    if library:
+        line["context_library_bf16_gemm"] = library
     print(json.dumps(line), flush=True)
 
 
