@@ -28,22 +28,34 @@ __device__ __forceinline__ void nf4_dequant_block(const uint8_t* __restrict__ pa
   const int64_t w0 = (blk_index * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 256;  // first word of the wave
   const float mu = mean[0];
   const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed);
+  // All four rounds' loads first (an out-of-range word loads word 0 and is
+  // not stored), so that a wave has its twelve loads in flight together.
+  uint32_t p[4], cd[4];
+  float sc[4];
+  bool ok[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t wd = w0 + 64 * q + lane;   // packed word: weights 8 wd .. 8 wd + 7
-    if (wd >= nwords) break;
-    const uint32_t p = pw[wd];
-    const int64_t blk = wd >> 3;             // 8 words per block of 64
-    const float ah = absmax_decode(codes[blk], scales[blk / kDQBlock], mu);
+    ok[q] = wd < nwords;
+    const int64_t wc = ok[q] ? wd : 0;
+    const int64_t blk = wc >> 3;             // 8 words per block of 64
+    p[q] = pw[wc];
+    cd[q] = codes[blk];
+    sc[q] = scales[blk / kDQBlock];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (!ok[q]) continue;
+    const float ah = absmax_decode(cd[q], sc[q], mu);
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t byte = (p >> (j * 8)) & 0xffu;
+      const uint32_t byte = (p[q] >> (j * 8)) & 0xffu;
       const float a = q4[byte >> 4] * ah;    // element 2j: high nibble
       const float b = q4[byte & 15u] * ah;
       o[j] = pack_bf16x2(a, b);
     }
-    reinterpret_cast<uint4*>(out)[wd] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4*>(out)[w0 + 64 * q + lane] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
