@@ -7,9 +7,10 @@
 // The contraction runs over n, the weight's row index, so the dequantised
 // weight is needed transposed.  One workgroup computes a 256 x 128 tile of
 // dX (tokens x input features) with eight waves, two per SIMD: wave w owns
-// input features 32 (w % 4) .. +31 of the tile and tokens 128 (w / 4) .. +127,
+// input features 64 (w % 2) .. +63 of the tile and tokens 64 (w / 2) .. +63,
 // four accumulators of v_mfma_f32_32x32x16_bf16, each a 32 (features) x 32
-// (tokens) block of dX^T.  At one wave per SIMD an MFMA and the same wave's
+// (tokens) block of dX^T: an MFMA step reads two weight and two dY operands
+// for its four MFMAs.  At one wave per SIMD an MFMA and the same wave's
 // other instructions barely overlap; the second wave issues its MFMAs while
 // the first decodes, reads LDS or waits.
 //
@@ -53,9 +54,9 @@ namespace qlk {
 
 constexpr int kDxBM = 256;                 // tokens per tile
 constexpr int kDxWaves = 8;
-constexpr int kDxWaveK = 32;               // features per wave
-constexpr int kDxWaveM = 128;              // tokens per wave
-constexpr int kDxBK = 4 * kDxWaveK;        // features per tile
+constexpr int kDxWaveK = 64;               // features per wave
+constexpr int kDxWaveM = 64;               // tokens per wave
+constexpr int kDxBK = 2 * kDxWaveK;        // features per tile
 constexpr int kDxStepN = 64;               // contraction (weight rows) per step
 constexpr int kDyTile = kDxBM * kDxStepN;  // elements per dY buffer
 constexpr int kWTile = kDxStepN * kDxBK;   // elements per weight buffer
@@ -101,7 +102,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: LDS bases, offsets
   const int c = lane & 31, h = lane >> 5;
-  const int fg = wave & 3, th = wave >> 2;   // feature group, token half
+  const int fg = wave & 1, tq = wave >> 1;   // feature half, token quarter
 
   int tm, tk;
   tile_coords(blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
@@ -139,9 +140,9 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) load_dyi(i, buf, kb);
   };
-  // Operand of token block i (32 tokens) of this wave's half, MFMA step t.
+  // Operand of token block i (32 tokens) of this wave's quarter, MFMA step t.
   auto yfrag = [&](const uint16_t* buf, int i, int t) -> bf16x8_t {
-    return *reinterpret_cast<const bf16x8_t*>(buf + (kDxWaveM * th + 32 * i) * kDxStepN + yrd[t]);
+    return *reinterpret_cast<const bf16x8_t*>(buf + (kDxWaveM * tq + 32 * i) * kDxStepN + yrd[t]);
   };
 
   // Weight decode: lane L of wave w owns row n = L of the step and features
@@ -222,23 +223,27 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     const int phys = (2 * wave + q) ^ wswz(wrow);
     *reinterpret_cast<uint4*>(buf + wrow * kDxBK + phys * 8) = v;
   };
-  // Transpose-read operand: features c of the wave's 32, rows 16t + 8h + 0..7.
+  // Transpose-read operand of feature block j (32 features) of the wave's
+  // 64: features c, rows 16t + 8h + 0..7.
   const int grp = lane >> 4, gi = lane & 15;
-  int wrd[4][2];
+  int wrd[2][4][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int n = 16 * t + 8 * (grp >> 1) + 4 * half + (gi >> 2);
-      const int col = 32 * fg + 16 * (grp & 1) + 4 * (gi & 3);
-      const int phys = (col / 8) ^ wswz(n);
-      wrd[t][half] = n * kDxBK + phys * 8 + (col & 7);
-    }
-  auto wfrag = [&](const uint16_t* buf, int t) -> bf16x8_t {
-    // NT: weight row 32 fg + c, whose swizzle equals that of row c
-    if constexpr (NT) return *reinterpret_cast<const bf16x8_t*>(buf + 32 * fg * kDxStepN + yrd[t]);
-    const v4s_t lo = lds_read_tr16(buf + wrd[t][0]);
-    const v4s_t hi = lds_read_tr16(buf + wrd[t][1]);
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int n = 16 * t + 8 * (grp >> 1) + 4 * half + (gi >> 2);
+        const int col = kDxWaveK * fg + 32 * j + 16 * (grp & 1) + 4 * (gi & 3);
+        const int phys = (col / 8) ^ wswz(n);
+        wrd[j][t][half] = n * kDxBK + phys * 8 + (col & 7);
+      }
+  auto wfrag = [&](const uint16_t* buf, int j, int t) -> bf16x8_t {
+    // NT: weight row 64 fg + 32 j + c, whose swizzle equals that of row c
+    if constexpr (NT)
+      return *reinterpret_cast<const bf16x8_t*>(buf + (kDxWaveK * fg + 32 * j) * kDxStepN + yrd[t]);
+    const v4s_t lo = lds_read_tr16(buf + wrd[j][t][0]);
+    const v4s_t hi = lds_read_tr16(buf + wrd[j][t][1]);
     typedef short v8s_t __attribute__((ext_vector_type(8)));
     const v8s_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8_t, v);
@@ -265,7 +270,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   // weight of step j in wr[j % 4] from its load (step j-3) to its decode
   // (step j-1) into weight buffer j % 2, read during step j.
   DxWRegs wr[4];
-  bf16x8_t b[2][4];   // dY operands
+  bf16x8_t b[2][2];   // dY operands [MFMA step parity][token block]
   __syncthreads();
   if constexpr (BF16W) {
     // W(0) into weight buffer 0, then dY(0..2); W(j+1) is copied during step j.
@@ -289,7 +294,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   }
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) b[0][i] = yfrag(dyb[0], i, 0);
+  for (int i = 0; i < 2; ++i) b[0][i] = yfrag(dyb[0], i, 0);
 
   // One step: 16 MFMA slots (t = u / 4 of the 64-row step, token block
   // i = u % 4); the operands of the next MFMA step, the decode of the next
@@ -311,16 +316,18 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     // at the address unit before their first MFMA.
     const int kload = min(kb + 3, nsteps - 1);
     uint16_t* const yload = dyb[(P + 3) % 4];
-    bf16x8_t a[2];
-    a[0] = wfrag(wcur, 0);
+    bf16x8_t a[2][2];   // weight operands [MFMA step parity][feature block]
+    a[0][0] = wfrag(wcur, 0, 0);
+    a[0][1] = wfrag(wcur, 1, 0);
     float ah = 0.0f;
     float lh[8], ll[8];
     uint32_t o[8];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
+      // accumulator i: feature block i / 2, token block i % 2
       const int t = u / 4, i = u % 4;
-      acc[i] = mfma_32x32x16(a[t & 1], b[t & 1][i], acc[i]);
+      acc[i] = mfma_32x32x16(a[t & 1][i >> 1], b[t & 1][i & 1], acc[i]);
       if constexpr (BF16W) {
         // W(kb+1) first (it must be complete at this step's end), then dY(kb+3)
         if (u < 2) load_wbi(u, wnext, min(kb + 1, nsteps - 1));
@@ -329,7 +336,11 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
         if (u < 4) load_dyi(u, yload, kload);
         else if (u < 7) load_wj(u - 4, wload, kload);
       }
-      if (i == 0 && t < 3) a[(t + 1) & 1] = wfrag(wcur, t + 1);
+      // operands of MFMA step t+1, one per slot (the other parity)
+      if (t < 3) {
+        if (i < 2) a[(t + 1) & 1][i] = wfrag(wcur, i, t + 1);
+        else b[(t + 1) & 1][i - 2] = yfrag(ycur, i - 2, t + 1);
+      }
       if constexpr (!BF16W) {
         if (u < 4) {
 #pragma unroll
@@ -349,19 +360,18 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
           wstore(wnext, q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
         }
       }
-      if (t < 3) b[(t + 1) & 1][i] = yfrag(ycur, i, t + 1);
       if (u == 15) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[0][j] = yfrag(ynext, j, 0);
+        for (int j = 0; j < 2; ++j) b[0][j] = yfrag(ynext, j, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // Before step kb+1: dY(kb+2) (loaded during step kb-1) in LDS from every
     // wave (at most this step's 7 global loads outstanding; with a bf16
     // weight, at most this step's 4 dY loads, so that W(kb+1) has arrived)
-    // and this wave's decoded weight stores done (at most the 4 operand
-    // reads of slot 15 outstanding), then the barrier.
-    __builtin_amdgcn_s_waitcnt(BF16W ? dx_wait(4, 4) : dx_wait(7, 4));
+    // and this wave's decoded weight stores done (at most the 2 operand
+    // reads of slot 15, issued after them, outstanding), then the barrier.
+    __builtin_amdgcn_s_waitcnt(BF16W ? dx_wait(4, 2) : dx_wait(7, 2));
     __builtin_amdgcn_s_barrier();
   };
   for (int kb = 0; kb < nsteps; kb += kDxUnroll) {
@@ -375,41 +385,47 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   // Adapter term: (s A)^T U^T over r in steps of 16, into the main
   // accumulators, or -- with a dropout mask -- into separate ones that are
   // masked and scaled before they are added.
-  const int64_t kf = k0 + 32 * fg + c;   // this lane's feature (operand row)
-  const int mw = m0 + kDxWaveM * th;     // first token of this wave
+  const int64_t kw = k0 + kDxWaveK * fg;   // first feature of this wave
+  const int mw = m0 + kDxWaveM * tq;       // first token of this wave
   auto adapter_into = [&](f32x16_t (&dst)[4]) {
     for (int r0 = 0; r0 < g.r; r0 += 16) {
       const int rr = r0 + 8 * h;
-      uint32_t av[4] = {0u, 0u, 0u, 0u};
-      if (NT && kf < K && rr < g.r) {
-        // s B, B = g.A here ([K, r]): eight consecutive r of weight row kf
-        const uint4 bv = *reinterpret_cast<const uint4*>(g.A + kf * g.r + rr);
-        const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      bf16x8_t uop[2];   // U rows of the two token blocks
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          av[q] = pack_bf16x2(bf16_to_f32(bw[q] & 0xffffu) * g.s, bf16_to_f32(bw[q] >> 16) * g.s);
-      } else if (!NT && kf < K && rr < g.r) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
-          const float hi = bf16_to_f32(g.A[(int64_t)(rr + 2 * q + 1) * K + kf]) * g.s;
-          av[q] = pack_bf16x2(lo, hi);
-        }
-      }
-      const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mw + 32 * i + c;
+      for (int ti = 0; ti < 2; ++ti) {
+        const int m = mw + 32 * ti + c;
         uint4 uv = make_uint4(0, 0, 0, 0);
         if (m < g.M && rr < g.r) uv = *reinterpret_cast<const uint4*>(g.U + (int64_t)m * g.r + rr);
-        dst[i] = mfma_32x32x16(afr, __builtin_bit_cast(bf16x8_t, uv), dst[i]);
+        uop[ti] = __builtin_bit_cast(bf16x8_t, uv);
+      }
+#pragma unroll
+      for (int fi = 0; fi < 2; ++fi) {
+        const int64_t kf = kw + 32 * fi + c;   // this lane's feature (operand row)
+        uint32_t av[4] = {0u, 0u, 0u, 0u};
+        if (NT && kf < K && rr < g.r) {
+          // s B, B = g.A here ([K, r]): eight consecutive r of weight row kf
+          const uint4 bv = *reinterpret_cast<const uint4*>(g.A + kf * g.r + rr);
+          const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            av[q] = pack_bf16x2(bf16_to_f32(bw[q] & 0xffffu) * g.s, bf16_to_f32(bw[q] >> 16) * g.s);
+        } else if (!NT && kf < K && rr < g.r) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
+            const float hi = bf16_to_f32(g.A[(int64_t)(rr + 2 * q + 1) * K + kf]) * g.s;
+            av[q] = pack_bf16x2(lo, hi);
+          }
+        }
+        const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) dst[2 * fi + ti] = mfma_32x32x16(afr, uop[ti], dst[2 * fi + ti]);
       }
     }
   };
 
-  // Accumulator i: lane holds token m = mw + 32 i + c and features
-  // 8 (v / 4) + 4 h + (v % 4) of the wave's 32.
-  const int64_t kw0 = k0 + 32 * fg;
+  // Accumulator i: lane holds token m = mw + 32 (i % 2) + c and features
+  // kw + 32 (i / 2) + 8 (v / 4) + 4 h + (v % 4).
   if (NT || g.mask == nullptr) {
     adapter_into(acc);
   } else {
@@ -419,11 +435,12 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) ad[i][v] = 0.0f;
     adapter_into(ad);
-    // The wave's 32 features start at a multiple of 32 and K % 64 == 0, so a
-    // token's 32 mask bits are one word; feature offset 8 (v / 4) + 4 h + v % 4.
+    // A feature block's 32 features start at a multiple of 32 and K % 64 == 0,
+    // so a token's 32 mask bits are one word; feature offset 8 (v / 4) + 4 h + v % 4.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = mw + 32 * i + c;
+      const int m = mw + 32 * (i & 1) + c;
+      const int64_t kw0 = kw + 32 * (i >> 1);
       const uint32_t bits = (m < g.M && kw0 < K) ? g.mask[((int64_t)m * K + kw0) >> 5] : 0u;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -434,12 +451,12 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = mw + 32 * i + c;
+    const int m = mw + 32 * (i & 1) + c;
     if (m >= g.M) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t k = kw0 + 8 * q + 4 * h;
-      if (k >= K) continue;   // K % 64 == 0
+      const int64_t k = kw + 32 * (i >> 1) + 8 * q + 4 * h;
+      if (k >= K) continue;   // K % 8 == 0: a group of four is all in or all out
       uint2* dst = reinterpret_cast<uint2*>(g.dX + (int64_t)m * K + k);
       float v0 = acc[i][4 * q + 0], v1 = acc[i][4 * q + 1], v2 = acc[i][4 * q + 2], v3 = acc[i][4 * q + 3];
       if (g.accumulate) {
