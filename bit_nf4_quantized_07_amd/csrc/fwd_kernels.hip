@@ -18,8 +18,10 @@
 //    (16 rows x 16 bytes per bank cycle) conflict-free.
 //  * The NF4 weight never goes through LDS: each lane loads the 16 packed
 //    bytes (32 weights) of its weight row that its half of the MFMA operand
-//    covers, plus the block's 8-bit code and second-level scale, and decodes
-//    them straight into the bf16 MFMA operand.  Every weight is decoded once.
+//    covers, and decodes them straight into the bf16 MFMA operand; the 8-bit
+//    codes of four consecutive blocks come in one 4-byte load, with their
+//    shared second-level scale, once every four steps.  Every weight is
+//    decoded once.
 //    The decode is the standalone dequantiser's arithmetic:
 //      a_hat = fp32(fp32(Q8[code] * scale) + mean),
 //      w_hat = bf16(fp32(Q4[nibble] * a_hat)),
@@ -82,7 +84,7 @@ struct FwdArgs {
   uint16_t* H;
 };
 
-struct FwdWRegs { uint4 p; uint32_t code; float sc; };   // NF4: 32 weights + block constant
+struct FwdWRegs { uint4 p; };   // NF4: 32 packed weights
 struct FwdBFrag { uint32_t d[4][4]; };   // [MFMA step][dword]
 
 __device__ __forceinline__ bf16x8_t as_frag(const uint32_t (&d)[4]) {
@@ -92,8 +94,10 @@ __device__ __forceinline__ bf16x8_t as_frag(const uint32_t (&d)[4]) {
 template <bool GATED = false>
 __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   using WRegs = FwdWRegs;
-  constexpr int kWLoads = 3;                      // weight loads per step
-  constexpr int kLoads = 8 + kWLoads;             // global loads per step
+  // Global loads per step: 8 of X and the packed weights, plus, once every
+  // four steps (P == 1), the codes and the scale of the next four blocks.
+  constexpr int kLoads = 9;
+  constexpr int kRunLoads = 2;
   // Tables first (low LDS addresses fit the instructions' offset field),
   // then the X buffers as four separate objects, so that the compiler can
   // tell that a load into one buffer does not alias reads of another.
@@ -161,22 +165,26 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
         rx, (__attribute__((address_space(3))) void*)(buf + (64 * wave + 8 * j) * kXRow), 16,
         xoff[j], k * (kBlock * 2), 0, 0);
   };
-  auto load_wj = [&](int j, WRegs& R, int kb) {
+  auto load_p = [&](WRegs& R, int kb) {
     const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
+    R.p = bload128s(rp, poff, k * (kBlock / 2));
+  };
+  // The 8-bit codes of blocks kb4 .. kb4+3 of the lane's row (kb4 a multiple
+  // of 4 and K / 64 too, so the 4 bytes are aligned) and their second-level
+  // scale (a group of 256 blocks starts at a multiple of 4, so the four
+  // blocks share it): one load of each per four steps.
+  uint32_t crun_cur = 0, crun_next = 0;
+  float srun_cur = 0.0f, srun_next = 0.0f;
+  auto load_run_j = [&](int j, int kb4) {
+    const uint32_t k = (uint32_t)__builtin_amdgcn_readfirstlane(kb4);
     if (j == 0)
-      R.p = bload128s(rp, poff, k * (kBlock / 2));
-    else if (j == 1)
-      R.code = bload8s(rc, coff, k);
+      crun_next = bload32s(rc, coff, k);
     else
-      R.sc = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + k) / kDQBlock) * 4u));
+      srun_next = __uint_as_float(bload32(rsc, coff == kOOB ? kOOB : ((coff + k) / kDQBlock) * 4u));
   };
   auto load_x = [&](uint16_t* buf, int kb) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) load_xj(j, buf, kb);
-  };
-  auto load_w = [&](WRegs& R, int kb) {
-#pragma unroll
-    for (int j = 0; j < kWLoads; ++j) load_wj(j, R, kb);
   };
   auto word = [](const FwdWRegs& R, int t) -> uint32_t {
     return t == 0 ? R.p.x : t == 1 ? R.p.y : t == 2 ? R.p.z : R.p.w;
@@ -194,8 +202,8 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   };
   auto hi4 = [](uint32_t w) { return (w >> 2) & 0x3C3C3C3Cu; };
   auto lo4 = [](uint32_t w) { return (w << 2) & 0x3C3C3C3Cu; };
-  auto decode_all = [&](const FwdWRegs& R, FwdBFrag& F) {
-    const float ah = absmax_decode_tab((int)R.code, R.sc, mean, q8);
+  auto decode_all = [&](const FwdWRegs& R, FwdBFrag& F, uint32_t code, float sc) {
+    const float ah = absmax_decode_tab((int)code, sc, mean, q8);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -219,11 +227,17 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     load_x(xbuf[j], min(j, nk - 1));
-    load_w(wr[j], min(j, nk - 1));
+    load_p(wr[j], min(j, nk - 1));
+    if (j == 0) {
+      load_run_j(0, 0);
+      load_run_j(1, 0);
+    }
   }
+  crun_cur = crun_next;
+  srun_cur = srun_next;
   // Only step 0's loads must have arrived (those of steps 1 and 2 may still
   // be in flight) before the barrier publishes X(0).
-  decode_all(wr[0], bf[0]);
+  decode_all(wr[0], bf[0], crun_cur & 0xffu, srun_cur);
   __builtin_amdgcn_s_waitcnt(wait_vm(2 * kLoads, 0));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -239,15 +253,23 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     // kb % 4 == P: the loop starts at 0 and steps by 4
     const uint16_t* xcur = xbuf[P];
     const uint16_t* xnext = xbuf[(P + 1) % kXBufs];
+    // Block kb+1 is decoded here: byte (kb+1) % 4 of its run, which is the
+    // next run at P == 3.
+    const uint32_t dcode = ((P == 3 ? crun_next : crun_cur) >> (8 * ((P + 1) % 4))) & 0xffu;
+    const float dsc = P == 3 ? srun_next : srun_cur;
+    // Run loads at P == 1: blocks kb+3 .. kb+6 (kb+3 is a multiple of 4), or
+    // the last run once those are past the end.
+    constexpr int kStepLoads = kLoads + (P == 1 ? kRunLoads : 0);
+    const int krun = min(kb + 3, nk - 4);
 
-    // 3 weight loads, then 8 X loads into the buffer of step kb-1 (its
-    // operand reads by this wave completed before the last barrier).
-    // This step's 11 loads (for step kb+3) go out one per MFMA slot 0..10,
+    // 8 X loads into the buffer of step kb-1 (its operand reads by this
+    // wave completed before the last barrier), then the weight loads.  This
+    // step's 9 loads (11 at P == 1; for step kb+3) go out one per MFMA slot,
     // so that the workgroup's waves, released together by the barrier, do
-    // not queue 44 loads at the address unit before their first MFMA.
+    // not queue all their loads at the address unit before their first MFMA.
     const int kload = min(kb + 3, nk - 1);
     uint16_t* const xload = xbuf[(P + 3) % kXBufs];
-    const float q8v = q8[wdec.code];
+    const float q8v = q8[dcode];
     float ah = 0.0f;
     float lh[16], ll[16];
     uint32_t nh[4], nl[4];
@@ -257,7 +279,8 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
       const int t = u / 8, i = u % 8;
       acc[i] = mfma_32x32x16(as_frag(bc.d[t]), a[t & 1][i], acc[i]);
       if (u < 8) load_xj(u, xload, kload);
-      else if (u < 8 + kWLoads) load_wj(u - 8, wload, kload);
+      else if (u == 8) load_p(wload, kload);
+      else if (P == 1 && u < 9 + kRunLoads) load_run_j(u - 9, krun);
       if (t < 3) a[(t + 1) & 1][i] = xfrag(xcur, i, t + 1);
       else a[0][i] = xfrag(xnext, i, 0);
       {
@@ -271,7 +294,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
         }
         if (u == 2) {
 #pragma clang fp contract(off)
-          const float p = q8v * wdec.sc;
+          const float p = q8v * dsc;
           ah = p + mean;
         }
         if (u >= 16) {
@@ -284,8 +307,12 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     // X(kb+2) (loaded during step kb-1) must be in LDS, from every wave,
     // before step kb+1 reads it: wait until at most this step's loads are
     // outstanding, then barrier.
-    __builtin_amdgcn_s_waitcnt(wait_vm(kLoads, 0xF));
+    __builtin_amdgcn_s_waitcnt(wait_vm(kStepLoads, 0xF));
     __builtin_amdgcn_s_barrier();
+    if constexpr (P == 3) {
+      crun_cur = crun_next;
+      srun_cur = srun_next;
+    }
   };
   for (int kb = 0; kb < nk; kb += kFwdUnroll) {
     step(std::integral_constant<int, 0>(), kb);
