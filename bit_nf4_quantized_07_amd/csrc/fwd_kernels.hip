@@ -37,7 +37,8 @@
 //  * The adapter term s T B^T is a last contraction over r into the same
 //    accumulators (the up-projection fused into the base GEMM).
 //  * The accumulator layout gives each lane four consecutive weight rows of
-//    one token, so Y is written 8 bytes at a time.
+//    one token (8 bytes of Y); the finished tile goes out through LDS so that
+//    every store instruction writes whole 256-byte row segments of Y.
 //
 // Gated variant (the fused gate/up projections of a SiLU-gated MLP): each
 // wave's weight rows come from one weight, so waves 0-1 take 64 rows of the
@@ -350,19 +351,58 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
 
   // Accumulator i: lane holds token m = m0 + 32 i + c and weight rows
   // 8 (v / 4) + 4 h + (v % 4) of the wave's 32; four consecutive rows are
-  // one 8-byte store.
+  // one 8-byte piece of Y.
   uint16_t* const Yp = upw ? g.Y2 : g.Y;
   uint32_t ob[8][4][2];   // the bf16 results, kept for the gated epilogue
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + 32 * i + c;
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t n = nw0 + 8 * q + 4 * h;
       ob[i][q][0] = pack_bf16x2(acc[i][4 * q + 0], acc[i][4 * q + 1]);
       ob[i][q][1] = pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3]);
-      if (m >= g.M || n >= N) continue;   // N % 8 == 0: a group of four is all in or all out
-      *reinterpret_cast<uint2*>(Yp + (int64_t)m * N + n) = make_uint2(ob[i][q][0], ob[i][q][1]);
+    }
+  if constexpr (!GATED) {
+    // The tile goes out through LDS (the X buffers are free now): rows of
+    // 128 weight rows x 2 bytes, tokens 0..127 in xs0 and 128..255 in xs1,
+    // the 16-byte pieces of row t XOR-swizzled by t & 15 (conflict-free
+    // writes of the lanes' 8-byte pieces and reads of whole rows); then each
+    // thread stores 16-byte pieces, a wave four whole 256-byte row segments
+    // per store instruction.
+    __syncthreads();   // every wave's loads into the X buffers have landed
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t* const st = i < 4 ? xs0 : xs1;
+      const int row = 32 * (i & 3) + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int piece = (4 * wave + q) ^ (row & 15);
+        *reinterpret_cast<uint2*>(st + row * kFwdBN + piece * 8 + 4 * h) =
+            make_uint2(ob[i][q][0], ob[i][q][1]);
+      }
+    }
+    __syncthreads();
+    const int64_t n0 = (int64_t)tn * kFwdBN;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int gidx = 256 * j + tid;          // 16-byte piece of the tile
+      const int row = gidx >> 4, piece = gidx & 15;
+      const uint16_t* ld = (row < 128 ? xs0 : xs1) + (row & 127) * kFwdBN;
+      const uint4 v = *reinterpret_cast<const uint4*>(ld + ((piece ^ (row & 15)) * 8));
+      const int m = m0 + row;
+      const int64_t n = n0 + 8 * piece;
+      if (m < g.M && n < N)   // N % 8 == 0: a piece is all in or all out
+        *reinterpret_cast<uint4*>(Yp + (int64_t)m * N + n) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + 32 * i + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = nw0 + 8 * q + 4 * h;
+        if (m >= g.M || n >= N) continue;   // N % 8 == 0: a group of four is all in or all out
+        *reinterpret_cast<uint2*>(Yp + (int64_t)m * N + n) = make_uint2(ob[i][q][0], ob[i][q][1]);
+      }
     }
   }
   if constexpr (GATED) {
