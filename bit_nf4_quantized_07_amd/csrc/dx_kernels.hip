@@ -34,7 +34,8 @@
 //  * The weight of step k+1 is decoded during step k into the second weight
 //    buffer; raw weight loads run three steps ahead.
 //  * The adapter term s U A is a last contraction over r into the same
-//    accumulators; each lane stores four consecutive features (8 bytes).
+//    accumulators.  The fp32 tile then goes out through the dY buffers, so
+//    that every store instruction writes whole 256-byte row segments of dX.
 //    With LoRA dropout on the adapter input the term is accumulated apart,
 //    multiplied by mask * 1/(1-p) per element, then added.
 //
@@ -449,23 +450,52 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
       }
     }
   }
+  // The fp32 tile goes out through LDS (the dY buffers are free now and hold
+  // it exactly: tokens 64 b .. 64 b + 63 in buffer b, rows of 128 features x
+  // 4 bytes, the 16-byte pieces of row t XOR-swizzled by t & 31); then each
+  // thread takes 8 consecutive features of a token (adds the old dX when
+  // accumulating, rounds once) and stores 16 bytes, a wave four whole
+  // 256-byte row segments of dX per store instruction.
+  __syncthreads();   // every wave's loads into the dY buffers have landed
+  {
+    float* const st = reinterpret_cast<float*>(tq == 0 ? dy0 : tq == 1 ? dy1 : tq == 2 ? dy2 : dy3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = mw + 32 * (i & 1) + c;
-    if (m >= g.M) continue;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * (i & 1) + c;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t k = kw + 32 * (i >> 1) + 8 * q + 4 * h;
-      if (k >= K) continue;   // K % 8 == 0: a group of four is all in or all out
-      uint2* dst = reinterpret_cast<uint2*>(g.dX + (int64_t)m * K + k);
-      float v0 = acc[i][4 * q + 0], v1 = acc[i][4 * q + 1], v2 = acc[i][4 * q + 2], v3 = acc[i][4 * q + 3];
-      if (g.accumulate) {
-        const uint2 old = *dst;
-        v0 += bf16_to_f32(old.x & 0xffffu); v1 += bf16_to_f32(old.x >> 16);
-        v2 += bf16_to_f32(old.y & 0xffffu); v3 += bf16_to_f32(old.y >> 16);
+      for (int q = 0; q < 4; ++q) {
+        const int piece = (16 * fg + 8 * (i >> 1) + 2 * q + h) ^ (row & 31);
+        *reinterpret_cast<float4*>(st + row * kDxBK + piece * 4) =
+            make_float4(acc[i][4 * q + 0], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
       }
-      *dst = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // piece 512 j + tid of the tile: token row 32 j + tid / 16, features
+    // 8 (tid % 16) .. +7; the row lies in buffer j / 2 at row 32 (j % 2) + tid / 16
+    const int rin = 32 * (j & 1) + (tid >> 4), op = tid & 15;
+    const int row = 64 * (j >> 1) + rin;
+    const float* ld = reinterpret_cast<const float*>(dyb[j >> 1]) + rin * kDxBK;
+    const float4 lo = *reinterpret_cast<const float4*>(ld + ((2 * op) ^ (rin & 31)) * 4);
+    const float4 hi = *reinterpret_cast<const float4*>(ld + ((2 * op + 1) ^ (rin & 31)) * 4);
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const int m = m0 + row;
+    const int64_t k = k0 + 8 * op;
+    if (m >= g.M || k >= K) continue;   // K % 8 == 0: a piece is all in or all out
+    uint4* dst = reinterpret_cast<uint4*>(g.dX + (int64_t)m * K + k);
+    if (g.accumulate) {
+      const uint4 old = *dst;
+      const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] += bf16_to_f32(ow[e] & 0xffffu);
+        v[2 * e + 1] += bf16_to_f32(ow[e] >> 16);
+      }
+    }
+    *dst = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
   }
 }
 
