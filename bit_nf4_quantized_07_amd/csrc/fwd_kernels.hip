@@ -394,52 +394,48 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
         *reinterpret_cast<uint4*>(Yp + (int64_t)m * N + n) = v;
     }
   } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + 32 * i + c;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = nw0 + 8 * q + 4 * h;
-        if (m >= g.M || n >= N) continue;   // N % 8 == 0: a group of four is all in or all out
-        *reinterpret_cast<uint2*>(Yp + (int64_t)m * N + n) = make_uint2(ob[i][q][0], ob[i][q][1]);
-      }
-    }
-  }
-  if constexpr (GATED) {
-    // Up waves (2, 3) hand their bf16 results to the gate waves (0, 1) with
-    // the same lane layout through the first X buffer: dword d of lane L of
-    // wave pair p at [d][p][L] (lane-contiguous, conflict-free).
-    uint32_t* const xch = reinterpret_cast<uint32_t*>(xs0);
-    __syncthreads();   // every wave is done with the X buffers
-    if (upw) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 2; ++e)
-            xch[((8 * i + 2 * q + e) * 2 + (wave & 1)) * 64 + lane] = ob[i][q][e];
-    }
-    __syncthreads();
-    if (!upw) {
+    // Gated: G (waves 0-1) and U (waves 2-3) go through LDS, each as 256
+    // token rows of 64 features x 2 bytes (G in xs0, U in xs1), the 16-byte
+    // pieces of row t XOR-swizzled by t & 7; then each thread takes matching
+    // 16-byte pieces of G and U, forms H = silu(G) U (the elementwise
+    // kernel's arithmetic on the same bf16 values) and stores all three, a
+    // wave eight whole 128-byte row segments of each per instruction.
+    __syncthreads();   // every wave's loads into the X buffers have landed
+    {
+      uint16_t* const st = upw ? xs1 : xs0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int m = m0 + 32 * i + c;
+        const int row = 32 * i + c;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t n = nw0 + 8 * q + 4 * h;
-          if (m >= g.M || n >= N) continue;
-          uint32_t hv[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const uint32_t gw = ob[i][q][e];
-            const uint32_t uw = xch[((8 * i + 2 * q + e) * 2 + (wave & 1)) * 64 + lane];
-            hv[e] = pack_bf16x2(silu_mul_f32(bf16_to_f32(gw & 0xffffu), bf16_to_f32(uw & 0xffffu)),
-                                silu_mul_f32(bf16_to_f32(gw >> 16), bf16_to_f32(uw >> 16)));
-          }
-          *reinterpret_cast<uint2*>(g.H + (int64_t)m * N + n) = make_uint2(hv[0], hv[1]);
+          const int piece = (4 * (wave & 1) + q) ^ (row & 7);
+          *reinterpret_cast<uint2*>(st + row * (kFwdBN / 2) + piece * 8 + 4 * h) =
+              make_uint2(ob[i][q][0], ob[i][q][1]);
         }
       }
+    }
+    __syncthreads();
+    const int64_t n0 = (int64_t)tn * (kFwdBN / 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int gidx = 256 * j + tid;          // 16-byte piece of the 256 x 64 tile
+      const int row = gidx >> 3, piece = gidx & 7;
+      const int off = row * (kFwdBN / 2) + ((piece ^ (row & 7)) * 8);
+      const uint4 gv = *reinterpret_cast<const uint4*>(xs0 + off);
+      const uint4 uv = *reinterpret_cast<const uint4*>(xs1 + off);
+      const int m = m0 + row;
+      const int64_t n = n0 + 8 * piece;
+      if (m >= g.M || n >= N) continue;   // N % 8 == 0: a piece is all in or all out
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+      uint32_t hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hv[e] = pack_bf16x2(silu_mul_f32(bf16_to_f32(gw[e] & 0xffffu), bf16_to_f32(uw[e] & 0xffffu)),
+                            silu_mul_f32(bf16_to_f32(gw[e] >> 16), bf16_to_f32(uw[e] >> 16)));
+      const int64_t o = (int64_t)m * N + n;
+      *reinterpret_cast<uint4*>(g.Y + o) = gv;
+      *reinterpret_cast<uint4*>(g.Y2 + o) = uv;
+      *reinterpret_cast<uint4*>(g.H + o) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     }
   }
 }
