@@ -83,6 +83,12 @@ struct FwdArgs {
   float s2;
   uint16_t* Y2;
   uint16_t* H;
+  // Split contraction (fewer tiles than the device has CUs): workgroup
+  // b + z tiles takes K-steps z kz_len .. +kz_len of tile b and writes its
+  // fp32 partial to part[z] ([M, N]); k_fwd_reduce adds the splits.
+  // kz_len == 0: one pass over K, Y written directly.
+  float* part;
+  int kz_len;
 };
 
 struct FwdWRegs { uint4 p; };   // NF4: 32 packed weights
@@ -116,13 +122,18 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   q8[tid] = dq_level(tid);
 
   int tm, tn;
-  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int zsplit = (int)blockIdx.x / ntiles;
+  tile_coords((int)blockIdx.x % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
   const int m0 = tm * kFwdBM;
   // This wave's weight (the up weight for waves 2-3 of the gated variant).
   const bool upw = GATED && wave >= 2;
   const NF4Weight W = upw ? g.w2 : g.w;
   const int64_t K = W.K, N = W.N, nkb = K / kBlock;
   const int nk = (int)nkb;
+  // this workgroup's K-steps (multiples of 4 at both ends)
+  const int kz0 = g.kz_len ? zsplit * g.kz_len : 0;
+  const int kz1 = g.kz_len ? min(nk, kz0 + g.kz_len) : nk;
   const float mean = W.mean[0];
 
   // X tile loads: wave w, load i fills rows 64 w + 8 i .. +7 (1 KB of LDS);
@@ -227,11 +238,11 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   __syncthreads();   // tables
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    load_x(xbuf[j], min(j, nk - 1));
-    load_p(wr[j], min(j, nk - 1));
+    load_x(xbuf[j], min(kz0 + j, kz1 - 1));
+    load_p(wr[j], min(kz0 + j, kz1 - 1));
     if (j == 0) {
-      load_run_j(0, 0);
-      load_run_j(1, 0);
+      load_run_j(0, kz0);
+      load_run_j(1, kz0);
     }
   }
   crun_cur = crun_next;
@@ -261,14 +272,14 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
     // Run loads at P == 1: blocks kb+3 .. kb+6 (kb+3 is a multiple of 4), or
     // the last run once those are past the end.
     constexpr int kStepLoads = kLoads + (P == 1 ? kRunLoads : 0);
-    const int krun = min(kb + 3, nk - 4);
+    const int krun = min(kb + 3, kz1 - 4);
 
     // 8 X loads into the buffer of step kb-1 (its operand reads by this
     // wave completed before the last barrier), then the weight loads.  This
     // step's 9 loads (11 at P == 1; for step kb+3) go out one per MFMA slot,
     // so that the workgroup's waves, released together by the barrier, do
     // not queue all their loads at the address unit before their first MFMA.
-    const int kload = min(kb + 3, nk - 1);
+    const int kload = min(kb + 3, kz1 - 1);
     uint16_t* const xload = xbuf[(P + 3) % kXBufs];
     const float q8v = q8[dcode];
     float ah = 0.0f;
@@ -315,7 +326,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
       srun_cur = srun_next;
     }
   };
-  for (int kb = 0; kb < nk; kb += kFwdUnroll) {
+  for (int kb = kz0; kb < kz1; kb += kFwdUnroll) {
     step(std::integral_constant<int, 0>(), kb);
     step(std::integral_constant<int, 1>(), kb + 1);
     step(std::integral_constant<int, 2>(), kb + 2);
@@ -328,7 +339,8 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   const uint16_t* const Bp = upw ? g.B2 : g.B;
   const int r = upw ? g.r2 : g.r;
   const float sc = upw ? g.s2 : g.s;
-  for (int r0 = 0; r0 < r; r0 += 16) {
+  const int radd = zsplit == 0 ? r : 0;   // the adapter term goes into split 0 only
+  for (int r0 = 0; r0 < radd; r0 += 16) {
     const int rr = r0 + 8 * h;
     uint4 bv = make_uint4(0, 0, 0, 0);
     if (nvalid && rr < r) {
@@ -352,6 +364,22 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   // Accumulator i: lane holds token m = m0 + 32 i + c and weight rows
   // 8 (v / 4) + 4 h + (v % 4) of the wave's 32; four consecutive rows are
   // one 8-byte piece of Y.
+  if (g.part != nullptr) {
+    // split contraction: this split's fp32 partial, four features per store
+    float* const pz = g.part + (int64_t)zsplit * g.M * N;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + 32 * i + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = nw0 + 8 * q + 4 * h;
+        if (m >= g.M || n >= N) continue;   // N % 8 == 0: a group of four is all in or all out
+        *reinterpret_cast<float4*>(pz + (int64_t)m * N + n) =
+            make_float4(acc[i][4 * q + 0], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
+      }
+    }
+    return;
+  }
   uint16_t* const Yp = upw ? g.Y2 : g.Y;
   uint32_t ob[8][4][2];   // the bf16 results, kept for the gated epilogue
 #pragma unroll
@@ -442,6 +470,35 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
 
 bool fwd_nf4_supported(int64_t K) { return (K / kBlock) % kFwdUnroll == 0; }
 
+// Y = bf16(sum of the split partials), added in the order z = 0, 1, ...;
+// one thread per 8 consecutive outputs (n8 = M N / 8).
+__global__ void __launch_bounds__(256)
+k_fwd_reduce(const float* __restrict__ part, int splits, int64_t stride, int64_t n8,
+             uint16_t* __restrict__ Y) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int z = 0; z < splits; ++z) {
+    const float4* p = reinterpret_cast<const float4*>(part + (int64_t)z * stride) + 2 * i;
+    const float4 a = p[0], b = p[1];
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  reinterpret_cast<uint4*>(Y)[i] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
+int fwd_split_len(int64_t M, int64_t K, int64_t N) {
+  const int64_t nk = K / kBlock;
+  const int64_t tiles = ((M + kFwdBM - 1) / kFwdBM) * ((N + kFwdBN - 1) / kFwdBN);
+  if (tiles >= 128 || nk < 2 * kFwdUnroll) return 0;   // two splits do not pay for the partials
+  int64_t splits = 256 / tiles;
+  if (splits > nk / kFwdUnroll) splits = nk / kFwdUnroll;
+  if (splits < 2) return 0;
+  const int64_t per = (nk + splits - 1) / splits;
+  return (int)(((per + kFwdUnroll - 1) / kFwdUnroll) * kFwdUnroll);
+}
+
 hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, const uint16_t* Tg,
                             const uint16_t* Bg, int rg, float sg, const NF4Weight& wu,
                             const uint16_t* Tu, const uint16_t* Bu, int ru, float su, uint16_t* G,
@@ -460,7 +517,8 @@ hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, c
 }
 
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
-                          const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
+                          const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st,
+                          float* part, int kz_len) {
   if (!fwd_nf4_supported(w.K) || w.bf16) return hipErrorInvalidValue;
   FwdArgs g{};
   g.X = X; g.M = (int)M; g.w = w; g.T = T; g.B = B; g.r = r; g.s = s; g.Y = Y;
@@ -468,7 +526,18 @@ hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, cons
   g.tiles_n = (int)((w.N + kFwdBN - 1) / kFwdBN);
   g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * w.K * 2,
                         (double)kFwdBN * w.K * 0.52);
-  hipLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n), dim3(256), 0, st, g);
+  const int64_t nk = w.K / kBlock;
+  const int splits = (part != nullptr && kz_len > 0) ? (int)((nk + kz_len - 1) / kz_len) : 1;
+  if (splits > 1) {
+    g.part = part;
+    g.kz_len = kz_len;
+  }
+  hipLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n * splits), dim3(256), 0, st, g);
+  if (splits > 1) {
+    const int64_t n8 = M * w.N / 8;
+    hipLaunchKernelGGL(k_fwd_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part,
+                       splits, M * w.N, n8, Y);
+  }
   return hipGetLastError();
 }
 

@@ -655,6 +655,12 @@ FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r) {
     p.t_splits = kTSplits;
     off += align256((size_t)kTSplits * M * r * 4);
   }
+  p.fwd_kz_len = (!p.gemv && fwd_nf4_supported(K) && !QLK_FWD_TILE_ENGINE) ? fwd_split_len(M, K, N) : 0;
+  p.off_fpart = off;
+  if (p.fwd_kz_len > 0) {
+    const int64_t splits = (K / kBlock + p.fwd_kz_len - 1) / p.fwd_kz_len;
+    off += align256((size_t)splits * M * N * 4);
+  }
   p.bytes = off;
   return p;
 }
@@ -821,7 +827,9 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   timer_begin(TK_FWD_GEMM, st);
   hipError_t e;
   if (!QLK_FWD_TILE_ENGINE && fwd_nf4_supported(K)) {
-    e = launch_fwd_nf4(X, M, w, T, B, r, s, Y, st);
+    e = launch_fwd_nf4(X, M, w, T, B, r, s, Y, st,
+                       plan.fwd_kz_len ? reinterpret_cast<float*>(base + plan.off_fpart) : nullptr,
+                       plan.fwd_kz_len);
   } else if (w.bf16) {
     g.b1 = opnd(w.bf16, K, (int)N, N);
     e = launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdBF16K<128, kBK, false>,

@@ -51,6 +51,10 @@ struct FwdPlan {
   bool gemv;          // small-M path
   int t_splits;       // contraction splits for T = X A^T
   size_t off_T, off_part, bytes;
+  // Split contraction of the register-decode forward when its tiles do not
+  // fill the device: K-steps per split (0: none) and the fp32 partials.
+  int fwd_kz_len;
+  size_t off_fpart;
 };
 struct BwdPlan {
   int u_splits, t_splits, m_splits_a, m_splits_b;
@@ -78,7 +82,10 @@ int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes
 // supported when K / 64 is a multiple of 4 (else the tile engine runs).
 bool fwd_nf4_supported(int64_t K);
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
-                          const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
+                          const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st,
+                          float* part = nullptr, int kz_len = 0);
+// K-steps per split of the forward's contraction for this shape (0: none).
+int fwd_split_len(int64_t M, int64_t K, int64_t N);
 // Fused gate/up projections of a SiLU-gated MLP (M > kGemvMaxM, K / 64 a
 // multiple of 4, both weights [I, K]): G = X Wg^T + sg Tg Bg^T,
 // U = X Wu^T + su Tu Bu^T, H = silu(G) U, all bf16 [M, I]; Tg, Tu precomputed.
