@@ -79,6 +79,12 @@ struct DxArgs {
   int tiles_m, tiles_k, group_m;
   const uint32_t* mask; // dropout of the adapter input: bit per element of dX, or null
   float keep_scale;     // 1 / (1 - p) for the kept elements
+  // Split contraction (fewer tiles than the device has CUs): workgroup
+  // b + z tiles takes steps z kz_len .. +kz_len of tile b and writes its fp32
+  // partial to part[z] ([M, K]); launch_split_reduce adds the splits.
+  // kz_len == 0: one pass, dX written directly.
+  float* part;
+  int kz_len;
 };
 
 struct DxWRegs { uint2 p; uint32_t code; float sc; };
@@ -106,13 +112,18 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   const int fg = wave & 1, tq = wave >> 1;   // feature half, token quarter
 
   int tm, tk;
-  tile_coords(blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
+  const int ntiles = g.tiles_m * g.tiles_k;
+  const int zsplit = (int)blockIdx.x / ntiles;
+  tile_coords((int)blockIdx.x % ntiles, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
   const int m0 = tm * kDxBM;
   const int64_t k0 = (int64_t)tk * kDxBK;
   // N: contraction length; K: output features (dX columns, or Y columns and
   // weight rows in the forward form).
   const int64_t N = NT ? g.w.K : g.w.N, K = NT ? g.w.N : g.w.K, nkb = K / kBlock;
   const int nsteps = (int)(N / kDxStepN);
+  // this workgroup's steps (multiples of 4 at both ends)
+  const int kz0 = g.kz_len ? zsplit * g.kz_len : 0;
+  const int kz1 = g.kz_len ? min(nsteps, kz0 + g.kz_len) : nsteps;
   const float mean = BF16W ? 0.0f : g.w.mean[0];
   const float qlev = nf4_level(lane & 15);   // source of the level lookups
 
@@ -275,16 +286,16 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   __syncthreads();
   if constexpr (BF16W) {
     // W(0) into weight buffer 0, then dY(0..2); W(j+1) is copied during step j.
-    load_wbi(0, wtb[0], 0);
-    load_wbi(1, wtb[0], 0);
+    load_wbi(0, wtb[0], kz0);
+    load_wbi(1, wtb[0], kz0);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) load_dy(dyb[j], min(j, nsteps - 1));
+    for (int j = 0; j < 3; ++j) load_dy(dyb[j], min(kz0 + j, kz1 - 1));
     __builtin_amdgcn_s_waitcnt(dx_wait(8, 0));   // W(0) and dY(0) arrived
   } else {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      load_dy(dyb[j], min(j, nsteps - 1));
-      load_w(wr[j], min(j, nsteps - 1));
+      load_dy(dyb[j], min(kz0 + j, kz1 - 1));
+      load_w(wr[j], min(kz0 + j, kz1 - 1));
     }
     // Only step 0's seven loads must have arrived (those of steps 1 and 2
     // may still be in flight) before its weight is decoded and the barrier
@@ -315,7 +326,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     // This step's 7 loads (for step kb+3) go out one per MFMA slot 0..6, so
     // that the waves released together by the barrier do not queue 56 loads
     // at the address unit before their first MFMA.
-    const int kload = min(kb + 3, nsteps - 1);
+    const int kload = min(kb + 3, kz1 - 1);
     uint16_t* const yload = dyb[(P + 3) % 4];
     bf16x8_t a[2][2];   // weight operands [MFMA step parity][feature block]
     a[0][0] = wfrag(wcur, 0, 0);
@@ -331,7 +342,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
       acc[i] = mfma_32x32x16(a[t & 1][i >> 1], b[t & 1][i & 1], acc[i]);
       if constexpr (BF16W) {
         // W(kb+1) first (it must be complete at this step's end), then dY(kb+3)
-        if (u < 2) load_wbi(u, wnext, min(kb + 1, nsteps - 1));
+        if (u < 2) load_wbi(u, wnext, min(kb + 1, kz1 - 1));
         else if (u < 6) load_dyi(u - 2, yload, kload);
       } else {
         if (u < 4) load_dyi(u, yload, kload);
@@ -375,7 +386,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     __builtin_amdgcn_s_waitcnt(BF16W ? dx_wait(4, 2) : dx_wait(7, 2));
     __builtin_amdgcn_s_barrier();
   };
-  for (int kb = 0; kb < nsteps; kb += kDxUnroll) {
+  for (int kb = kz0; kb < kz1; kb += kDxUnroll) {
     step(std::integral_constant<int, 0>(), kb);
     step(std::integral_constant<int, 1>(), kb + 1);
     step(std::integral_constant<int, 2>(), kb + 2);
@@ -427,7 +438,9 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
 
   // Accumulator i: lane holds token m = mw + 32 (i % 2) + c and features
   // kw + 32 (i / 2) + 8 (v / 4) + 4 h + (v % 4).
-  if (NT || g.mask == nullptr) {
+  if (zsplit != 0) {
+    // the adapter term goes into split 0 only
+  } else if (NT || g.mask == nullptr) {
     adapter_into(acc);
   } else {
     f32x16_t ad[4];
@@ -449,6 +462,22 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
         acc[i][v] += ((bits >> bit) & 1u) ? ad[i][v] * g.keep_scale : 0.0f;
       }
     }
+  }
+  if (g.part != nullptr) {
+    // split contraction: this split's fp32 partial, four features per store
+    float* const pz = g.part + (int64_t)zsplit * g.M * K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mw + 32 * (i & 1) + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t k = kw + 32 * (i >> 1) + 8 * q + 4 * h;
+        if (m >= g.M || k >= K) continue;   // K % 8 == 0: a group of four is all in or all out
+        *reinterpret_cast<float4*>(pz + (int64_t)m * K + k) =
+            make_float4(acc[i][4 * q + 0], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
+      }
+    }
+    return;
   }
   // The fp32 tile goes out through LDS (the dY buffers are free now and hold
   // it exactly: tokens 64 b .. 64 b + 63 in buffer b, rows of 128 features x
@@ -503,9 +532,10 @@ bool dx_nf4_supported(int64_t N) { return N % (kDxStepN * kDxUnroll) == 0; }
 
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
                          const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
-                         hipStream_t st, const uint32_t* mask, float keep_scale) {
+                         hipStream_t st, const uint32_t* mask, float keep_scale, float* part,
+                         int kz_len) {
   if (!dx_nf4_supported(w.N)) return hipErrorInvalidValue;
-  DxArgs g;
+  DxArgs g{};
   g.dY = dY; g.M = (int)M; g.w = w; g.U = U; g.A = A; g.r = r; g.s = s; g.dX = dX;
   g.accumulate = accumulate ? 1 : 0;
   g.mask = mask; g.keep_scale = keep_scale;
@@ -513,11 +543,30 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
   g.tiles_k = (int)((w.K + kDxBK - 1) / kDxBK);
   g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2,
                         (double)kDxBK * w.N * (w.bf16 ? 2.0 : 0.52));
+  const int nsteps = (int)(w.N / kDxStepN);
+  const int splits = (part != nullptr && kz_len > 0) ? (nsteps + kz_len - 1) / kz_len : 1;
+  if (splits > 1) {
+    g.part = part;
+    g.kz_len = kz_len;
+  }
+  const dim3 grid(g.tiles_m * g.tiles_k * splits);
   if (w.bf16)
-    hipLaunchKernelGGL(k_dx_nf4<true>, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
+    hipLaunchKernelGGL(k_dx_nf4<true>, grid, dim3(64 * kDxWaves), 0, st, g);
   else
-    hipLaunchKernelGGL(k_dx_nf4<false>, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st, g);
+    hipLaunchKernelGGL(k_dx_nf4<false>, grid, dim3(64 * kDxWaves), 0, st, g);
+  if (splits > 1) return launch_split_reduce(part, splits, M * w.K, dX, accumulate, st);
   return hipGetLastError();
+}
+
+int dx_split_len(int64_t M, int64_t K, int64_t N) {
+  const int64_t nsteps = N / kDxStepN;
+  const int64_t tiles = ((M + kDxBM - 1) / kDxBM) * ((K + kDxBK - 1) / kDxBK);
+  if (tiles >= 128 || nsteps < 2 * kDxUnroll) return 0;   // two splits do not pay for the partials
+  int64_t splits = 256 / tiles;
+  if (splits > nsteps / kDxUnroll) splits = nsteps / kDxUnroll;
+  if (splits < 2) return 0;
+  const int64_t per = (nsteps + splits - 1) / splits;
+  return (int)(((per + kDxUnroll - 1) / kDxUnroll) * kDxUnroll);
 }
 
 // Forward on a bf16 weight wb ([N, K]): Y = X wb^T + s T B^T.

@@ -85,7 +85,7 @@ struct FwdArgs {
   uint16_t* H;
   // Split contraction (fewer tiles than the device has CUs): workgroup
   // b + z tiles takes K-steps z kz_len .. +kz_len of tile b and writes its
-  // fp32 partial to part[z] ([M, N]); k_fwd_reduce adds the splits.
+  // fp32 partial to part[z] ([M, N]); launch_split_reduce adds the splits.
   // kz_len == 0: one pass over K, Y written directly.
   float* part;
   int kz_len;
@@ -470,11 +470,12 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
 
 bool fwd_nf4_supported(int64_t K) { return (K / kBlock) % kFwdUnroll == 0; }
 
-// Y = bf16(sum of the split partials), added in the order z = 0, 1, ...;
-// one thread per 8 consecutive outputs (n8 = M N / 8).
+// out = bf16(sum of the split partials (+ out's bf16 values when
+// accumulating)), added in the order z = 0, 1, ..., then the old value; one
+// thread per 8 consecutive outputs (n8 = stride / 8).
 __global__ void __launch_bounds__(256)
-k_fwd_reduce(const float* __restrict__ part, int splits, int64_t stride, int64_t n8,
-             uint16_t* __restrict__ Y) {
+k_split_reduce(const float* __restrict__ part, int splits, int64_t stride, int64_t n8,
+               uint16_t* __restrict__ out, int accumulate) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n8) return;
   float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -484,8 +485,26 @@ k_fwd_reduce(const float* __restrict__ part, int splits, int64_t stride, int64_t
     v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
     v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
   }
-  reinterpret_cast<uint4*>(Y)[i] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  uint4* const o = reinterpret_cast<uint4*>(out) + i;
+  if (accumulate) {
+    const uint4 old = *o;
+    const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] += bf16_to_f32(ow[e] & 0xffffu);
+      v[2 * e + 1] += bf16_to_f32(ow[e] >> 16);
+    }
+  }
+  *o = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                  pack_bf16x2(v[6], v[7]));
+}
+
+hipError_t launch_split_reduce(const float* part, int splits, int64_t stride, uint16_t* out,
+                               bool accumulate, hipStream_t st) {
+  const int64_t n8 = stride / 8;
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part,
+                     splits, stride, n8, out, accumulate ? 1 : 0);
+  return hipGetLastError();
 }
 
 int fwd_split_len(int64_t M, int64_t K, int64_t N) {
@@ -533,11 +552,7 @@ hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, cons
     g.kz_len = kz_len;
   }
   hipLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n * splits), dim3(256), 0, st, g);
-  if (splits > 1) {
-    const int64_t n8 = M * w.N / 8;
-    hipLaunchKernelGGL(k_fwd_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part,
-                       splits, M * w.N, n8, Y);
-  }
+  if (splits > 1) return launch_split_reduce(part, splits, M * w.N, Y, false, st);
   return hipGetLastError();
 }
 

@@ -683,6 +683,12 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r) {
                  !QLK_DX_TILE_ENGINE;
   p.off_wbf16 = p.bytes;
   if (p.dequant_dx) p.bytes += align256((size_t)N * K * 2);
+  p.dx_kz_len = (dx_nf4_supported(N) && !QLK_DX_TILE_ENGINE) ? dx_split_len(M, K, N) : 0;
+  p.off_dxpart = p.bytes;
+  if (p.dx_kz_len > 0) {
+    const int64_t splits = (N / 64 + p.dx_kz_len - 1) / p.dx_kz_len;
+    p.bytes += align256((size_t)splits * M * K * 4);
+  }
   return p;
 }
 
@@ -912,7 +918,9 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     timer_begin(TK_DX_GEMM, st);
     hipError_t e;
     if (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N)) {
-      e = launch_dx_nf4(dY, M, wx, U, A, r, s, dX, accumulate_dx, st, mask, keep_scale);
+      e = launch_dx_nf4(dY, M, wx, U, A, r, s, dX, accumulate_dx, st, mask, keep_scale,
+                        plan.dx_kz_len ? reinterpret_cast<float*>(base + plan.off_dxpart) : nullptr,
+                        plan.dx_kz_len);
     } else if (mask) {
       // Tile engine with a dropout mask: the masked adapter term is written
       // (or added) first, then dY W_hat is accumulated on top of it.

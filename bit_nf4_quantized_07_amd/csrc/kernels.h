@@ -63,6 +63,10 @@ struct BwdPlan {
   // instead of decoding every tile in each of the M / 256 token tiles.
   bool dequant_dx;
   size_t off_wbf16;
+  // Split contraction of the dX kernel when its tiles do not fill the
+  // device: steps per split (0: none) and the fp32 partials.
+  int dx_kz_len;
+  size_t off_dxpart;
 };
 // Token count from which the backward dequantises the NF4 weight once.
 constexpr int64_t kDequantDxMinM = 1024;
@@ -118,7 +122,14 @@ bool dx_nf4_supported(int64_t N);
 // becomes mask * keep_scale * s U A.
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
                          const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
-                         hipStream_t st, const uint32_t* mask = nullptr, float keep_scale = 1.0f);
+                         hipStream_t st, const uint32_t* mask = nullptr, float keep_scale = 1.0f,
+                         float* part = nullptr, int kz_len = 0);
+// Steps per split of the dX kernel's contraction for this shape (0: none).
+int dx_split_len(int64_t M, int64_t K, int64_t N);
+// out (bf16, stride values per split) = the fixed-order sum of the fp32
+// split partials, plus out's own values when accumulating; one rounding.
+hipError_t launch_split_reduce(const float* part, int splits, int64_t stride, uint16_t* out,
+                               bool accumulate, hipStream_t st);
 // dX (+)= bf16(mask * keep_scale * s U A): the adapter term alone, for the
 // tile-engine fallback of the dropout backward.
 hipError_t launch_dx_adapter_masked(const uint16_t* U, const uint16_t* A, int64_t M, int64_t K,
