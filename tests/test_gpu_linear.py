@@ -57,6 +57,9 @@ CASES = [
     (520, 264, 768, 72, 144.0),   # forward kernel: ragged M and N, r = 72
     (300, 512, 704, 40, 80.0),    # dX kernel: ragged M, K % 128 == 64
     (272, 768, 1280, 136, 272.0), # both kernels, r = 136 (nine adapter steps)
+    # few tiles: both kernels split the contraction 8 ways (fp32 partials and
+    # the fixed-order reduce)
+    (100, 4096, 4096, 16, 32.0),
 ]
 
 
