@@ -129,7 +129,11 @@ int codebook_dequant(const uint8_t* packed, const uint8_t* codes, const float* s
  *   Y  bf16 [M, N]     output
  *   T_out bf16 [M, r]  optional: X A^T for the backward (NULL = not stored)
  * W_hat is never written to memory: tiles are dequantised on the fly.
- * Accumulation is fp32; Y is rounded to bf16 once.  Results meet
+ * Accumulation is fp32; Y is rounded to bf16 once.  When Y has fewer than
+ * 128 tiles of 256 tokens x 128 outputs, the contraction over K is split
+ * into ranges whose fp32 partials pass through the workspace and are added
+ * in a fixed order: still deterministic, though the bits can differ from a
+ * shape that does not split.  Results meet
  * |err|_F / |ref|_F <= 1e-2 and max|err| <= 3e-2 max|ref| against an exact
  * evaluation of the same bf16 inputs.
  * Requires 1 <= M, K % 64 == 0, N % 8 == 0, r % 8 == 0, 8 <= r <= 256, each
@@ -155,8 +159,10 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
  * For M >= 1024 (and N % 256 == 0, 2 N K < 2 GiB) the weight is dequantised
  * once per call into the workspace (2 N K bytes of it) and dX runs on that
  * bf16 copy (the pages' dequantise-then-matmul, llm-compass 直觉与动机): the
- * same bits as decoding in every tile, without decoding it again for every
- * 256 tokens. */
+ * same bits as decoding in every tile with the same split of the
+ * contraction, without decoding it again for every 256 tokens.  dX splits
+ * its contraction over N like the forward when its tiles (256 tokens x 128
+ * features) number fewer than 128. */
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
                      const uint8_t* packed, const uint8_t* codes, const float* scales,
                      const float* mean, const uint16_t* A, const uint16_t* B,
