@@ -166,7 +166,9 @@ def test_dequant_once_dx_equals_in_tile_decode(N, K):
     dX kernel on the bf16 copy; below, every tile decodes the NF4 bytes.  dX
     rows depend on their own dY row only, so the first 512 rows of a
     1024-token backward must equal a 512-token backward of those rows bit for
-    bit (dA, dB sum over tokens and differ)."""
+    bit (dA, dB sum over tokens and differ).  At these shapes both token
+    counts split the contraction over N into the same ranges (4 steps of 64),
+    so the sums run in the same order."""
     t = pytest.importorskip("torch")
     case = wl.linear_case(12, 1024, N, K, 16, 32.0)
     qw = q.quantize(dev_f32(case["W"]))
