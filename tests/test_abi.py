@@ -140,6 +140,22 @@ def test_workspace_sizes():
     assert small < 2 * 4096 * 4096
 
 
+def test_workspace_holds_the_split_partials():
+    """With fewer than 128 output tiles (256 tokens x 128 outputs) the forward
+    and dX kernels split their contraction so that about 256 workgroups run,
+    and the workspace holds one fp32 [M, N] (forward) or [M, K] (dX) partial
+    per split; from 128 tiles on they run in one pass."""
+    K = N = 4096
+    splits = 8   # 256 tokens: 32 tiles, 256 / 32 = 8 splits of 8 K-steps
+    assert lib.qlora_workspace_bytes(256, K, N, 16, 0) >= splits * 256 * N * 4
+    assert lib.qlora_workspace_bytes(256, K, N, 16, 1) >= splits * 256 * K * 4
+    # 128 and 256 tiles: no partials (T, U and the adapter-gradient splits only,
+    # and the bf16 weight copy in the backward)
+    assert lib.qlora_workspace_bytes(1024, K, N, 16, 0) < 1024 * N * 4
+    assert lib.qlora_workspace_bytes(2048, K, N, 16, 0) < 2048 * N * 4
+    assert lib.qlora_workspace_bytes(1024, K, N, 16, 1) < 2 * N * K + 1024 * K * 4
+
+
 def test_kernel_timer_validation():
     assert lib.qlora_set_kernel_timer(0, None, None) == q.ERR_ARG
     assert lib.qlora_set_kernel_timer(5, None, None) == q.ERR_ARG
