@@ -189,12 +189,21 @@ def make_linear_sets(q, torch, wl, cfg_name, idx, M, sets):
     return out
 
 
-def linear_step(q, d, ws, weight="qw"):
+def linear_step(q, d, ws, weight="qw", timing=None):
     lin = d["lin"]
     q.linear_fwd(d["X"], d[weight], d["A"], d["B"], lin.alpha, out=d["Y"], T_out=d["T"],
-                 workspace=ws)
+                 workspace=ws, timing=timing)
     q.linear_bwd(d["dY"], d["X"], d[weight], d["A"], d["B"], lin.alpha, T=d["T"],
-                 dX_out=d["dX"], dA_out=d["dA"], dB_out=d["dB"], workspace=ws)
+                 dX_out=d["dX"], dA_out=d["dA"], dB_out=d["dB"], workspace=ws, timing=timing)
+
+
+def timing_for(q, slots):
+    """A qlora_timing struct with events in the given slots ({kernel: (start, stop)})."""
+    t = q.TimingC()
+    for k, (a, b) in slots.items():
+        t.start[k] = a
+        t.stop[k] = b
+    return t
 
 
 DROPOUT_P = 0.05
@@ -238,14 +247,11 @@ def run_linear(args, q, torch, wl, lib, ev):
     # out of the pass that gives the step time.
     evs = {k: (ev.create(K), ev.create(K))
            for k in (q.KERNEL_FWD_GEMM, q.KERNEL_DX_GEMM, q.KERNEL_DX_DEQUANT)}
+    timings = [timing_for(q, {k: (a[i], b[i]) for k, (a, b) in evs.items()}) for i in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
-        for k, (a, b) in evs.items():
-            lib.qlora_set_kernel_timer(k, a[i], b[i])
-        linear_step(q, sets[i % len(sets)], ws)
+        linear_step(q, sets[i % len(sets)], ws, timing=timings[i])
     torch.cuda.synchronize()
-    for k in evs:
-        lib.qlora_set_kernel_timer(k, None, None)
     flops = linear_flops(M, lin.N, lin.K, lin.r)
     kern = {}
     names = {q.KERNEL_FWD_GEMM: "fwd_gemm", q.KERNEL_DX_GEMM: "dx_gemm",
@@ -328,22 +334,21 @@ def run_gemv(args, q, torch, wl, lib, ev):
         Ys = [torch.empty(M, lin.N, dtype=torch.bfloat16, device="cuda") for _ in sets]
         Ts = [torch.empty(M, lin.r, dtype=torch.bfloat16, device="cuda") for _ in sets]
 
-        def call(i):
+        def call(i, timing=None):
             d = sets[i % len(sets)]
             q.linear_fwd(d["X"][:M], d["qw"], d["A"], d["B"], lin.alpha, out=Ys[i % len(sets)],
-                         T_out=Ts[i % len(sets)], workspace=ws)
+                         T_out=Ts[i % len(sets)], workspace=ws, timing=timing)
         for i in range(10):
             call(i)
         torch.cuda.synchronize()
         n = max(args.steps * 5, 50)
         a, b = ev.create(n), ev.create(n)
         t0 = time.perf_counter()
+        timings = [timing_for(q, {q.KERNEL_GEMV: (a[i], b[i])}) for i in range(n)]
         for i in range(n):
-            lib.qlora_set_kernel_timer(q.KERNEL_GEMV, a[i], b[i])
-            call(i)
+            call(i, timings[i])
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        lib.qlora_set_kernel_timer(q.KERNEL_GEMV, None, None)
         d = [ev.elapsed_ms(a[i], b[i]) for i in range(n)]
         ev.destroy(a + b)
         avg = float(np.mean(d)) * 1e-3

@@ -71,4 +71,42 @@ hipError_t launch_silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint
   return hipGetLastError();
 }
 
+// dst [rows_dst, cols_dst] = src [rows_src, cols_src] zero-extended (or cut)
+// to the new shape, both row-major and contiguous.  The adapter rank is
+// padded with it to the kernels' granule (zero rows of A, zero columns of B
+// and T) and the results are cut back to the caller's rank.
+template <class T>
+__global__ void __launch_bounds__(256)
+k_pad2d(const T* __restrict__ src, int64_t rows_src, int64_t cols_src, T* __restrict__ dst,
+        int64_t rows_dst, int64_t cols_dst) {
+  const int64_t n = rows_dst * cols_dst;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / cols_dst, col = i - row * cols_dst;
+    dst[i] = (row < rows_src && col < cols_src) ? src[row * cols_src + col] : T(0);
+  }
+}
+
+template <class T>
+static hipError_t pad2d(const T* src, int64_t rows_src, int64_t cols_src, T* dst, int64_t rows_dst,
+                        int64_t cols_dst, hipStream_t st) {
+  const int64_t n = rows_dst * cols_dst;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) return hipSuccess;
+  hipLaunchKernelGGL(k_pad2d<T>, dim3((unsigned)blocks), dim3(256), 0, st, src, rows_src, cols_src,
+                     dst, rows_dst, cols_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad2d(const uint16_t* src, int64_t rows_src, int64_t cols_src, uint16_t* dst,
+                        int64_t rows_dst, int64_t cols_dst, hipStream_t st) {
+  return pad2d(src, rows_src, cols_src, dst, rows_dst, cols_dst, st);
+}
+
+hipError_t launch_pad2d(const float* src, int64_t rows_src, int64_t cols_src, float* dst,
+                        int64_t rows_dst, int64_t cols_dst, hipStream_t st) {
+  return pad2d(src, rows_src, cols_src, dst, rows_dst, cols_dst, st);
+}
+
 }  // namespace qlk

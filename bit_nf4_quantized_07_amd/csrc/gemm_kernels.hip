@@ -35,10 +35,6 @@ namespace qlk {
 
 constexpr int kThreads = 256;
 
-// 1: loads run two K-steps ahead of the MFMAs (two register sets); 0: one.
-#ifndef QLK_PREFETCH2
-#define QLK_PREFETCH2 0
-#endif
 constexpr int kPad = 8;   // bf16 elements of padding per LDS row (bank spread)
 
 struct Operand {
@@ -370,21 +366,10 @@ struct Tile {
     }
   }
 
-  template <class LA, class LB>
-  __device__ static void phase(const GemmArgs& g, const Operand& opa, const Operand& opb, int p0,
-                               int q0, int cbeg, int cend, uint16_t* smem, f32x16_t (&acc)[TM][TN],
-                               const Dec& d, int tid, int wm, int wn, int lane) {
-#if QLK_PREFETCH2
-    phase2<LA, LB>(g, opa, opb, p0, q0, cbeg, cend, smem, acc, d, tid, wm, wn, lane);
-#else
-    phase1<LA, LB>(g, opa, opb, p0, q0, cbeg, cend, smem, acc, d, tid, wm, wn, lane);
-#endif
-  }
-
   // Distance-1 pipeline: loads for step it+1 are issued before step it is
   // multiplied and land in the other LDS stage after it.
   template <class LA, class LB>
-  __device__ static void phase1(const GemmArgs& g, const Operand& opa, const Operand& opb, int p0,
+  __device__ static void phase(const GemmArgs& g, const Operand& opa, const Operand& opb, int p0,
                                 int q0, int cbeg, int cend, uint16_t* smem, f32x16_t (&acc)[TM][TN],
                                 const Dec& d, int tid, int wm, int wn, int lane) {
     const int nk = (cend - cbeg + BK - 1) / BK;
@@ -417,51 +402,6 @@ struct Tile {
     }
   }
 
-  template <class LA, class LB>
-  __device__ static void phase2(const GemmArgs& g, const Operand& opa, const Operand& opb, int p0,
-                                int q0, int cbeg, int cend, uint16_t* smem, f32x16_t (&acc)[TM][TN],
-                                const Dec& d, int tid, int wm, int wn, int lane) {
-    const int nk = (cend - cbeg + BK - 1) / BK;
-    if (nk <= 0) return;
-    LA la;
-    LB lb;
-    la.init(opa, g, p0, tid);
-    lb.init(opb, g, q0, tid);
-    typename LA::Regs ra0, ra1;
-    typename LB::Regs rb0, rb1;
-    la.load(ra0, opa, g, cbeg, cend);
-    lb.load(rb0, opb, g, cbeg, cend);
-    if (nk > 1) {
-      la.load(ra1, opa, g, cbeg + BK, cend);
-      lb.load(rb1, opb, g, cbeg + BK, cend);
-    }
-    la.store(ra0, opa, smem, d);
-    lb.store(rb0, opb, smem + LDSA, d);
-    __syncthreads();
-    for (int it = 0; it < nk; it += 2) {
-      if (it + 2 < nk) {
-        la.load(ra0, opa, g, cbeg + (it + 2) * BK, cend);
-        lb.load(rb0, opb, g, cbeg + (it + 2) * BK, cend);
-      }
-      compute<LA::TR, LB::TR>(smem, smem + LDSA, acc, wm, wn, lane);
-      if (it + 1 < nk) {
-        la.store(ra1, opa, smem + STAGE, d);
-        lb.store(rb1, opb, smem + STAGE + LDSA, d);
-      }
-      __syncthreads();
-      if (it + 1 >= nk) break;
-      if (it + 3 < nk) {
-        la.load(ra1, opa, g, cbeg + (it + 3) * BK, cend);
-        lb.load(rb1, opb, g, cbeg + (it + 3) * BK, cend);
-      }
-      compute<LA::TR, LB::TR>(smem + STAGE, smem + STAGE + LDSA, acc, wm, wn, lane);
-      if (it + 2 < nk) {
-        la.store(ra0, opa, smem, d);
-        lb.store(rb0, opb, smem + LDSA, d);
-      }
-      __syncthreads();
-    }
-  }
 };
 
 // One workgroup of the tile engine: tile index `bx` (walked by tile_coords),
@@ -571,24 +511,6 @@ __global__ void __launch_bounds__(kThreads) k_gemm_pair(GemmArgs g1, int blocks1
 // thread per four outputs (coalesced 16-byte loads, eight splits in flight).
 constexpr int kRedThreads = 64;
 
-// ---------------------------- measurement hook ------------------------------
-
-namespace {
-hipEvent_t g_timer_start[TK_COUNT] = {};
-hipEvent_t g_timer_stop[TK_COUNT] = {};
-}  // namespace
-
-void set_kernel_timer(int kernel, hipEvent_t start, hipEvent_t stop) {
-  g_timer_start[kernel] = start;
-  g_timer_stop[kernel] = stop;
-}
-void timer_begin(int kernel, hipStream_t st) {
-  if (g_timer_start[kernel]) (void)hipEventRecord(g_timer_start[kernel], st);
-}
-void timer_end(int kernel, hipStream_t st) {
-  if (g_timer_stop[kernel]) (void)hipEventRecord(g_timer_stop[kernel], st);
-}
-
 // ------------------------------- planning ----------------------------------
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -599,30 +521,8 @@ constexpr int kBK = 64;
 static_assert(kBK == kPairBK, "paired products use the engine's contraction step");
 
 // dX tile (rows of dX x columns of dX).
-#ifndef QLK_DX_BM
-#define QLK_DX_BM 128
-#endif
-#ifndef QLK_DX_BN
-#define QLK_DX_BN 128
-#endif
-
-// 1: the forward runs on the generic tile engine (NF4 tiles decoded into
-// LDS); 0: on the register-decode forward kernel.
-#ifndef QLK_FWD_TILE_ENGINE
-#define QLK_FWD_TILE_ENGINE 0
-#endif
-
-// 1: dX runs on the generic tile engine; 0: on the dedicated dX kernel.
-#ifndef QLK_DX_TILE_ENGINE
-#define QLK_DX_TILE_ENGINE 0
-#endif
-
-// Token counts at or above this use 256-row forward tiles (fewer decodes of
-// each weight tile per MFMA flop).  Measured on MI355X the 128-row tile is
-// faster at every size tried, so the tall tile is off by default.
-#ifndef QLK_FWD_TALL_MIN_M
-#define QLK_FWD_TALL_MIN_M (1 << 30)
-#endif
+constexpr int kDxBM = 128;
+constexpr int kDxBN = 128;
 
 // Split a contraction of length C over `blocks` tiles so that roughly 512
 // workgroups run, keeping at least 2 BK-steps per split.
@@ -643,7 +543,7 @@ static inline int actual_splits(int64_t C, int splits) {
   return ceil_div(C, split_len(C, splits));
 }
 
-FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r) {
+FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r, bool nf4) {
   FwdPlan p{};
   p.gemv = M <= kGemvMaxM;
   p.off_T = 0;
@@ -655,7 +555,7 @@ FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r) {
     p.t_splits = kTSplits;
     off += align256((size_t)kTSplits * M * r * 4);
   }
-  p.fwd_kz_len = (!p.gemv && fwd_nf4_supported(K) && !QLK_FWD_TILE_ENGINE) ? fwd_split_len(M, K, N) : 0;
+  p.fwd_kz_len = (nf4 && !p.gemv && fwd_nf4_supported(K)) ? fwd_split_len(M, K, N) : 0;
   p.off_fpart = off;
   if (p.fwd_kz_len > 0) {
     const int64_t splits = (K / kBlock + p.fwd_kz_len - 1) / p.fwd_kz_len;
@@ -665,12 +565,12 @@ FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r) {
   return p;
 }
 
-BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r) {
+BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r, bool dx) {
   BwdPlan p{};
   p.off_U = 0;
   p.off_T = align256((size_t)M * r * 2);
   p.off_part = p.off_T + align256((size_t)M * r * 2);
-  const int64_t mt = ceil_div(M, 128), rt = ceil_div(r, r_tile(r));
+  const int64_t rt = ceil_div(r, r_tile(r));
   p.t_splits = 1;   // T and U in one pass (no partial sums)
   p.u_splits = 1;
   p.m_splits_a = actual_splits(M, choose_splits((int64_t)ceil_div(r, r_tile(r)) * ceil_div(K, 128), M));
@@ -679,11 +579,10 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r) {
   p.bytes = p.off_part_b + align256((size_t)p.m_splits_b * N * r * 4);
   // Large M: the dequantised weight (bf16, 2 N K bytes, addressed with 32-bit
   // buffer offsets) is reused by every token tile of the dX kernel.
-  p.dequant_dx = M >= kDequantDxMinM && dx_nf4_supported(N) && N * K * 2 < ((int64_t)1 << 31) &&
-                 !QLK_DX_TILE_ENGINE;
+  p.dequant_dx = dx && M >= kDequantDxMinM && dx_nf4_supported(N) && N * K * 2 < ((int64_t)1 << 31);
   p.off_wbf16 = p.bytes;
   if (p.dequant_dx) p.bytes += align256((size_t)N * K * 2);
-  p.dx_kz_len = (dx_nf4_supported(N) && !QLK_DX_TILE_ENGINE) ? dx_split_len(M, K, N) : 0;
+  p.dx_kz_len = (dx && dx_nf4_supported(N)) ? dx_split_len(M, K, N) : 0;
   p.off_dxpart = p.bytes;
   if (p.dx_kz_len > 0) {
     const int64_t splits = (N / 64 + p.dx_kz_len - 1) / p.dx_kz_len;
@@ -806,19 +705,20 @@ static hipError_t compute_T(const uint16_t* X, int64_t M, int64_t K, const uint1
 
 hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                             const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
-                            void* ws, const FwdPlan& plan, hipStream_t st, const uint16_t* Xa) {
+                            void* ws, const FwdPlan& plan, hipStream_t st, const uint16_t* Xa,
+                            const Timing* tm) {
   const int64_t K = w.K, N = w.N;
   char* base = reinterpret_cast<char*>(ws);
   uint16_t* T = T_out ? T_out : reinterpret_cast<uint16_t*>(base + plan.off_T);
   float* part = reinterpret_cast<float*>(base + plan.off_part);
   if (!Xa) Xa = X;
-  if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st, Xa);
+  if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st, Xa, tm);
   QLK_TRY(compute_T(Xa, M, K, A, r, T, st));
   // A bf16 base: the dX kernel's forward form.
-  if (w.bf16 && dx_nf4_supported(K) && !QLK_FWD_TILE_ENGINE) {
-    timer_begin(TK_FWD_GEMM, st);
+  if (w.bf16 && dx_nf4_supported(K)) {
+    timer_begin(tm, TK_FWD_GEMM, st);
     const hipError_t e = launch_fwd_bf16(X, M, w.bf16, N, K, T, B, r, s, Y, st);
-    timer_end(TK_FWD_GEMM, st);
+    timer_end(tm, TK_FWD_GEMM, st);
     return e;
   }
   GemmArgs g{};
@@ -830,9 +730,9 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   g.P = (int)M; g.Q = (int)N;
   g.c1_len = (int)K; g.c1_split = (int)K; g.c2_len = r;
   g.out = Y; g.ldo = N; g.accumulate = 0;
-  timer_begin(TK_FWD_GEMM, st);
+  timer_begin(tm, TK_FWD_GEMM, st);
   hipError_t e;
-  if (!QLK_FWD_TILE_ENGINE && fwd_nf4_supported(K)) {
+  if (fwd_nf4_supported(K)) {
     e = launch_fwd_nf4(X, M, w, T, B, r, s, Y, st,
                        plan.fwd_kz_len ? reinterpret_cast<float*>(base + plan.off_fpart) : nullptr,
                        plan.fwd_kz_len);
@@ -841,42 +741,32 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
     e = launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdBF16K<128, kBK, false>,
                     LdBF16K<128, kBK, false>, LdBF16K<128, kBK, true>, EPI_BF16>(
         g, 1, 128.0 * K * 2, 128.0 * K * 2, st);
-  } else if (M >= QLK_FWD_TALL_MIN_M) {
-    e = launch_gemm<256, 128, kBK, LdBF16K<256, kBK, false>, LdNF4K<128>, LdBF16K<256, kBK, false>,
-                    LdBF16K<128, kBK, true>, EPI_BF16>(g, 1, 256.0 * K * 2, 128.0 * K * 0.52, st);
   } else {
     e = launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdNF4K<128>, LdBF16K<128, kBK, false>,
                     LdBF16K<128, kBK, true>, EPI_BF16>(g, 1, 128.0 * K * 2, 128.0 * K * 0.52, st);
   }
-  timer_end(TK_FWD_GEMM, st);
+  timer_end(tm, TK_FWD_GEMM, st);
   return e;
 }
 
+bool mlp_fwd_fused(int64_t M, int64_t K) { return M > kGemvMaxM && fwd_nf4_supported(K); }
+
 hipError_t launch_mlp_fwd(const uint16_t* X, int64_t M, const LoraLinear& gate,
                           const LoraLinear& up, uint16_t* G, uint16_t* U, uint16_t* H,
-                          uint16_t* Tg, uint16_t* Tu, void* ws, size_t ws_bytes, hipStream_t st) {
-  const int64_t K = gate.w.K, I = gate.w.N;
-  if (M > kGemvMaxM && fwd_nf4_supported(K) && !QLK_FWD_TILE_ENGINE) {
-    QLK_TRY(compute_T(X, M, K, gate.A, gate.r, Tg, st));
-    QLK_TRY(compute_T(X, M, K, up.A, up.r, Tu, st));
-    timer_begin(TK_FWD_GEMM, st);
-    const hipError_t e = launch_fwd_gated(X, M, gate.w, Tg, gate.B, gate.r, gate.s, up.w, Tu, up.B,
-                                          up.r, up.s, G, U, H, st);
-    timer_end(TK_FWD_GEMM, st);
-    return e;
-  }
-  const FwdPlan pg = plan_fwd(M, K, I, gate.r), pu = plan_fwd(M, K, I, up.r);
-  if (ws_bytes < pg.bytes || ws_bytes < pu.bytes) return hipErrorInvalidValue;
-  QLK_TRY(launch_qlora_fwd(X, M, gate.w, gate.A, gate.B, gate.r, gate.s, G, Tg, ws, pg, st));
-  QLK_TRY(launch_qlora_fwd(X, M, up.w, up.A, up.B, up.r, up.s, U, Tu, ws, pu, st));
-  return launch_silu_mul_fwd(G, U, M * I, H, st);
+                          uint16_t* Tg, uint16_t* Tu, hipStream_t st) {
+  const int64_t K = gate.w.K;
+  if (!mlp_fwd_fused(M, K)) return hipErrorInvalidValue;
+  QLK_TRY(compute_T(X, M, K, gate.A, gate.r, Tg, st));
+  QLK_TRY(compute_T(X, M, K, up.A, up.r, Tu, st));
+  return launch_fwd_gated(X, M, gate.w, Tg, gate.B, gate.r, gate.s, up.w, Tu, up.B, up.r, up.s,
+                          G, U, H, st);
 }
 
 hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const NF4Weight& w,
                             const uint16_t* A, const uint16_t* B, int r, float s,
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,
                             bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st,
-                            const uint32_t* mask, float keep_scale) {
+                            const uint32_t* mask, float keep_scale, const Timing* tm) {
   const int64_t K = w.K, N = w.N;
   char* base = reinterpret_cast<char*>(ws);
   uint16_t* U = reinterpret_cast<uint16_t*>(base + plan.off_U);
@@ -897,9 +787,9 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
   NF4Weight wx = w;
   if (dX && !w.bf16 && plan.dequant_dx) {
     uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
-    timer_begin(TK_DX_DEQUANT, st);
+    timer_begin(tm, TK_DX_DEQUANT, st);
     QLK_TRY(launch_rank16_and_dequant(dY, M, N, B, r, U, w, wb, st));
-    timer_end(TK_DX_DEQUANT, st);
+    timer_end(tm, TK_DX_DEQUANT, st);
     wx.bf16 = wb;
   } else {
     QLK_TRY(launch_rank16(dY, M, N, B, true, r, U, st));
@@ -915,9 +805,9 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     g.P = (int)M; g.Q = (int)K;
     g.c1_len = (int)N; g.c1_split = (int)N; g.c2_len = r;
     g.out = dX; g.ldo = K; g.accumulate = accumulate_dx ? 1 : 0;
-    timer_begin(TK_DX_GEMM, st);
+    timer_begin(tm, TK_DX_GEMM, st);
     hipError_t e;
-    if (!QLK_DX_TILE_ENGINE && dx_nf4_supported(N)) {
+    if (dx_nf4_supported(N)) {
       e = launch_dx_nf4(dY, M, wx, U, A, r, s, dX, accumulate_dx, st, mask, keep_scale,
                         plan.dx_kz_len ? reinterpret_cast<float*>(base + plan.off_dxpart) : nullptr,
                         plan.dx_kz_len);
@@ -930,30 +820,30 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
         g.accumulate = 1;
         if (w.bf16) {
           g.b1 = opnd(w.bf16, K, (int)K, N);
-          e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
-                          LdBF16T<QLK_DX_BN, kBK, false>, LdBF16K<QLK_DX_BM, kBK, false>,
-                          LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
-              g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 2, st);
+          e = launch_gemm<kDxBM, kDxBN, kBK, LdBF16K<kDxBM, kBK, false>,
+                          LdBF16T<kDxBN, kBK, false>, LdBF16K<kDxBM, kBK, false>,
+                          LdBF16T<kDxBN, kBK, true>, EPI_BF16>(
+              g, 1, (double)kDxBM * N * 2, (double)kDxBN * N * 2, st);
         } else {
-          e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
-                          LdNF4T<QLK_DX_BN>, LdBF16K<QLK_DX_BM, kBK, false>,
-                          LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
-              g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 0.52, st);
+          e = launch_gemm<kDxBM, kDxBN, kBK, LdBF16K<kDxBM, kBK, false>,
+                          LdNF4T<kDxBN>, LdBF16K<kDxBM, kBK, false>,
+                          LdBF16T<kDxBN, kBK, true>, EPI_BF16>(
+              g, 1, (double)kDxBM * N * 2, (double)kDxBN * N * 0.52, st);
         }
       }
     } else if (w.bf16) {
       g.b1 = opnd(w.bf16, K, (int)K, N);   // transposed load of W [N, K]: rows k, contraction n
-      e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
-                      LdBF16T<QLK_DX_BN, kBK, false>, LdBF16K<QLK_DX_BM, kBK, false>,
-                      LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
-          g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 2, st);
+      e = launch_gemm<kDxBM, kDxBN, kBK, LdBF16K<kDxBM, kBK, false>,
+                      LdBF16T<kDxBN, kBK, false>, LdBF16K<kDxBM, kBK, false>,
+                      LdBF16T<kDxBN, kBK, true>, EPI_BF16>(
+          g, 1, (double)kDxBM * N * 2, (double)kDxBN * N * 2, st);
     } else {
-      e = launch_gemm<QLK_DX_BM, QLK_DX_BN, kBK, LdBF16K<QLK_DX_BM, kBK, false>,
-                      LdNF4T<QLK_DX_BN>, LdBF16K<QLK_DX_BM, kBK, false>,
-                      LdBF16T<QLK_DX_BN, kBK, true>, EPI_BF16>(
-          g, 1, (double)QLK_DX_BM * N * 2, (double)QLK_DX_BN * N * 0.52, st);
+      e = launch_gemm<kDxBM, kDxBN, kBK, LdBF16K<kDxBM, kBK, false>,
+                      LdNF4T<kDxBN>, LdBF16K<kDxBM, kBK, false>,
+                      LdBF16T<kDxBN, kBK, true>, EPI_BF16>(
+          g, 1, (double)kDxBM * N * 2, (double)kDxBN * N * 0.52, st);
     }
-    timer_end(TK_DX_GEMM, st);
+    timer_end(tm, TK_DX_GEMM, st);
     QLK_TRY(e);
   }
   // dA = s U^T X: rows j (U^T, transposed), cols k (X^T, transposed), and
@@ -970,19 +860,6 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
                      actual_splits(M, plan.m_splits_a), na, dA, part_b, actual_splits(M, plan.m_splits_b),
                      nb, dB, blocks_a, s);
   return hipGetLastError();
-}
-
-hipError_t launch_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, const LoraLinear& gate,
-                          const LoraLinear& up, const uint16_t* G, const uint16_t* U,
-                          const uint16_t* Tg, const uint16_t* Tu, uint16_t* dG, uint16_t* dU,
-                          uint16_t* dX, float* dAg, float* dBg, float* dAu, float* dBu,
-                          bool accumulate_dx, void* ws, hipStream_t st) {
-  const int64_t K = gate.w.K, I = gate.w.N;
-  QLK_TRY(launch_silu_mul_bwd(dH, G, U, M * I, dG, dU, st));
-  QLK_TRY(launch_qlora_bwd(dG, X, M, gate.w, gate.A, gate.B, gate.r, gate.s, Tg, dX, dAg, dBg,
-                           accumulate_dx, ws, plan_bwd(M, K, I, gate.r), st));
-  return launch_qlora_bwd(dU, X, M, up.w, up.A, up.B, up.r, up.s, Tu, dX, dAu, dBu, true, ws,
-                          plan_bwd(M, K, I, up.r), st);
 }
 
 }  // namespace qlk

@@ -443,18 +443,18 @@ k_lora_down_partial(const uint16_t* __restrict__ X, int M, int64_t K, const uint
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
-                       hipStream_t st, const uint16_t* Xa) {
+                       hipStream_t st, const uint16_t* Xa, const Timing* tm) {
   hipLaunchKernelGGL(k_lora_down_partial, dim3((r + 31) / 32, kTSplits), dim3(256), 0, st,
                      Xa ? Xa : X, (int)M, w.K, A, r, Tpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((w.N + 63) / 64);
-  timer_begin(TK_GEMV, st);
+  timer_begin(tm, TK_GEMV, st);
   if ((w.K / kBlock) % (4 * kGemvSS) == 0)
     hipLaunchKernelGGL(k_gemv_dma<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
   else
     hipLaunchKernelGGL(k_gemv_nf4<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
-  timer_end(TK_GEMV, st);
+  timer_end(tm, TK_GEMV, st);
   return hipGetLastError();
 }
 

@@ -28,6 +28,22 @@ hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const
 hipError_t launch_lora_dropout(const uint16_t* X, int64_t numel, uint32_t threshold, float scale,
                                uint64_t seed, uint16_t* Xd, uint32_t* mask, hipStream_t st);
 
+// Measurement: caller-owned HIP events recorded on the launch stream around
+// individual launches (a null event records nothing; a null Timing times
+// nothing).  Passed down per call: the library keeps no timing state.
+enum TimedKernel { TK_NONE = 0, TK_FWD_GEMM = 1, TK_DX_GEMM = 2, TK_GEMV = 3, TK_DX_DEQUANT = 4,
+                   TK_COUNT = 5 };
+struct Timing {
+  hipEvent_t start[TK_COUNT];
+  hipEvent_t stop[TK_COUNT];
+};
+inline void timer_begin(const Timing* t, int kernel, hipStream_t st) {
+  if (t && t->start[kernel]) (void)hipEventRecord(t->start[kernel], st);
+}
+inline void timer_end(const Timing* t, int kernel, hipStream_t st) {
+  if (t && t->stop[kernel]) (void)hipEventRecord(t->stop[kernel], st);
+}
+
 // Base weight [N, K] as stored: NF4 (packed, codes, scales, mean) or, for
 // the unquantised comparison path, plain bf16 (`bf16` non-null, the NF4
 // fields unused).
@@ -70,15 +86,18 @@ struct BwdPlan {
 };
 // Token count from which the backward dequantises the NF4 weight once.
 constexpr int64_t kDequantDxMinM = 1024;
-FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r);
-BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r);
+// nf4: the base weight is NF4 (only the NF4 register-decode forward splits
+// its contraction); dx: the backward computes dX (its bf16 weight copy and
+// split partials are needed only then).
+FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r, bool nf4 = true);
+BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r, bool dx = true);
 
 // Xa: input of the adapter's down projection (the dropout output); null
 // means X itself.
 hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                             const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T_out,
                             void* ws, const FwdPlan& plan, hipStream_t st,
-                            const uint16_t* Xa = nullptr);
+                            const uint16_t* Xa = nullptr, const Timing* tm = nullptr);
 // Workgroup tile rows walked together by tile_coords (balances the operand
 // footprints each XCD keeps in its L2).
 int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes);
@@ -97,8 +116,9 @@ hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, c
                             const uint16_t* Bg, int rg, float sg, const NF4Weight& wu,
                             const uint16_t* Tu, const uint16_t* Bu, int ru, float su, uint16_t* G,
                             uint16_t* U, uint16_t* H, hipStream_t st);
-// The gated MLP's gate/up forward: the fused kernel where it applies, else
-// two layer forwards and the elementwise gating.
+// The gated MLP's gate/up forward in one kernel (with the two T launches
+// before it), taken when mlp_fwd_fused(M, K); the caller composes the two
+// layer forwards and the gating otherwise.  Needs no workspace.
 struct LoraLinear {
   NF4Weight w;
   const uint16_t* A;
@@ -106,16 +126,10 @@ struct LoraLinear {
   int r;
   float s;
 };
+bool mlp_fwd_fused(int64_t M, int64_t K);
 hipError_t launch_mlp_fwd(const uint16_t* X, int64_t M, const LoraLinear& gate,
                           const LoraLinear& up, uint16_t* G, uint16_t* U, uint16_t* H,
-                          uint16_t* Tg, uint16_t* Tu, void* ws, size_t ws_bytes, hipStream_t st);
-// Its backward from dH: dG, dU by the elementwise gating backward, then the
-// two layer backwards, the second accumulating into dX.
-hipError_t launch_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, const LoraLinear& gate,
-                          const LoraLinear& up, const uint16_t* G, const uint16_t* U,
-                          const uint16_t* Tg, const uint16_t* Tu, uint16_t* dG, uint16_t* dU,
-                          uint16_t* dX, float* dAg, float* dBg, float* dAu, float* dBu,
-                          bool accumulate_dx, void* ws, hipStream_t st);
+                          uint16_t* Tg, uint16_t* Tu, hipStream_t st);
 // dX = dY W_hat (+ s U A) for N a multiple of 256 (else the tile engine runs).
 bool dx_nf4_supported(int64_t N);
 // With a dropout mask (bit per element of dX, row-major), the adapter term
@@ -151,7 +165,7 @@ hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t
                          int r, uint16_t* out, hipStream_t st);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
-                       hipStream_t st, const uint16_t* Xa = nullptr);
+                       hipStream_t st, const uint16_t* Xa = nullptr, const Timing* tm = nullptr);
 // X is the adapter input (the dropout output Xd when mask is non-null): it
 // feeds T (when not given) and dA.  mask/keep_scale: dropout of the adapter
 // input, applied to the adapter term of dX.
@@ -159,18 +173,20 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
                             const uint16_t* A, const uint16_t* B, int r, float s,
                             const uint16_t* T, uint16_t* dX, float* dA, float* dB,
                             bool accumulate_dx, void* ws, const BwdPlan& plan, hipStream_t st,
-                            const uint32_t* mask = nullptr, float keep_scale = 1.0f);
+                            const uint32_t* mask = nullptr, float keep_scale = 1.0f,
+                            const Timing* tm = nullptr);
 
-// Measurement hook: events recorded around individual launches.
-enum TimedKernel { TK_NONE = 0, TK_FWD_GEMM = 1, TK_DX_GEMM = 2, TK_GEMV = 3, TK_DX_DEQUANT = 4,
-                   TK_COUNT = 5 };
-void set_kernel_timer(int kernel, hipEvent_t start, hipEvent_t stop);
-void timer_begin(int kernel, hipStream_t st);
-void timer_end(int kernel, hipStream_t st);
 
 // W_merged = bf16(w_hat + s B A), bf16 [N, K].
 hipError_t launch_merge(const NF4Weight& w, const uint16_t* A, const uint16_t* B, int r, float s,
                         uint16_t* out, hipStream_t st);
+
+// dst [rows_dst, cols_dst] = src [rows_src, cols_src] zero-extended or cut
+// (row-major, contiguous): adapter-rank padding at the boundary.
+hipError_t launch_pad2d(const uint16_t* src, int64_t rows_src, int64_t cols_src, uint16_t* dst,
+                        int64_t rows_dst, int64_t cols_dst, hipStream_t st);
+hipError_t launch_pad2d(const float* src, int64_t rows_src, int64_t cols_src, float* dst,
+                        int64_t rows_dst, int64_t cols_dst, hipStream_t st);
 
 hipError_t launch_silu_mul_fwd(const uint16_t* G, const uint16_t* U, int64_t n, uint16_t* H,
                                hipStream_t st);

@@ -79,7 +79,18 @@ k_merge(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
     for (int nb = 0; nb < 2; ++nb) {
       const int64_t n = n0 + 32 * nb + c;
       uint4 av = make_uint4(0, 0, 0, 0);
-      if (n < N && r0 + 8 * h < r) av = *reinterpret_cast<const uint4*>(B + n * r + r0 + 8 * h);
+      if (n < N && r0 + 8 * h < r) {
+        const uint16_t* bp = B + n * r + r0 + 8 * h;
+        if ((r & 7) == 0) {
+          av = *reinterpret_cast<const uint4*>(bp);
+        } else {   // rows of B are not 16-byte aligned: eight 2-byte loads, zero past r
+          uint32_t e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] = r0 + 8 * h + i < r ? bp[i] : 0u;
+          av = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                          e[6] | (e[7] << 16));
+        }
+      }
       acc[nb] = mfma_32x32x16(__builtin_bit_cast(bf16x8_t, av), bop, acc[nb]);
     }
     __syncthreads();   // before the next chunk overwrites `as`

@@ -14,7 +14,50 @@ constexpr int kDQBlock = 256;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;   // keeps every tile index in int
 constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
 
+constexpr int kMaxRank = 256;
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The kernels read adapter rows (A, B, T, U) as 16-byte pieces, so they take
+// a rank that is a multiple of 8.  Any other rank r is run as the next
+// multiple of 8, rp, on zero-padded copies of A (extra zero rows) and B
+// (extra zero columns) in the workspace; the padded T, U, dA and dB then hold
+// zeros in the extra rows or columns, every product the caller sees is the
+// same sum (plus exact zero terms), and T, dA and dB are cut back to r
+// columns or rows.  s stays alpha / r.
+inline int padded_rank(int r) { return (r + 7) & ~7; }
+struct PadPlan {
+  int rp;
+  size_t off_A, off_B, off_T, off_dA, off_dB, bytes;
+};
+// `base` is the kernels' own workspace need for rank rp; the padded copies
+// follow it.
+PadPlan plan_pad(size_t base, int64_t M, int64_t K, int64_t N, int r, bool bwd) {
+  PadPlan p{};
+  p.rp = padded_rank(r);
+  size_t off = align256(base);
+  if (p.rp != r) {
+    const size_t rp = (size_t)p.rp;
+    p.off_A = off; off += align256(rp * K * 2);
+    p.off_B = off; off += align256((size_t)N * rp * 2);
+    p.off_T = off; off += align256((size_t)M * rp * 2);
+    if (bwd) {
+      p.off_dA = off; off += align256(rp * K * 4);
+      p.off_dB = off; off += align256((size_t)N * rp * 4);
+    }
+    p.bytes = off;
+  } else {
+    p.bytes = base;
+  }
+  return p;
+}
+PadPlan fwd_layout(int64_t M, int64_t K, int64_t N, int r, bool nf4) {
+  return plan_pad(qlk::plan_fwd(M, K, N, padded_rank(r), nf4).bytes, M, K, N, r, false);
+}
+PadPlan bwd_layout(int64_t M, int64_t K, int64_t N, int r, bool dx) {
+  return plan_pad(qlk::plan_bwd(M, K, N, padded_rank(r), dx).bytes, M, K, N, r, true);
+}
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int launch_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_LAUNCH; }
 
@@ -41,7 +84,7 @@ int check_linear_common(const uint16_t* X, int64_t M, int64_t K, int64_t N, cons
   int st = check_weight_shape(N, K);
   if (st) return st;
   if (N % 8 != 0) return QLORA_ERR_SHAPE;
-  if (r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_SHAPE;
+  if (r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
   // The kernels address X, dY, Y, dX and the stored weight with 32-bit
   // buffer offsets and mark out-of-range lanes with offset 2^31.
   if (M * K * 2 >= kMaxBufferBytes || M * N * 2 >= kMaxBufferBytes || weight_bytes >= kMaxBufferBytes)
@@ -86,34 +129,66 @@ qlk::NF4Weight weight_bf16(const uint16_t* W, int64_t N, int64_t K) {
 int fwd_common(const uint16_t* X, int64_t M, int64_t K, int64_t N, const qlk::NF4Weight& w,
                const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
                uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream,
-               const uint16_t* Xa = nullptr) {
+               const uint16_t* Xa = nullptr, const qlk::Timing* tm = nullptr) {
   if (!Y) return QLORA_ERR_NULL;
   if (!aligned16(Y) || (T_out && !aligned16(T_out))) return QLORA_ERR_ALIGN;
-  const qlk::FwdPlan plan = qlk::plan_fwd(M, K, N, r);
-  if (workspace_bytes < plan.bytes || (plan.bytes && !workspace)) return QLORA_ERR_WORKSPACE;
+  const int rp = padded_rank(r);
+  const qlk::FwdPlan plan = qlk::plan_fwd(M, K, N, rp, w.bf16 == nullptr);
+  const PadPlan pad = plan_pad(plan.bytes, M, K, N, r, false);
+  if (workspace_bytes < pad.bytes || (pad.bytes && !workspace)) return QLORA_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return QLORA_ERR_ALIGN;
   const float s = alpha / (float)r;
-  return launch_status(qlk::launch_qlora_fwd(X, M, w, A, B, r, s, Y, T_out, workspace, plan,
-                                             as_stream(stream), Xa));
+  const hipStream_t st = as_stream(stream);
+  if (rp == r)
+    return launch_status(qlk::launch_qlora_fwd(X, M, w, A, B, r, s, Y, T_out, workspace, plan, st,
+                                               Xa, tm));
+  char* base = reinterpret_cast<char*>(workspace);
+  uint16_t* Ap = reinterpret_cast<uint16_t*>(base + pad.off_A);
+  uint16_t* Bp = reinterpret_cast<uint16_t*>(base + pad.off_B);
+  uint16_t* Tp = reinterpret_cast<uint16_t*>(base + pad.off_T);
+  hipError_t e = qlk::launch_pad2d(A, r, K, Ap, rp, K, st);
+  if (e == hipSuccess) e = qlk::launch_pad2d(B, N, r, Bp, N, rp, st);
+  if (e == hipSuccess) e = qlk::launch_qlora_fwd(X, M, w, Ap, Bp, rp, s, Y, Tp, workspace, plan, st, Xa, tm);
+  if (e == hipSuccess && T_out) e = qlk::launch_pad2d(Tp, M, rp, T_out, M, r, st);
+  return launch_status(e);
 }
 
 int bwd_common(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
                const qlk::NF4Weight& w, const uint16_t* A, const uint16_t* B, int r, float alpha,
                const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags, void* workspace,
                size_t workspace_bytes, void* stream, const uint32_t* mask = nullptr,
-               float keep_scale = 1.0f) {
+               float keep_scale = 1.0f, const qlk::Timing* tm = nullptr) {
   if (!dY || !dA || !dB) return QLORA_ERR_NULL;
   if (flags & ~QLORA_BWD_ACCUMULATE_DX) return QLORA_ERR_ARG;
   if (!aligned16(dY) || !aligned16(dA) || !aligned16(dB) || (dX && !aligned16(dX)) ||
       (T && !aligned16(T)))
     return QLORA_ERR_ALIGN;
-  const qlk::BwdPlan plan = qlk::plan_bwd(M, K, N, r);
-  if (workspace_bytes < plan.bytes || !workspace) return QLORA_ERR_WORKSPACE;
+  const int rp = padded_rank(r);
+  const qlk::BwdPlan plan = qlk::plan_bwd(M, K, N, rp, dX != nullptr);
+  const PadPlan pad = plan_pad(plan.bytes, M, K, N, r, true);
+  if (workspace_bytes < pad.bytes || !workspace) return QLORA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
   const float s = alpha / (float)r;
-  return launch_status(qlk::launch_qlora_bwd(dY, X, M, w, A, B, r, s, T, dX, dA, dB,
-                                             (flags & QLORA_BWD_ACCUMULATE_DX) != 0, workspace,
-                                             plan, as_stream(stream), mask, keep_scale));
+  const bool acc = (flags & QLORA_BWD_ACCUMULATE_DX) != 0;
+  const hipStream_t st = as_stream(stream);
+  if (rp == r)
+    return launch_status(qlk::launch_qlora_bwd(dY, X, M, w, A, B, r, s, T, dX, dA, dB, acc,
+                                               workspace, plan, st, mask, keep_scale, tm));
+  char* base = reinterpret_cast<char*>(workspace);
+  uint16_t* Ap = reinterpret_cast<uint16_t*>(base + pad.off_A);
+  uint16_t* Bp = reinterpret_cast<uint16_t*>(base + pad.off_B);
+  uint16_t* Tp = reinterpret_cast<uint16_t*>(base + pad.off_T);
+  float* dAp = reinterpret_cast<float*>(base + pad.off_dA);
+  float* dBp = reinterpret_cast<float*>(base + pad.off_dB);
+  hipError_t e = qlk::launch_pad2d(A, r, K, Ap, rp, K, st);
+  if (e == hipSuccess) e = qlk::launch_pad2d(B, N, r, Bp, N, rp, st);
+  if (e == hipSuccess && T) e = qlk::launch_pad2d(T, M, r, Tp, M, rp, st);
+  if (e == hipSuccess)
+    e = qlk::launch_qlora_bwd(dY, X, M, w, Ap, Bp, rp, s, T ? Tp : nullptr, dX, dAp, dBp, acc,
+                              workspace, plan, st, mask, keep_scale, tm);
+  if (e == hipSuccess) e = qlk::launch_pad2d(dAp, rp, K, dA, r, K, st);
+  if (e == hipSuccess) e = qlk::launch_pad2d(dBp, N, rp, dB, N, r, st);
+  return launch_status(e);
 }
 
 int check_codebook(const float* levels) {
@@ -121,6 +196,18 @@ int check_codebook(const float* levels) {
   for (int i = 0; i < 16; ++i)
     if (!isfinite(levels[i]) || (i > 0 && !(levels[i - 1] < levels[i]))) return QLORA_ERR_ARG;
   return QLORA_OK;
+}
+
+// The caller's events (hipEvent_t as void*) in the launchers' form; null for
+// an untimed call.
+const qlk::Timing* to_timing(const qlora_timing* t, qlk::Timing& out) {
+  if (!t) return nullptr;
+  static_assert(QLORA_KERNEL_COUNT == qlk::TK_COUNT, "one event slot per timed kernel");
+  for (int k = 0; k < qlk::TK_COUNT; ++k) {
+    out.start[k] = reinterpret_cast<hipEvent_t>(t->start[k]);
+    out.stop[k] = reinterpret_cast<hipEvent_t>(t->stop[k]);
+  }
+  return &out;
 }
 
 bool valid_p(double p) { return p >= 0.0 && p < 1.0; }   // false for NaN
@@ -215,7 +302,7 @@ int qlora_merge(const uint8_t* packed, const uint8_t* codes, const float* scales
   if (blocksize != kBlock || dq_blocksize != kDQBlock) return QLORA_ERR_UNSUPPORTED;
   int st = check_weight_shape(N, K);
   if (st) return st;
-  if (N % 8 != 0 || r < 8 || r > 256 || r % 8 != 0) return QLORA_ERR_SHAPE;
+  if (N % 8 != 0 || r < 1 || r > kMaxRank) return QLORA_ERR_SHAPE;
   if (N * K > ((int64_t)1 << 40) || (N + 63) / 64 > 65535) return QLORA_ERR_SHAPE;
   if (!isfinite(alpha)) return QLORA_ERR_ARG;
   if (!aligned16(packed) || !aligned16(codes) || !aligned16(scales) || !aligned16(mean) ||
@@ -226,18 +313,29 @@ int qlora_merge(const uint8_t* packed, const uint8_t* codes, const float* scales
 }
 
 size_t qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int r, int is_bwd) {
-  if (M <= 0 || M > kMaxDim || check_weight_shape(N, K) || r < 8 || r > 256 || r % 8) return 0;
-  return is_bwd ? qlk::plan_bwd(M, K, N, r).bytes : qlk::plan_fwd(M, K, N, r).bytes;
+  if (M <= 0 || M > kMaxDim || check_weight_shape(N, K) || r < 1 || r > kMaxRank) return 0;
+  return is_bwd ? bwd_layout(M, K, N, r, true).bytes : fwd_layout(M, K, N, r, true).bytes;
+}
+
+int qlora_linear_fwd_timed(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                           const uint8_t* packed, const uint8_t* codes, const float* scales,
+                           const float* mean, const uint16_t* A, const uint16_t* B, int r,
+                           float alpha, uint16_t* Y, uint16_t* T_out, void* workspace,
+                           size_t workspace_bytes, void* stream, const qlora_timing* timing) {
+  int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
+  if (st) return st;
+  qlk::Timing tm;
+  const qlk::Timing* tp = to_timing(timing, tm);
+  return fwd_common(X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, Y,
+                    T_out, workspace, workspace_bytes, stream, nullptr, tp);
 }
 
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                      const uint8_t* codes, const float* scales, const float* mean,
                      const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* Y,
                      uint16_t* T_out, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
-  if (st) return st;
-  return fwd_common(X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, Y,
-                    T_out, workspace, workspace_bytes, stream);
+  return qlora_linear_fwd_timed(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha, Y, T_out,
+                                workspace, workspace_bytes, stream, nullptr);
 }
 
 int qlora_linear_fwd_dropout(const uint16_t* X, const uint16_t* Xd, int64_t M, int64_t K,
@@ -263,15 +361,27 @@ int qlora_linear_fwd_bf16(const uint16_t* X, int64_t M, int64_t K, int64_t N, co
                     workspace_bytes, stream);
 }
 
+int qlora_linear_bwd_timed(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K,
+                           int64_t N, const uint8_t* packed, const uint8_t* codes,
+                           const float* scales, const float* mean, const uint16_t* A,
+                           const uint16_t* B, int r, float alpha, const uint16_t* T, uint16_t* dX,
+                           float* dA, float* dB, int flags, void* workspace,
+                           size_t workspace_bytes, void* stream, const qlora_timing* timing) {
+  int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
+  if (st) return st;
+  qlk::Timing tm;
+  const qlk::Timing* tp = to_timing(timing, tm);
+  return bwd_common(dY, X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, T,
+                    dX, dA, dB, flags, workspace, workspace_bytes, stream, nullptr, 1.0f, tp);
+}
+
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
                      const uint8_t* packed, const uint8_t* codes, const float* scales,
                      const float* mean, const uint16_t* A, const uint16_t* B, int r, float alpha,
                      const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
-  if (st) return st;
-  return bwd_common(dY, X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, T,
-                    dX, dA, dB, flags, workspace, workspace_bytes, stream);
+  return qlora_linear_bwd_timed(dY, X, M, K, N, packed, codes, scales, mean, A, B, r, alpha, T,
+                                dX, dA, dB, flags, workspace, workspace_bytes, stream, nullptr);
 }
 
 int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* Xd, const uint32_t* mask,
@@ -306,22 +416,41 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t I,
                   size_t workspace_bytes, void* stream) {
   if (!gate || !up) return QLORA_ERR_NULL;
   const qlora_lora_linear* lin[2] = {gate, up};
-  qlk::LoraLinear L[2];
-  for (int j = 0; j < 2; ++j) {
-    const qlora_lora_linear& l = *lin[j];
-    int st = check_linear(X, M, K, I, l.packed, l.codes, l.scales, l.mean, l.A, l.B, l.r, l.alpha);
+  for (const qlora_lora_linear* l : lin) {
+    int st = check_linear(X, M, K, I, l->packed, l->codes, l->scales, l->mean, l->A, l->B, l->r,
+                          l->alpha);
     if (st) return st;
-    L[j].w = weight(l.packed, l.codes, l.scales, l.mean, I, K);
-    L[j].A = l.A; L[j].B = l.B; L[j].r = l.r; L[j].s = l.alpha / (float)l.r;
-    const size_t need = qlk::plan_fwd(M, K, I, l.r).bytes;
-    if (workspace_bytes < need || (need && !workspace)) return QLORA_ERR_WORKSPACE;
   }
   if (!G || !U || !H || !Tg || !Tu) return QLORA_ERR_NULL;
   if (!aligned16(G) || !aligned16(U) || !aligned16(H) || !aligned16(Tg) || !aligned16(Tu) ||
       (workspace && !aligned16(workspace)))
     return QLORA_ERR_ALIGN;
-  return launch_status(qlk::launch_mlp_fwd(X, M, L[0], L[1], G, U, H, Tg, Tu, workspace,
-                                           workspace_bytes, as_stream(stream)));
+  const bool whole_rank = padded_rank(gate->r) == gate->r && padded_rank(up->r) == up->r;
+  if (whole_rank && qlk::mlp_fwd_fused(M, K)) {
+    // One kernel for both projections and the gating; T of each projection
+    // goes straight to Tg and Tu, so no workspace is needed.
+    qlk::LoraLinear L[2];
+    for (int j = 0; j < 2; ++j) {
+      const qlora_lora_linear& l = *lin[j];
+      L[j].w = weight(l.packed, l.codes, l.scales, l.mean, I, K);
+      L[j].A = l.A; L[j].B = l.B; L[j].r = l.r; L[j].s = l.alpha / (float)l.r;
+    }
+    return launch_status(qlk::launch_mlp_fwd(X, M, L[0], L[1], G, U, H, Tg, Tu, as_stream(stream)));
+  }
+  // Otherwise the two layer forwards and the elementwise gating, one after
+  // the other on the stream (they share the workspace).
+  for (const qlora_lora_linear* l : lin) {
+    const size_t need = fwd_layout(M, K, I, l->r, true).bytes;
+    if (workspace_bytes < need || (need && !workspace)) return QLORA_ERR_WORKSPACE;
+  }
+  int st = fwd_common(X, M, K, I, weight(gate->packed, gate->codes, gate->scales, gate->mean, I, K),
+                      gate->A, gate->B, gate->r, gate->alpha, G, Tg, workspace, workspace_bytes,
+                      stream);
+  if (st) return st;
+  st = fwd_common(X, M, K, I, weight(up->packed, up->codes, up->scales, up->mean, I, K), up->A,
+                  up->B, up->r, up->alpha, U, Tu, workspace, workspace_bytes, stream);
+  if (st) return st;
+  return launch_status(qlk::launch_silu_mul_fwd(G, U, M * I, H, as_stream(stream)));
 }
 
 int qlora_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, int64_t K, int64_t I,
@@ -331,14 +460,11 @@ int qlora_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, int64_t K, i
                   int flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (!gate || !up) return QLORA_ERR_NULL;
   const qlora_lora_linear* lin[2] = {gate, up};
-  qlk::LoraLinear L[2];
-  for (int j = 0; j < 2; ++j) {
-    const qlora_lora_linear& l = *lin[j];
-    int st = check_linear(X, M, K, I, l.packed, l.codes, l.scales, l.mean, l.A, l.B, l.r, l.alpha);
+  for (const qlora_lora_linear* l : lin) {
+    int st = check_linear(X, M, K, I, l->packed, l->codes, l->scales, l->mean, l->A, l->B, l->r,
+                          l->alpha);
     if (st) return st;
-    L[j].w = weight(l.packed, l.codes, l.scales, l.mean, I, K);
-    L[j].A = l.A; L[j].B = l.B; L[j].r = l.r; L[j].s = l.alpha / (float)l.r;
-    if (workspace_bytes < qlk::plan_bwd(M, K, I, l.r).bytes || !workspace)
+    if (workspace_bytes < bwd_layout(M, K, I, l->r, true).bytes || !workspace)
       return QLORA_ERR_WORKSPACE;
   }
   if (!dH || !G || !U || !Tg || !Tu || !dG || !dU || !dX || !dAg || !dBg || !dAu || !dBu)
@@ -347,9 +473,18 @@ int qlora_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, int64_t K, i
   const void* ptrs[] = {dH, G, U, Tg, Tu, dG, dU, dX, dAg, dBg, dAu, dBu, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return QLORA_ERR_ALIGN;
-  return launch_status(qlk::launch_mlp_bwd(dH, X, M, L[0], L[1], G, U, Tg, Tu, dG, dU, dX, dAg,
-                                           dBg, dAu, dBu, (flags & QLORA_BWD_ACCUMULATE_DX) != 0,
-                                           workspace, as_stream(stream)));
+  // dG and dU feed three products each (the dX GEMM, U = dY B and dB), so the
+  // gating backward materialises them; then the two layer backwards, the up
+  // projection's adding its dX to the gate's.
+  int st = launch_status(qlk::launch_silu_mul_bwd(dH, G, U, M * I, dG, dU, as_stream(stream)));
+  if (st) return st;
+  st = bwd_common(dG, X, M, K, I, weight(gate->packed, gate->codes, gate->scales, gate->mean, I, K),
+                  gate->A, gate->B, gate->r, gate->alpha, Tg, dX, dAg, dBg, flags, workspace,
+                  workspace_bytes, stream);
+  if (st) return st;
+  return bwd_common(dU, X, M, K, I, weight(up->packed, up->codes, up->scales, up->mean, I, K),
+                    up->A, up->B, up->r, up->alpha, Tu, dX, dAu, dBu, QLORA_BWD_ACCUMULATE_DX,
+                    workspace, workspace_bytes, stream);
 }
 
 int silu_mul_fwd(const uint16_t* G, const uint16_t* Up, int64_t n, uint16_t* H, void* stream) {
@@ -393,13 +528,6 @@ const char* qlora_strerror(int status) {
     case QLORA_ERR_ARG: return "invalid argument";
     default: return "unknown status";
   }
-}
-
-int qlora_set_kernel_timer(int kernel, void* ev_start, void* ev_stop) {
-  if (kernel <= 0 || kernel >= QLORA_KERNEL_COUNT) return QLORA_ERR_ARG;
-  qlk::set_kernel_timer(kernel, reinterpret_cast<hipEvent_t>(ev_start),
-                        reinterpret_cast<hipEvent_t>(ev_stop));
-  return QLORA_OK;
 }
 
 int qlora_version(void) { return 100; }

@@ -17,8 +17,9 @@
  *     Every call only enqueues work on that stream and returns immediately.
  *   - Outputs are overwritten (never accumulated) unless a flag says
  *     otherwise.  The library allocates no device memory: scratch space comes
- *     from the caller's `workspace`.  Its only mutable global state is the
- *     optional measurement hook (qlora_set_kernel_timer).
+ *     from the caller's `workspace`.  It holds no mutable state, so calls on
+ *     different streams with different workspaces may run concurrently; two
+ *     calls that share a workspace must be ordered (e.g. on one stream).
  *   - Calls return a status code (QLORA_* below).  All argument checks run on
  *     the host before any launch, so a non-zero status means nothing was
  *     enqueued.  Faults inside a kernel surface at the next stream
@@ -48,7 +49,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define QLORA_OK                 0
 #define QLORA_ERR_NULL          -1  /* a required pointer is NULL                   */
-#define QLORA_ERR_SHAPE         -2  /* M,N,K <= 0; K % 64; N % 8; r % 8 or r > 256;
+#define QLORA_ERR_SHAPE         -2  /* M,N,K <= 0; K % 64; N % 8; r outside [1, 256];
                                        N*K odd or too large; an operand >= 2 GiB      */
 #define QLORA_ERR_UNSUPPORTED   -3  /* blocksize != 64 or dq_blocksize != 256       */
 #define QLORA_ERR_ALIGN         -4  /* a pointer is not 16-byte aligned             */
@@ -136,9 +137,14 @@ int codebook_dequant(const uint8_t* packed, const uint8_t* codes, const float* s
  * shape that does not split.  Results meet
  * |err|_F / |ref|_F <= 1e-2 and max|err| <= 3e-2 max|ref| against an exact
  * evaluation of the same bf16 inputs.
- * Requires 1 <= M, K % 64 == 0, N % 8 == 0, r % 8 == 0, 8 <= r <= 256, each
- * of X, Y (2 M K, 2 M N bytes) and the packed weight (N K / 2 bytes) under
- * 2 GiB, and workspace_bytes >= qlora_workspace_bytes(M, K, N, r, 0). */
+ * Requires 1 <= M, K % 64 == 0, N % 8 == 0 (every row of X, Y, dY and dX
+ * starts on a 16-byte boundary: the kernels move rows in 128-bit pieces),
+ * 1 <= r <= 256, each of X, Y (2 M K, 2 M N bytes) and the packed weight
+ * (N K / 2 bytes) under 2 GiB, and workspace_bytes >=
+ * qlora_workspace_bytes(M, K, N, r, 0).  A rank that is not a multiple of 8
+ * runs as the next multiple of 8 on zero-padded copies of A and B in the
+ * workspace (the kernels read adapter rows in 16-byte pieces); the padding
+ * adds only exact zeros, and s stays alpha / r. */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
                      const uint8_t* packed, const uint8_t* codes, const float* scales,
                      const float* mean, const uint16_t* A, const uint16_t* B,
@@ -260,12 +266,13 @@ typedef struct qlora_lora_linear {
  *   X  bf16 [M, K];   G, U, H  bf16 [M, I];   Tg, Tu  bf16 [M, rg], [M, ru]
  * G, U, Tg and Tu are what the backward needs.  G and U are bit-identical to
  * qlora_linear_fwd on each projection and H to silu_mul_fwd(G, U).  For
- * M > 16 and K % 256 == 0 one kernel computes G and U tile by tile and writes
- * H from the same tile (no second pass over G and U); other shapes run the
- * two layer forwards and the elementwise gating.
+ * M > 16, K % 256 == 0 and both ranks multiples of 8, one kernel computes G
+ * and U tile by tile and writes H from the same tile (no second pass over G
+ * and U) and needs no workspace; other shapes run the two layer forwards and
+ * the elementwise gating.
  * Requires the shape rules of qlora_linear_fwd for each projection (I plays
  * N), both weights [I, K], and workspace_bytes >= qlora_workspace_bytes(M, K,
- * I, r, 0) for both r. */
+ * I, r, 0) for both r (always sufficient). */
 int qlora_mlp_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t I,
                   const qlora_lora_linear* gate, const qlora_lora_linear* up,
                   uint16_t* G, uint16_t* U, uint16_t* H, uint16_t* Tg, uint16_t* Tu,
@@ -303,8 +310,8 @@ int qlora_mlp_bwd(const uint16_t* dH, const uint16_t* X, int64_t M, int64_t K, i
  * B A is accumulated in fp32 (MFMA), added with one fp32 fused multiply-add
  * and rounded to bf16 once; each value is within one bf16 rounding step of
  * the exactly evaluated merge.
- * Requires K % 64 == 0, N % 8 == 0, r % 8 == 0, 8 <= r <= 256,
- * blocksize == 64, dq_blocksize == 256, finite alpha. */
+ * Requires K % 64 == 0, N % 8 == 0, 1 <= r <= 256, blocksize == 64,
+ * dq_blocksize == 256, finite alpha. */
 int qlora_merge(const uint8_t* packed, const uint8_t* codes, const float* scales,
                 const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
                 const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* W_merged,
@@ -320,7 +327,7 @@ int silu_mul_fwd(const uint16_t* G, const uint16_t* Up, int64_t n, uint16_t* H,
 int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int64_t n,
                  uint16_t* dG, uint16_t* dUp, void* stream);
 
-/* ---- measurement hook ---------------------------------------------------- */
+/* ---- measurement ---------------------------------------------------------- */
 
 /* Internal kernels that can be timed individually. */
 #define QLORA_KERNEL_FWD_GEMM   1  /* fused dequant GEMM  Y = X W_hat^T + s T B^T     */
@@ -330,13 +337,30 @@ int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int6
                                        launched together with U = dY B                 */
 #define QLORA_KERNEL_COUNT      5
 
-/* While set, each launch of `kernel` is bracketed by hipEventRecord(ev_start)
- * and hipEventRecord(ev_stop) on the stream of the call that launches it
- * (events are hipEvent_t passed as void*, created by the caller).  Passing
- * NULL events clears the slot.  The slots are process-wide and not
- * thread-safe: this is for benchmarks, not for production use.  Returns
- * QLORA_ERR_ARG for an unknown kernel id. */
-int qlora_set_kernel_timer(int kernel, void* ev_start, void* ev_stop);
+/* Caller-owned HIP events (hipEvent_t as void*), indexed by the kernel ids
+ * above (slot 0 unused).  A timed call records start[k] and stop[k] on its
+ * stream right before and after each launch of kernel k; NULL slots record
+ * nothing.  The struct is read during the call only. */
+typedef struct qlora_timing {
+  void* start[QLORA_KERNEL_COUNT];
+  void* stop[QLORA_KERNEL_COUNT];
+} qlora_timing;
+
+/* qlora_linear_fwd / qlora_linear_bwd with the launches of their dominant
+ * kernels bracketed by the caller's events (for benchmarks: an event record
+ * between two kernels breaks their back-to-back dispatch).  Same arguments,
+ * results and status codes; timing == NULL makes them the plain calls. */
+int qlora_linear_fwd_timed(const uint16_t* X, int64_t M, int64_t K, int64_t N,
+                           const uint8_t* packed, const uint8_t* codes, const float* scales,
+                           const float* mean, const uint16_t* A, const uint16_t* B, int r,
+                           float alpha, uint16_t* Y, uint16_t* T_out, void* workspace,
+                           size_t workspace_bytes, void* stream, const qlora_timing* timing);
+int qlora_linear_bwd_timed(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K,
+                           int64_t N, const uint8_t* packed, const uint8_t* codes,
+                           const float* scales, const float* mean, const uint16_t* A,
+                           const uint16_t* B, int r, float alpha, const uint16_t* T, uint16_t* dX,
+                           float* dA, float* dB, int flags, void* workspace,
+                           size_t workspace_bytes, void* stream, const qlora_timing* timing);
 
 /* ---- host-side helpers --------------------------------------------------- */
 

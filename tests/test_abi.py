@@ -89,6 +89,15 @@ def _fwd(**kw):
                                 a["Y"], a["T"], a["ws"], a["wsb"], a["stream"])
 
 
+def _fwd_bf16(**kw):
+    a = dict(X=D, M=16, K=256, N=256, W=D, A=D, B=D, r=8, alpha=16.0, Y=D, T=None, ws=D,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.qlora_linear_fwd_bf16(a["X"], a["M"], a["K"], a["N"], a["W"], a["A"], a["B"],
+                                     a["r"], a["alpha"], a["Y"], a["T"], a["ws"], a["wsb"],
+                                     a["stream"])
+
+
 def _bwd(**kw):
     a = dict(dY=D, X=D, M=16, K=256, N=256, packed=D, codes=D, scales=D, mean=D, A=D, B=D,
              r=8, alpha=16.0, T=None, dX=D, dA=D, dB=D, flags=0, ws=D, wsb=1 << 30,
@@ -107,14 +116,55 @@ def test_linear_validation(fn):
     assert fn(M=0) == q.ERR_SHAPE
     assert fn(K=96) == q.ERR_SHAPE          # K % 64
     assert fn(N=260) == q.ERR_SHAPE         # N % 8
-    assert fn(r=4) == q.ERR_SHAPE
-    assert fn(r=12) == q.ERR_SHAPE
+    assert fn(r=0) == q.ERR_SHAPE
+    assert fn(r=-3) == q.ERR_SHAPE
+    assert fn(r=257) == q.ERR_SHAPE
     assert fn(r=264) == q.ERR_SHAPE
     assert fn(alpha=float("nan")) == q.ERR_ARG
     assert fn(A=MIS) == q.ERR_ALIGN
     assert fn(ws=None, wsb=0) == q.ERR_WORKSPACE
     assert fn(wsb=16) == q.ERR_WORKSPACE
     assert fn(ws=MIS) == q.ERR_ALIGN
+
+
+@pytest.mark.parametrize("fn", [_fwd, _bwd])
+def test_any_rank_from_1_to_256_is_accepted_up_to_the_workspace(fn):
+    """Every rank in [1, 256] passes validation: with a workspace too small
+    by one byte the call stops at the workspace check (so nothing else was
+    refused), and ranks that are not multiples of 8 need room for the
+    zero-padded adapter copies."""
+    M, K, N = 16, 256, 256
+    is_bwd = 1 if fn is _bwd else 0
+    for r in (1, 4, 7, 8, 12, 24, 100, 255, 256):
+        need = lib.qlora_workspace_bytes(M, K, N, r, is_bwd)
+        assert need > 0, r
+        assert fn(r=r, wsb=need - 1) == q.ERR_WORKSPACE, r
+    # padding: r = 12 runs as 16 with room for padded A, B, T (and dA, dB)
+    pad = 16 * K * 2 + N * 16 * 2 + M * 16 * 2 + (16 * K * 4 + N * 16 * 4 if is_bwd else 0)
+    assert (lib.qlora_workspace_bytes(M, K, N, 12, is_bwd)
+            >= lib.qlora_workspace_bytes(M, K, N, 16, is_bwd) + pad)
+
+
+def _timing():
+    t = q.TimingC()
+    return ctypes.byref(t)
+
+
+def test_timed_entry_points_validate_like_the_plain_calls():
+    ff, fb = lib.qlora_linear_fwd_timed, lib.qlora_linear_bwd_timed
+    fwd = [D, 16, 256, 256, D, D, D, D, D, D, 8, 16.0, D, None, D, 1 << 30, None]
+    bwd = [D, D, 16, 256, 256, D, D, D, D, D, D, 8, 16.0, None, D, D, D, 0, D, 1 << 30, None]
+    for t in (None, _timing()):
+        for i, v, code in ((0, None, q.ERR_NULL), (2, 96, q.ERR_SHAPE), (10, 0, q.ERR_SHAPE),
+                           (11, float("nan"), q.ERR_ARG), (15, 16, q.ERR_WORKSPACE)):
+            a = list(fwd)
+            a[i] = v
+            assert ff(*a, t) == code, (i, v)
+        for i, v, code in ((0, None, q.ERR_NULL), (3, 96, q.ERR_SHAPE), (11, 257, q.ERR_SHAPE),
+                           (17, 2, q.ERR_ARG), (19, 16, q.ERR_WORKSPACE)):
+            a = list(bwd)
+            a[i] = v
+            assert fb(*a, t) == code, (i, v)
 
 
 def test_linear_output_validation():
@@ -131,7 +181,8 @@ def test_workspace_sizes():
     assert lib.qlora_workspace_bytes(2048, 4096, 4096, 16, 1) > 0
     assert lib.qlora_workspace_bytes(0, 256, 256, 8, 0) == 0
     assert lib.qlora_workspace_bytes(16, 100, 256, 8, 0) == 0
-    assert lib.qlora_workspace_bytes(16, 256, 256, 5, 1) == 0
+    assert lib.qlora_workspace_bytes(16, 256, 256, 0, 1) == 0
+    assert lib.qlora_workspace_bytes(16, 256, 256, 257, 1) == 0
     # the backward needs room for U and T at least
     assert lib.qlora_workspace_bytes(2048, 4096, 4096, 16, 1) >= 2 * 2048 * 16 * 2
     # from 1024 tokens on it also holds the once-dequantised bf16 weight
@@ -156,11 +207,22 @@ def test_workspace_holds_the_split_partials():
     assert lib.qlora_workspace_bytes(1024, K, N, 16, 1) < 2 * N * K + 1024 * K * 4
 
 
-def test_kernel_timer_validation():
-    assert lib.qlora_set_kernel_timer(0, None, None) == q.ERR_ARG
-    assert lib.qlora_set_kernel_timer(5, None, None) == q.ERR_ARG
-    for k in (1, 2, 3, 4):
-        assert lib.qlora_set_kernel_timer(k, None, None) == q.OK
+def test_split_partials_are_reserved_only_where_a_split_runs():
+    """Only the NF4 register-decode forward splits its contraction; the
+    bf16-base forward needs T alone, and a backward without dX needs no dX
+    partials.  A misaligned workspace of the right size gets past the size
+    check and stops at the alignment check (no launch), one byte less stops
+    at the size check."""
+    K = N = 4096
+    M, r = 256, 16
+    t_only = M * r * 2                       # T, the bf16 forward's whole need
+    assert _fwd_bf16(M=M, K=K, N=N, r=r, ws=MIS, wsb=t_only) == q.ERR_ALIGN
+    assert _fwd_bf16(M=M, K=K, N=N, r=r, ws=MIS, wsb=t_only - 1) == q.ERR_WORKSPACE
+    assert _fwd(M=M, K=K, N=N, r=r, ws=MIS, wsb=t_only) == q.ERR_WORKSPACE   # NF4: partials
+    full = lib.qlora_workspace_bytes(M, K, N, r, 1)
+    dx_parts = 8 * M * K * 4                 # 8 splits of the dX contraction
+    assert _bwd(M=M, K=K, N=N, r=r, dX=None, ws=MIS, wsb=full - dx_parts) == q.ERR_ALIGN
+    assert _bwd(M=M, K=K, N=N, r=r, ws=MIS, wsb=full - dx_parts) == q.ERR_WORKSPACE
 
 
 def test_silu_validation():
@@ -196,7 +258,7 @@ def test_merge_validation():
     assert call(dqbs=128) == q.ERR_UNSUPPORTED
     assert call(K=100) == q.ERR_SHAPE
     assert call(N=12) == q.ERR_SHAPE
-    assert call(r=12) == q.ERR_SHAPE
+    assert call(r=0) == q.ERR_SHAPE
     assert call(r=264) == q.ERR_SHAPE
     assert call(alpha=float("nan")) == q.ERR_ARG
     assert call(B=MIS) == q.ERR_ALIGN
@@ -277,7 +339,7 @@ def test_mlp_fwd_validation():
         return f(D, M, K, I, gp, upp, G, U, H, Tg, Tu, ws, wsb, None)
     assert call(gate=None) == q.ERR_NULL
     assert call(up=None) == q.ERR_NULL
-    assert call(up=q.LoraLinearC(D, D, D, D, D, D, 12, 32.0)) == q.ERR_SHAPE     # r % 8
+    assert call(up=q.LoraLinearC(D, D, D, D, D, D, 0, 32.0)) == q.ERR_SHAPE      # r < 1
     assert call(gate=q.LoraLinearC(D, None, D, D, D, D, 16, 32.0)) == q.ERR_NULL
     assert call(up=q.LoraLinearC(D, D, D, D, D, D, 16, float("inf"))) == q.ERR_ARG
     assert call(K=100) == q.ERR_SHAPE
@@ -286,6 +348,9 @@ def test_mlp_fwd_validation():
     assert call(Tu=None) == q.ERR_NULL
     assert call(U=MIS) == q.ERR_ALIGN
     assert call(M=4, ws=None, wsb=0) == q.ERR_WORKSPACE      # small M needs workspace
+    # the fused gate/up kernel (M > 16, whole ranks) needs none; a rank that
+    # is not a multiple of 8 runs the padded composition, which does
+    assert call(up=q.LoraLinearC(D, D, D, D, D, D, 12, 32.0), ws=None, wsb=0) == q.ERR_WORKSPACE
 
 
 def test_mlp_bwd_validation():
