@@ -441,11 +441,399 @@ k_lora_down_partial(const uint16_t* __restrict__ X, int M, int64_t K, const uint
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M forward with the contraction split over the waves of a workgroup
+// (k_gemv_split), taken when K is 2048, 4096 or 8192, r <= 64 and the weight
+// has at most 256 x 8 groups of 16 rows.
+//
+// The weight is read once from HBM, so the kernel has to keep every CU
+// streaming and spend as little issue time per weight as it can:
+//  * one 512-thread workgroup per CU (at most 256 workgroups); each owns a run
+//    of R rows (R a multiple of 16, the same for all but the last), so every
+//    CU moves the same number of bytes;
+//  * its 8 waves split K into 8 slices of S blocks; a wave keeps the
+//    activations of its slice in registers (as MFMA operands) and walks the
+//    workgroup's rows 16 at a time (a row group), so no activation is read
+//    twice; each wave leaves its partial product of every row group in LDS
+//    and the 8 slices are added once, at the end, in a fixed order (no
+//    barrier in the loop);
+//  * the weight goes straight from HBM into registers, 8 loads of 1 KB per
+//    wave in flight (a ring that runs across row groups): for M <= 8, lane
+//    (n = lane % 16, g = lane / 16) loads the 16 bytes [16 g, 16 g + 16) of
+//    the 64-byte run of row n covering two blocks (groups 0-1 block b, groups
+//    2-3 block b + 1); for M <= 16 the 8 bytes [8 g, 8 g + 8) of one block;
+//  * each packed byte is decoded to its two bf16 NF4 levels by one LDS read
+//    from a 64 KB table that gives every lane its own column (entry e of lane
+//    L at byte e * 256 + 4 L), so the reads never conflict; the address is one
+//    byte permute of the packed word and the lane's offset;
+//  * v_mfma_f32_16x16x32_bf16 multiplies the unscaled levels (columns = weight
+//    rows) with the zero-padded activations (rows = tokens); a_hat of the
+//    block multiplies the 16 x 16 partial product afterwards.  For M <= 8 the
+//    MFMA's 16 token rows hold the tokens of block b in rows 0-7 and those of
+//    block b + 1 in rows 8-15 (each half's activations are zero in the other
+//    block's lanes), so two blocks with different a_hat share one MFMA chain;
+//  * T = Xa A^T: every workgroup computes the same T from A (bf16, through
+//    L2) on its wave slices before the weight loop, adds the slices in a fixed
+//    order at the end and rounds it to bf16; the adapter term s T B^T of each
+//    row group is one more MFMA chain over r, and Y is rounded once.  For
+//    M <= 8 each 16-row A tile is loaded as 64 contiguous bytes per row and
+//    instruction and put into the activations' contraction order by a 4 x 4
+//    exchange between the lane groups (v_permlane32_swap, v_permlane16_swap).
+//    Workgroup 0 writes T; every workgroup computes the same T in the same
+//    order, so the result does not depend on which one wrote it.
+//
+//   Y = X W_hat^T + s T B^T,   T = Xa A^T   (llm-compass "QLoRA", 方法与公式,
+//                                            the equation; Xa = X unless the
+//                                            adapter input is dropped)
+constexpr int kGsWaves = 8;
+constexpr int kGsThreads = kGsWaves * 64;
+constexpr int kGsMaxRG = 8;                      // row groups of 16 per workgroup
+constexpr int kGsMaxRT = 4;                      // adapter tiles of 16 (r <= 64)
+constexpr int kGsTable = 256 * 64;               // dwords: entry e, lane L at e * 64 + L
+constexpr int kGsRing = 8;                       // weight loads in flight per wave
+
+template <int S, bool PAIR>
+struct GsShape {
+  static constexpr int NU = PAIR ? S / 2 : S;    // load units per row group and wave
+  static constexpr int MF = PAIR ? 4 : 2;        // MFMAs per unit
+  static constexpr int CW = S / 4;               // code dwords per row and slice
+  static constexpr int D = NU < kGsRing ? NU : kGsRing;
+};
+
+// 4 x 4 exchange of 16-byte pieces between the four lane groups (lanes
+// 16 g .. 16 g + 15): on return, register j of lane group g holds what
+// register g of lane group j held.
+__device__ __forceinline__ void lane_group_transpose4(bf16x8_t (&v)[4]) {
+  uint32_t d[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 x = __builtin_bit_cast(uint4, v[q]);
+    d[q][0] = x.x; d[q][1] = x.y; d[q][2] = x.z; d[q][3] = x.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // lane groups 2-3 of registers 0, 1 <-> lane groups 0-1 of registers 2, 3
+    auto s02 = __builtin_amdgcn_permlane32_swap(d[0][e], d[2][e], false, false);
+    d[0][e] = s02[0]; d[2][e] = s02[1];
+    auto s13 = __builtin_amdgcn_permlane32_swap(d[1][e], d[3][e], false, false);
+    d[1][e] = s13[0]; d[3][e] = s13[1];
+    // then within each pair of lane groups: odd group of register 2i <-> even
+    // group of register 2i + 1
+    auto s01 = __builtin_amdgcn_permlane16_swap(d[0][e], d[1][e], false, false);
+    d[0][e] = s01[0]; d[1][e] = s01[1];
+    auto s23 = __builtin_amdgcn_permlane16_swap(d[2][e], d[3][e], false, false);
+    d[2][e] = s23[0]; d[3][e] = s23[1];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = __builtin_bit_cast(bf16x8_t, make_uint4(d[q][0], d[q][1], d[q][2], d[q][3]));
+}
+
+template <int S, bool PAIR, int MI, int RT>
+__global__ void __launch_bounds__(kGsThreads)
+k_gemv_split(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Xa, int M, NF4Weight w,
+             const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
+             uint16_t* __restrict__ Y, uint16_t* __restrict__ T_out, int rows_wg) {
+  using Sh = GsShape<S, PAIR>;
+  constexpr int NU = Sh::NU, MF = Sh::MF, CW = Sh::CW, D = Sh::D;
+  constexpr int PARTW = kGsWaves * 64 * MI;      // floats of one row group's partials
+  __shared__ __attribute__((aligned(16))) uint32_t tbl[kGsTable];           // 64 KB
+  __shared__ __attribute__((aligned(16))) float part[kGsMaxRG * PARTW];     // 16 or 64 KB
+  __shared__ __attribute__((aligned(16))) float tpart[RT * kGsWaves * 64 * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int64_t N = w.N, K = w.K, Kb = K / kBlock;
+  const int64_t row0 = (int64_t)blockIdx.x * rows_wg;
+  const int rgs = (int)((min((int64_t)rows_wg, N - row0) + 15) / 16);
+  const int kb0 = wave * S;                        // first block of this wave's slice
+
+  const __amdgpu_buffer_rsrc_t rw = rsrc_whole(w.packed, (uint32_t)(N * (K / 2)));
+  const __amdgpu_buffer_rsrc_t rc = rsrc_whole(w.codes, (uint32_t)(N * Kb));
+  const __amdgpu_buffer_rsrc_t rs =
+      rsrc_whole(w.scales, (uint32_t)(((N * Kb + kDQBlock - 1) / kDQBlock) * 4));
+
+  // --- the weight ring: unit u of row group jr goes to slot u % D ---------
+  uint4 wu[D];
+  uint32_t cw[CW];
+  float sc;
+  auto row_of = [&](int jr) -> int64_t { return row0 + 16 * jr + col; };
+  auto load_unit = [&](int jr, int u) {
+    const int64_t n = row_of(jr);
+    if (PAIR) {
+      const uint32_t off = n < N ? (uint32_t)(n * (K / 2) + (kb0 + 2 * u) * 32 + 16 * g) : kOOB;
+      wu[u % D] = bload128s(rw, off, 0);
+    } else {
+      const uint32_t off = n < N ? (uint32_t)(n * (K / 2) + (kb0 + u) * 32 + 8 * g) : kOOB;
+      const uint2 v = bload64s(rw, off, 0);
+      wu[u % D] = make_uint4(v.x, v.y, 0u, 0u);
+    }
+  };
+  auto load_consts = [&](int jr) {   // the slice's 8-bit codes of row n and its scale
+    const int64_t n = row_of(jr);
+    const bool ok = n < N;
+    const uint32_t coff = ok ? (uint32_t)(n * Kb + kb0) : kOOB;
+    if constexpr (CW == 4) {
+      const uint4 v = bload128s(rc, coff, 0);
+      cw[0] = v.x; cw[1] = v.y; cw[2] = v.z; cw[3] = v.w;
+    } else if constexpr (CW == 2) {
+      const uint2 v = bload64s(rc, coff, 0);
+      cw[0] = v.x; cw[1] = v.y;
+    } else {
+      cw[0] = bload32s(rc, coff, 0);
+    }
+    sc = __uint_as_float(bload32s(rs, ok ? (uint32_t)((n * Kb + kb0) / kDQBlock) * 4u : kOOB, 0));
+  };
+  // The first loads go out before anything else, so that they are in flight
+  // while the table, the activations and T are prepared.
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_unit(0, u);
+  load_consts(0);
+  const float mean = w.mean[0];
+
+  // B rows of row group `wave`, for its adapter term at the end: one 16-byte
+  // piece per lane and 32 of r (r is a multiple of 8).
+  constexpr int BCH = (RT + 1) / 2;
+  const int64_t bn = row0 + 16 * wave + col;
+  const bool bvalid = wave < rgs && bn < N;
+  const __amdgpu_buffer_rsrc_t rb = rsrc_whole(B, (uint32_t)(N * r * 2));
+  uint4 bpre[BCH];
+#pragma unroll
+  for (int c = 0; c < BCH; ++c)
+    bpre[c] = bload128s(rb, bvalid && 32 * c + 8 * g < r ? (uint32_t)((bn * r + 32 * c + 8 * g) * 2) : kOOB, 0);
+
+  // --- the byte -> (level of the high nibble, level of the low nibble)
+  // table, one column per lane.  Thread t fills entries e = t / 64 + 8 k of
+  // its lane's column: the high nibble of e is k / 2, the low t / 64 + 8 (k & 1).
+  {
+    const int e0 = tid >> 6;
+    const float lo0 = nf4_level(e0), lo1 = nf4_level(e0 + 8);
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      tbl[k * kGsThreads + tid] = pack_bf16x2(nf4_level(k >> 1), (k & 1) ? lo1 : lo0);
+  }
+  const uint32_t lane4 = (uint32_t)lane * 4u;
+
+  // --- activations of the slice as MFMA operands (rows = tokens) -----------
+  bf16x8_t xop[NU][MF];
+  auto load_x = [&](const uint16_t* src) {
+    const __amdgpu_buffer_rsrc_t rx = rsrc_whole(src, (uint32_t)((int64_t)M * K * 2));
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int j = 0; j < MF; ++j) {
+        int t, blk, k;
+        bool ok;
+        if (PAIR) {
+          const int half = col >> 3;
+          t = col & 7;
+          blk = kb0 + 2 * u + half;
+          k = 32 * (g & 1) + 8 * j;
+          ok = half == (g >> 1) && t < M;
+        } else {
+          t = col;
+          blk = kb0 + u;
+          k = 16 * g + 8 * j;
+          ok = t < M;
+        }
+        const uint32_t off = ok ? (uint32_t)(((int64_t)t * K + (int64_t)blk * kBlock + k) * 2) : kOOB;
+        xop[u][j] = __builtin_bit_cast(bf16x8_t, bload128s(rx, off, 0));
+      }
+  };
+  load_x(Xa);
+
+  // --- T partials of the slice, 16 adapter rows per tile -------------------
+  {
+    const __amdgpu_buffer_rsrc_t ra = rsrc_whole(A, (uint32_t)((int64_t)r * K * 2));
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int ri = rt * 16 + col;
+      f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        bf16x8_t av[MF];
+        if constexpr (PAIR) {
+          // instruction q: lane group g loads 16-byte piece 4 q + g of the
+          // row's two-block run; the unit's operand for MFMA j in lane group g
+          // is piece 4 g + j
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t off = ri < r ? (uint32_t)(((int64_t)ri * K + (int64_t)(kb0 + 2 * u) * kBlock) * 2 +
+                                                     64 * q + 16 * g)
+                                        : kOOB;
+            av[q] = __builtin_bit_cast(bf16x8_t, bload128s(ra, off, 0));
+          }
+          lane_group_transpose4(av);
+        } else {
+#pragma unroll
+          for (int j = 0; j < MF; ++j) {
+            const uint32_t off = ri < r ? (uint32_t)(((int64_t)ri * K + (int64_t)(kb0 + u) * kBlock + 16 * g + 8 * j) * 2)
+                                        : kOOB;
+            av[j] = __builtin_bit_cast(bf16x8_t, bload128s(ra, off, 0));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < MF; ++j) c = mfma_16x16x32(xop[u][j], av[j], c);
+      }
+      *reinterpret_cast<f32x4_t*>(&tpart[((rt * kGsWaves + wave) * 64 + lane) * 4]) = c;
+    }
+  }
+  if (Xa != X) load_x(X);
+
+  // --- the weight stream -----------------------------------------------------
+  for (int jr = 0; jr < rgs; ++jr) {
+    float acc[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) acc[i] = 0.0f;
+    uint32_t cwl[CW];
+#pragma unroll
+    for (int q = 0; q < CW; ++q) cwl[q] = cw[q];
+    const float scl = sc;
+    if (jr + 1 < rgs) load_consts(jr + 1);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      // a_hat of the lane's block (row n; block 2u + g/2 of the slice, or u)
+      const int b = PAIR ? 2 * u : u;
+      const uint32_t sh = 8u * (uint32_t)(b & 3) + (PAIR ? 8u * (uint32_t)(g >> 1) : 0u);
+      const int code = (int)((cwl[b >> 2] >> sh) & 0xffu);
+      const float ah = absmax_decode(code, scl, mean);
+      const uint4 pw = wu[u % D];
+      if (u + D < NU) load_unit(jr, u + D);
+      else if (jr + 1 < rgs) load_unit(jr + 1, u + D - NU);
+      const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
+      f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < MF; ++j) {
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // byte e of the word: address = byte * 256 + 4 * lane
+          const uint32_t addr = __builtin_amdgcn_perm(words[j], lane4, 0x0C0C0400u | ((4u + e) << 8));
+          o[e] = tbl[addr >> 2];
+        }
+        c = mfma_16x16x32(xop[u][j], __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3])), c);
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) acc[i] += ah * c[i];
+    }
+    float* pb = part + jr * PARTW;
+    if constexpr (MI == 4) {
+      *reinterpret_cast<f32x4_t*>(&pb[(wave * 64 + lane) * 4]) = f32x4_t{acc[0], acc[1 % MI], acc[2 % MI], acc[3 % MI]};
+    } else {
+      pb[wave * 64 + lane] = acc[0];
+    }
+  }
+  __syncthreads();
+
+  // --- T, the adapter term, Y (the table's space is free now) ---------------
+  uint16_t* tl = reinterpret_cast<uint16_t*>(tbl);            // T bf16 [M][r]
+  float* ad = reinterpret_cast<float*>(tbl) + 2048;           // (T B^T)[16 jr + row][m]
+  // C row 4 g + i of a slice's MFMA is token (4 g + i) % 8 of block half
+  // (4 g + i) / 8 (M <= 8) or token 4 g + i; slices and halves are added in a
+  // fixed order.
+  for (int i = tid; i < RT * 16 * M; i += kGsThreads) {
+    const int rt = i / (16 * M), m = (i / 16) % M, cc = i % 16;
+    const int rr = rt * 16 + cc;
+    float t = 0.0f;
+    for (int ww = 0; ww < kGsWaves; ++ww) {
+      const float* tp = tpart + (rt * kGsWaves + ww) * 64 * 4;
+      if (PAIR) {
+        for (int h = 0; h < 2; ++h) t += tp[(cc + 16 * (2 * h + (m >> 2))) * 4 + (m & 3)];
+      } else {
+        t += tp[(cc + 16 * (m >> 2)) * 4 + (m & 3)];
+      }
+    }
+    if (rr < r) {
+      const uint16_t tb = f32_to_bf16(t);
+      tl[m * r + rr] = tb;
+      if (blockIdx.x == 0) T_out[m * r + rr] = tb;
+    }
+  }
+  __syncthreads();
+  if (wave < rgs) {   // wave w: adapter term of row group w, tokens x rows
+    f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ch = 0; ch < BCH; ++ch) {
+      uint4 tv = make_uint4(0, 0, 0, 0);
+      if (col < M && 32 * ch + 8 * g < r) tv = *reinterpret_cast<const uint4*>(tl + col * r + 32 * ch + 8 * g);
+      c = mfma_16x16x32(__builtin_bit_cast(bf16x8_t, tv), __builtin_bit_cast(bf16x8_t, bpre[ch]), c);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[(16 * wave + col) * kGemvMaxM + 4 * g + i] = c[i];
+  }
+  __syncthreads();
+  for (int i = tid; i < rgs * 16 * M; i += kGsThreads) {
+    const int jr = i / (16 * M), m = (i / 16) % M, cc = i % 16;
+    const int64_t n = row0 + 16 * jr + cc;
+    const float* pb = part + jr * PARTW;
+    float base = 0.0f;
+    for (int ww = 0; ww < kGsWaves; ++ww) {
+      if (MI == 1) {
+        for (int h = 0; h < 2; ++h) base += pb[ww * 64 + cc + 32 * h];
+      } else if (PAIR) {
+        for (int h = 0; h < 2; ++h) base += pb[(ww * 64 + cc + 16 * (2 * h + (m >> 2))) * 4 + (m & 3)];
+      } else {
+        base += pb[(ww * 64 + cc + 16 * (m >> 2)) * 4 + (m & 3)];
+      }
+    }
+    if (n < N) Y[(int64_t)m * N + n] = f32_to_bf16(base + s * ad[(16 * jr + cc) * kGemvMaxM + m]);
+  }
+}
+
+// The split kernel's shapes: K of 32, 64 or 128 blocks (S = 4, 8, 16 blocks
+// per wave), r <= 64, rows in at most 256 x kGsMaxRG groups of 16.
+static int gemv_split_rows(int64_t N, int64_t K, int r) {
+  const int64_t Kb = K / kBlock;
+  if (Kb != 32 && Kb != 64 && Kb != 128) return 0;
+  if (r > 16 * kGsMaxRT || r % 8 != 0) return 0;
+  const int64_t groups = (N + 15) / 16;
+  const int64_t per = (groups + 255) / 256;       // row groups per workgroup
+  if (per > kGsMaxRG) return 0;
+  return (int)(per * 16);
+}
+
+template <int S, int RT>
+static void launch_gemv_split_rt(const uint16_t* X, const uint16_t* Xa, int M, const NF4Weight& w,
+                                 const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                                 uint16_t* T, int rows_wg, hipStream_t st) {
+  const dim3 grid((unsigned)((w.N + rows_wg - 1) / rows_wg));
+  if (M == 1)
+    hipLaunchKernelGGL((k_gemv_split<S, true, 1, RT>), grid, dim3(kGsThreads), 0, st, X, Xa, M, w,
+                       A, B, r, s, Y, T, rows_wg);
+  else if (M <= 8)
+    hipLaunchKernelGGL((k_gemv_split<S, true, 4, RT>), grid, dim3(kGsThreads), 0, st, X, Xa, M, w,
+                       A, B, r, s, Y, T, rows_wg);
+  else
+    hipLaunchKernelGGL((k_gemv_split<S, false, 4, RT>), grid, dim3(kGsThreads), 0, st, X, Xa, M, w,
+                       A, B, r, s, Y, T, rows_wg);
+}
+
+template <int S>
+static void launch_gemv_split_s(const uint16_t* X, const uint16_t* Xa, int M, const NF4Weight& w,
+                                const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                                uint16_t* T, int rows_wg, hipStream_t st) {
+  if (r <= 16) launch_gemv_split_rt<S, 1>(X, Xa, M, w, A, B, r, s, Y, T, rows_wg, st);
+  else if (r <= 32) launch_gemv_split_rt<S, 2>(X, Xa, M, w, A, B, r, s, Y, T, rows_wg, st);
+  else launch_gemv_split_rt<S, 4>(X, Xa, M, w, A, B, r, s, Y, T, rows_wg, st);
+}
+
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
                        hipStream_t st, const uint16_t* Xa, const Timing* tm) {
+  if (!Xa) Xa = X;
+  const int rows_wg = gemv_split_rows(w.N, w.K, r);
+  if (rows_wg > 0) {
+    timer_begin(tm, TK_GEMV, st);
+    switch (w.K / kBlock) {
+      case 32: launch_gemv_split_s<4>(X, Xa, (int)M, w, A, B, r, s, Y, T, rows_wg, st); break;
+      case 64: launch_gemv_split_s<8>(X, Xa, (int)M, w, A, B, r, s, Y, T, rows_wg, st); break;
+      default: launch_gemv_split_s<16>(X, Xa, (int)M, w, A, B, r, s, Y, T, rows_wg, st); break;
+    }
+    timer_end(tm, TK_GEMV, st);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_lora_down_partial, dim3((r + 31) / 32, kTSplits), dim3(256), 0, st,
-                     Xa ? Xa : X, (int)M, w.K, A, r, Tpart);
+                     Xa, (int)M, w.K, A, r, Tpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((w.N + 63) / 64);
