@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = (
     0, -1, -2, -3, -4, -5, -6, -7)
+ERR_SCRATCH = -8
+NOALLOC_SCRATCH_BYTES = 64 << 20
 BWD_ACCUMULATE_DX = 1
 BLOCKSIZE = 64
 DQ_BLOCKSIZE = 256
@@ -83,6 +85,8 @@ SIGNATURES = {
     "dq_codebook": (_I, [_P, ctypes.POINTER(_I)]),
     "qlora_strerror": (ctypes.c_char_p, [_I]),
     "qlora_version": (_I, []),
+    "qlora_linear_bwd_noalloc": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F,
+                                      _P, _P, _P, _P, _I, _P]),
     "qlora_linear_fwd_timed": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F, _P,
                                     _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(TimingC)]),
     "qlora_linear_bwd_timed": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F,

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/qlora.h"
 #include "kernels.h"
 
@@ -153,16 +155,24 @@ int fwd_common(const uint16_t* X, int64_t M, int64_t K, int64_t N, const qlk::NF
   return launch_status(e);
 }
 
-int bwd_common(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
-               const qlk::NF4Weight& w, const uint16_t* A, const uint16_t* B, int r, float alpha,
-               const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags, void* workspace,
-               size_t workspace_bytes, void* stream, const uint32_t* mask = nullptr,
-               float keep_scale = 1.0f, const qlk::Timing* tm = nullptr) {
+// The backward's own arguments (beyond those check_linear covers).
+int check_bwd_args(const uint16_t* dY, const uint16_t* T, const uint16_t* dX, const float* dA,
+                   const float* dB, int flags) {
   if (!dY || !dA || !dB) return QLORA_ERR_NULL;
   if (flags & ~QLORA_BWD_ACCUMULATE_DX) return QLORA_ERR_ARG;
   if (!aligned16(dY) || !aligned16(dA) || !aligned16(dB) || (dX && !aligned16(dX)) ||
       (T && !aligned16(T)))
     return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+int bwd_common(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K, int64_t N,
+               const qlk::NF4Weight& w, const uint16_t* A, const uint16_t* B, int r, float alpha,
+               const uint16_t* T, uint16_t* dX, float* dA, float* dB, int flags, void* workspace,
+               size_t workspace_bytes, void* stream, const uint32_t* mask = nullptr,
+               float keep_scale = 1.0f, const qlk::Timing* tm = nullptr) {
+  const int bad = check_bwd_args(dY, T, dX, dA, dB, flags);
+  if (bad) return bad;
   const int rp = padded_rank(r);
   const qlk::BwdPlan plan = qlk::plan_bwd(M, K, N, rp, dX != nullptr);
   const PadPlan pad = plan_pad(plan.bytes, M, K, N, r, true);
@@ -238,6 +248,46 @@ int dequant_common(const uint8_t* packed, const uint8_t* codes, const float* sca
     return QLORA_ERR_ALIGN;
   return launch_status(
       qlk::launch_nf4_dequant(packed, codes, scales, mean, N * K, cb, W_bf16, as_stream(stream)));
+}
+
+// ---- static scratch of qlora_linear_bwd_noalloc ---------------------------
+//
+// Callers that cannot allocate (graph capture, serving loops, harnesses that
+// forbid it) get a backward whose scratch memory is this file-scope array:
+// every GPU the library runs on holds its own copy from module load until the
+// process ends.  On the host, `scratch` is only a stand-in for the symbol;
+// the device address of each GPU's copy is looked up once per device (with
+// that device current) and kept, and only that address is handed to kernels.
+// No kernel of the backward needs its scratch to start at zero (every value
+// it reads back was written earlier in the same call), so nothing is cleared.
+// Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[QLORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the scratch array on the GPU of `stream` (or of the
+// current device for the null stream).
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0, cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return QLORA_ERR_LAUNCH;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return QLORA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_ERR_LAUNCH;
+  std::call_once(g_scratch_once[dev], [dev, cur] {
+    hipError_t e = hipSuccess;
+    if (dev != cur) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return QLORA_ERR_LAUNCH;
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
 }
 
 }  // namespace
@@ -384,6 +434,24 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K
                                 dX, dA, dB, flags, workspace, workspace_bytes, stream, nullptr);
 }
 
+int qlora_linear_bwd_noalloc(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K,
+                             int64_t N, const uint8_t* packed, const uint8_t* codes,
+                             const float* scales, const float* mean, const uint16_t* A,
+                             const uint16_t* B, int r, float alpha, const uint16_t* T, uint16_t* dX,
+                             float* dA, float* dB, int flags, void* stream) {
+  int st = check_linear(X, M, K, N, packed, codes, scales, mean, A, B, r, alpha);
+  if (st) return st;
+  st = check_bwd_args(dY, T, dX, dA, dB, flags);
+  if (st) return st;
+  if (bwd_layout(M, K, N, r, dX != nullptr).bytes > (size_t)QLORA_NOALLOC_SCRATCH_BYTES)
+    return QLORA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(as_stream(stream), &ws);
+  if (st) return st;
+  return bwd_common(dY, X, M, K, N, weight(packed, codes, scales, mean, N, K), A, B, r, alpha, T,
+                    dX, dA, dB, flags, ws, (size_t)QLORA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int qlora_linear_bwd_dropout(const uint16_t* dY, const uint16_t* Xd, const uint32_t* mask,
                              double p, int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                              const uint8_t* codes, const float* scales, const float* mean,
@@ -526,6 +594,7 @@ const char* qlora_strerror(int status) {
     case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
     case QLORA_ERR_LAUNCH: return "HIP launch failed";
     case QLORA_ERR_ARG: return "invalid argument";
+    case QLORA_ERR_SCRATCH: return "needs more scratch memory than the static array holds";
     default: return "unknown status";
   }
 }

@@ -58,6 +58,8 @@ extern "C" {
 #define QLORA_ERR_ARG           -7  /* other invalid argument (alpha not finite,
                                        unknown flag bits, p outside [0, 1), a
                                        codebook not finite and ascending)            */
+#define QLORA_ERR_SCRATCH       -8  /* qlora_linear_bwd_noalloc: the call needs more
+                                       than QLORA_NOALLOC_SCRATCH_BYTES of scratch   */
 
 /* qlora_linear_bwd flag: add the computed dX into the bf16 values already in
  * dX instead of overwriting them (used when two linears share an input, as
@@ -175,6 +177,24 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K
                      int r, float alpha, const uint16_t* T,
                      uint16_t* dX, float* dA, float* dB, int flags,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* qlora_linear_bwd for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments without the workspace, the same kernels and bit-identical
+ * results.  Its scratch memory is a static device array of
+ * QLORA_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds from
+ * module load until the process ends; the call allocates nothing.  Shapes
+ * whose backward needs more scratch than that (qlora_workspace_bytes(M, K, N,
+ * r, 1), less the dX parts when dX is NULL) return QLORA_ERR_SCRATCH before
+ * anything is launched; 64 MiB holds the backward of a 4096 x 4096 layer at
+ * 2048 tokens.  All calls on one GPU share the array: two calls that overlap
+ * on the same GPU (different streams, no ordering between them) race. */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int qlora_linear_bwd_noalloc(const uint16_t* dY, const uint16_t* X, int64_t M, int64_t K,
+                             int64_t N, const uint8_t* packed, const uint8_t* codes,
+                             const float* scales, const float* mean, const uint16_t* A,
+                             const uint16_t* B, int r, float alpha, const uint16_t* T, uint16_t* dX,
+                             float* dA, float* dB, int flags, void* stream);
 
 /* The same layer with an unquantised bf16 base weight W [N, K] (bf16,
  * row-major): the comparison the pages draw between LoRA on a bf16 base and

@@ -50,7 +50,7 @@ def test_codebooks_match_oracle_bits():
 
 
 def test_strerror_and_version():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = lib.qlora_strerror(code).decode()
         assert s and s != "unknown status"
     assert lib.qlora_strerror(5).decode() == "unknown status"
@@ -165,6 +165,25 @@ def test_timed_entry_points_validate_like_the_plain_calls():
             a = list(bwd)
             a[i] = v
             assert fb(*a, t) == code, (i, v)
+
+
+def test_noalloc_backward_refuses_shapes_beyond_its_static_scratch():
+    """qlora_linear_bwd_noalloc validates like qlora_linear_bwd and refuses, before
+    anything is launched, a backward that needs more scratch than the static
+    array holds (here the 65B-shaped 22016 x 8192 layer at 4096 tokens)."""
+    f = lib.qlora_linear_bwd_noalloc
+    big = (D, D, 4096, 8192, 22016, D, D, D, D, D, D, 16, 32.0, None, D, D, D, 0, None)
+    assert lib.qlora_workspace_bytes(4096, 8192, 22016, 16, 1) > q.NOALLOC_SCRATCH_BYTES
+    assert f(*big) == q.ERR_SCRATCH
+    assert lib.qlora_strerror(q.ERR_SCRATCH).decode() != "unknown status"
+    ok = list(big)
+    ok[2], ok[3], ok[4] = 64, 256, 256
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == q.ERR_NULL
+    bad = list(ok); bad[11] = 0
+    assert f(*bad) == q.ERR_SHAPE
+    bad = list(ok); bad[17] = 2
+    assert f(*bad) == q.ERR_ARG
 
 
 def test_linear_output_validation():
