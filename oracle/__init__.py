@@ -41,10 +41,16 @@ Functions and what pins them (tests/test_oracle_*.py):
   int4 codebook     even spacing, round trip, error bound; NF4 beats it on
                     Gaussian blocks in error and in code entropy, as the
                     pages argue
+  float8 DQ table  its values against torch's own float8_e4m3fn decoding of
+                    all 256 bit patterns; count, range, symmetry, exact zero;
+                    round trip of the levels; nearest-level bound; fewer
+                    absmax reconstruction errors than the linear code on a
+                    heavy-tailed group
 No function is "parity unpinned".
 """
 from .nf4 import (  # noqa: F401
-    NF4_DELTA, nf4_codebook, dq_codebook, int4_codebook, nearest_index, absmax_blocks,
+    NF4_DELTA, nf4_codebook, dq_codebook, int4_codebook, fp8_e4m3_values, dq_float8_codebook,
+    nearest_index, absmax_blocks,
     quantize_nf4, quantize_blocks, pack_nibbles, unpack_nibbles, double_quant, dequant_absmax,
     dequant_nf4, dequant_codes, f32_to_bf16_bits, bf16_bits_to_f64, bits_per_param,
 )

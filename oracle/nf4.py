@@ -74,6 +74,39 @@ def dq_codebook() -> np.ndarray:
     return (i - np.float32(127.0)) / np.float32(127.0)
 
 
+def fp8_e4m3_values() -> np.ndarray:
+    """Every finite value of the 8-bit float with one sign bit, 4 exponent bits
+    (bias 7) and 3 mantissa bits, no infinities and one NaN pattern per sign
+    (exponent and mantissa all ones), decoded from its bit fields in fp64:
+    exponent 0 gives the subnormals m / 8 * 2^-6, exponent e > 0 the normal
+    values (1 + m / 8) * 2^(e - 7).  Sorted, +0 and -0 counted once: 253
+    values from -448 to 448."""
+    vals = set()
+    for b in range(256):
+        sign, e, m = b >> 7, (b >> 3) & 15, b & 7
+        if e == 15 and m == 7:
+            continue                               # NaN
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        vals.add(-v if sign else v)
+    return np.array(sorted(vals), dtype=np.float64)
+
+
+def dq_float8_codebook() -> np.ndarray:
+    """Q8F[0..252] as fp32: an 8-bit float code for the centred block constants.
+
+    The pages give only the width of the second level, 8 bits ([AU] Dubbele
+    Quantisatie box; [LC] 方法与公式 item 2).  This table is the other reading
+    of "8-bit" next to the linear code: the finite values of the 8-bit float
+    above (4 exponent, 3 mantissa bits), divided by the largest one (448) so
+    that the levels span the normalised range [-1, 1] with an exact zero,
+    each quotient evaluated in fp64 and rounded once to fp32.  Its levels are
+    dense near zero and sparse near +-1, so small constants in a group with
+    one large outlier keep their relative precision.  Code byte = index
+    (0..252, zero at 126); bytes 253..255 unused.
+    """
+    return (fp8_e4m3_values() / 448.0).astype(np.float32)
+
+
 def int4_codebook() -> np.ndarray:
     """Uniform 4-bit codebook for the comparison the pages draw with NF4:
     16 levels spaced evenly over the absmax-normalised range [-1, 1] ([LI] §2,
@@ -190,7 +223,7 @@ def _fixed_order_sum(a: np.ndarray, group: int) -> float:
     return total
 
 
-def double_quant(absmax: np.ndarray, dq_blocksize: int = 256):
+def double_quant(absmax: np.ndarray, dq_blocksize: int = 256, levels=None):
     """absmax fp32 [nb] -> (codes uint8 [nb], scales fp32 [ceil(nb/256)], mean fp32).
 
     [AU] Dubbele Quantisatie box / [LC] 方法与公式 item 2: the constants are
@@ -202,6 +235,8 @@ def double_quant(absmax: np.ndarray, dq_blocksize: int = 256):
         s_g = max |c_b| over the group;
       * 8-bit code = nearest level of the linear codebook to fp32(c_b / s_g),
         ties to the lower index; a group with s_g = 0 gets the zero code 127.
+    ``levels`` replaces the linear codebook (e.g. dq_float8_codebook()); the
+    code of a group with s_g = 0 is then the index of its zero level.
     """
     a = np.asarray(absmax, dtype=np.float32).reshape(-1)
     nb = a.size
@@ -216,14 +251,16 @@ def double_quant(absmax: np.ndarray, dq_blocksize: int = 256):
         scales[g] = s
         if s > 0:
             n2[g * dq_blocksize:(g + 1) * dq_blocksize] = (seg / s).astype(np.float32)
-    codes = nearest_index(n2, dq_codebook())
+    codes = nearest_index(n2, dq_codebook() if levels is None else levels)
     return codes, scales, mu
 
 
-def dequant_absmax(codes: np.ndarray, scales: np.ndarray, mean, dq_blocksize: int = 256):
-    """a_hat_b = fp32( fp32(Q8[code_b] * s_g) + mu ): two separately rounded fp32 ops."""
+def dequant_absmax(codes: np.ndarray, scales: np.ndarray, mean, dq_blocksize: int = 256,
+                   levels=None):
+    """a_hat_b = fp32( fp32(Q8[code_b] * s_g) + mu ): two separately rounded fp32 ops
+    (Q8 the linear codebook, or ``levels``)."""
     c = np.asarray(codes, dtype=np.uint8).reshape(-1)
-    q8 = dq_codebook()
+    q8 = dq_codebook() if levels is None else np.asarray(levels, dtype=np.float32)
     s = np.repeat(np.asarray(scales, dtype=np.float32), dq_blocksize)[:c.size]
     prod = (q8[c] * s).astype(np.float32)
     return (prod + np.float32(mean)).astype(np.float32)
@@ -250,7 +287,7 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
 
 
 def dequant_nf4(packed: np.ndarray, codes: np.ndarray, scales: np.ndarray, mean,
-                N: int, K: int, blocksize: int = 64, dq_blocksize: int = 256):
+                N: int, K: int, blocksize: int = 64, dq_blocksize: int = 256, levels8=None):
     """(packed, 8-bit codes, scales, mean) -> (w_hat fp32 [N,K], bf16 bits [N,K]).
 
     w_hat = fp32(Q4[nibble] * a_hat_block); the bf16 weight fed to the matmul is
@@ -258,7 +295,7 @@ def dequant_nf4(packed: np.ndarray, codes: np.ndarray, scales: np.ndarray, mean,
     [LC] 直觉与动机: back to bf16 for the matrix product).
     """
     nib = unpack_nibbles(packed)[:N * K]
-    a_hat = dequant_absmax(codes, scales, mean, dq_blocksize)
+    a_hat = dequant_absmax(codes, scales, mean, dq_blocksize, levels=levels8)
     w_hat, wb = dequant_codes(nib, a_hat, blocksize)
     return w_hat.reshape(N, K), wb.reshape(N, K)
 
