@@ -605,7 +605,32 @@ def run_standalone(args, q, torch, lib, ev):
         torch.cuda.synchronize()
         errs[name] = float(np.linalg.norm(f64(deq_w) - W64) / np.linalg.norm(W64))
     out["codebook_rel_err"] = errs
+    out["dq_table_abs_err"] = second_level_errors(q, torch)
     return out
+
+
+def second_level_errors(q, torch):
+    """Reconstruction error of the block constants (absmax) of the 65B-shaped
+    layer's 8192 x 8192 q-projection weight (99 % N(0, 0.02), 1 % 0.05 t(3)
+    outliers) with the linear second-level code and with the 8-bit-float
+    table, through double_quant_table / absmax_dequant."""
+    import qlora_workloads as wl
+    w = wl.workloads()["c5_decoder_8192"]
+    lin = w.linears[0]
+    W = torch.from_numpy(wl.weight(0, w.cfg_id, 0, lin)).cuda()
+    _, absmax = q.nf4_quantize(W)
+    del W
+    res = dict(weight=f"c5_decoder_8192/{lin.name} {lin.N}x{lin.K}", blocks=int(absmax.numel()))
+    for name, lv in (("linear", q.dq_levels()), ("float8", q.dq_float8_levels())):
+        c, s, mu = q.double_quant_table(absmax, lv)
+        ah = q.absmax_dequant(c, s, mu, lv)
+        e = (ah - absmax).double()
+        rel = e.abs() / absmax.double().clamp_min(1e-30)
+        res[name] = dict(levels=len(lv), rel_frobenius=float(e.norm() / absmax.double().norm()),
+                         rel_median=float(rel.median()), rel_p99=float(rel.quantile(0.99)),
+                         rel_max=float(rel.max()))
+    torch.cuda.synchronize()
+    return res
 
 
 def run_cpu_baseline(budget_s: float):

@@ -85,6 +85,10 @@ SIGNATURES = {
     "dq_codebook": (_I, [_P, ctypes.POINTER(_I)]),
     "qlora_strerror": (ctypes.c_char_p, [_I]),
     "qlora_version": (_I, []),
+    "double_quant_table": (_I, [_P, _I64, _I, _P, _I, _P, _P, _P, _P]),
+    "absmax_dequant": (_I, [_P, _P, _P, _I64, _I, _P, _I, _P, _P]),
+    "dequant_tables": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P, _I, _P, _P]),
+    "dq_float8_codebook": (_I, [_P, ctypes.POINTER(_I)]),
     "qlora_linear_bwd_noalloc": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F,
                                       _P, _P, _P, _P, _I, _P]),
     "qlora_linear_fwd_timed": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I, _F, _P,
@@ -682,6 +686,77 @@ def codebook():
     buf = (ctypes.c_float * 16)()
     _check("nf4_codebook", load_library().nf4_codebook(ctypes.cast(buf, _P)))
     return list(buf)
+
+
+def dq_float8_levels():
+    """The 253 levels of the 8-bit-float second-level table (host copy)."""
+    buf = (ctypes.c_float * 256)()
+    n = _I(0)
+    _check("dq_float8_codebook", load_library().dq_float8_codebook(ctypes.cast(buf, _P),
+                                                                   ctypes.byref(n)))
+    return list(buf)[: n.value]
+
+
+def _levels8(levels):
+    vals = [float(v) for v in levels]
+    if not 2 <= len(vals) <= 256:
+        raise ValueError("a second-level table has 2 to 256 levels")
+    return (ctypes.c_float * len(vals))(*vals), len(vals)
+
+
+def double_quant_table(absmax, levels):
+    """double_quant with the given second-level table (host sequence,
+    ascending) -> (codes uint8 [nb], scales fp32, mean fp32 [1])."""
+    torch = _torch()
+    chk = _Checker()
+    if not isinstance(absmax, torch.Tensor) or absmax.dim() != 1:
+        raise ValueError("absmax: a 1-D fp32 tensor")
+    chk("absmax", absmax, torch.float32, tuple(absmax.shape))
+    dev = chk.device()
+    nb = absmax.numel()
+    codes = torch.empty(nb, dtype=torch.uint8, device=dev)
+    scales = torch.empty((nb + DQ_BLOCKSIZE - 1) // DQ_BLOCKSIZE, dtype=torch.float32, device=dev)
+    mean = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+    lv, n = _levels8(levels)
+    _check("double_quant_table", load_library().double_quant_table(
+        _ptr(absmax), nb, DQ_BLOCKSIZE, ctypes.cast(lv, _P), n, _ptr(codes), _ptr(scales),
+        _ptr(mean), _stream(dev)))
+    return codes, scales, mean
+
+
+def absmax_dequant(codes, scales, mean, levels):
+    """-> fp32 [nb]: the decoded block constants fp32(fp32(levels[c] * s) + mean)."""
+    torch = _torch()
+    chk = _Checker()
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 1:
+        raise ValueError("codes: a 1-D uint8 tensor")
+    nb = codes.numel()
+    chk("codes", codes, torch.uint8, (nb,))
+    chk("scales", scales, torch.float32, ((nb + DQ_BLOCKSIZE - 1) // DQ_BLOCKSIZE,))
+    chk("mean", mean, torch.float32, (1,))
+    dev = chk.device()
+    out = torch.empty(nb, dtype=torch.float32, device=dev)
+    lv, n = _levels8(levels)
+    _check("absmax_dequant", load_library().absmax_dequant(
+        _ptr(codes), _ptr(scales), _ptr(mean), nb, DQ_BLOCKSIZE, ctypes.cast(lv, _P), n,
+        _ptr(out), _stream(dev)))
+    return out
+
+
+def dequant_tables(qw: QuantizedWeight, levels8, levels4=None):
+    """-> bf16 [N, K]: the weight dequantised with the given second-level table
+    (and 4-bit codebook; None = NF4)."""
+    torch = _torch()
+    chk = _Checker()
+    chk.weight(qw)
+    dev = chk.device()
+    out = torch.empty(qw.N, qw.K, dtype=torch.bfloat16, device=dev)
+    lv8, n8 = _levels8(levels8)
+    lv4 = None if levels4 is None else ctypes.cast(_levels(levels4), _P)
+    _check("dequant_tables", load_library().dequant_tables(
+        _ptr(qw.packed), _ptr(qw.codes), _ptr(qw.scales), _ptr(qw.mean), qw.N, qw.K, BLOCKSIZE,
+        DQ_BLOCKSIZE, lv4, ctypes.cast(lv8, _P), n8, _ptr(out), _stream(dev)))
+    return out
 
 
 def dq_levels():

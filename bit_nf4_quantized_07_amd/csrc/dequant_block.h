@@ -4,6 +4,7 @@
 // takes word 64 q + L of the wave's range, so every load and store
 // instruction of the wave covers one contiguous range.  The block's waves
 // take consecutive ranges; `blk` is the block's index in the dequant grid.
+// q8: the 8-bit levels as a table in LDS, or null for the linear code.
 #pragma once
 #include "device_common.h"
 #include "kernels.h"
@@ -15,7 +16,8 @@ __device__ __forceinline__ void nf4_dequant_block(const uint8_t* __restrict__ pa
                                                   const float* __restrict__ scales,
                                                   const float* __restrict__ mean, int64_t nwords,
                                                   const Codebook4& cb, uint16_t* __restrict__ out,
-                                                  int64_t blk_index) {
+                                                  int64_t blk_index,
+                                                  const float* q8 = nullptr) {
   __shared__ float q4[16];
   if (threadIdx.x < 16) {
     float v = 0.0f;
@@ -46,7 +48,8 @@ __device__ __forceinline__ void nf4_dequant_block(const uint8_t* __restrict__ pa
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (!ok[q]) continue;
-    const float ah = absmax_decode(cd[q], sc[q], mu);
+    // 8-bit levels: the linear code computed, or a table (in LDS)
+    const float ah = q8 ? absmax_decode_tab((int)cd[q], sc[q], mu, q8) : absmax_decode(cd[q], sc[q], mu);
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

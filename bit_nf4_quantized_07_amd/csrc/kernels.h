@@ -15,14 +15,25 @@ struct Codebook4 {
 };
 Codebook4 make_codebook(const float* levels16);
 Codebook4 nf4_codebook4();
+// A second-level (8-bit) code table passed as data: n <= 256 ascending levels
+// (entries from n on hold 0) and the n - 1 thresholds built the same way.
+struct Codebook8 {
+  float lv[256];
+  float thr[255];
+  int n;
+};
+Codebook8 make_codebook8(const float* levels, int n);
 
 hipError_t launch_nf4_quantize(const float* W, int64_t numel, const Codebook4& cb, uint8_t* packed,
                                float* absmax, hipStream_t st);
+// cb8: the second-level table (null: the linear code).
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, float* scales,
-                               float* mean, hipStream_t st);
+                               float* mean, hipStream_t st, const Codebook8* cb8 = nullptr);
 hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
                               const float* mean, int64_t numel, const Codebook4& cb, uint16_t* out,
-                              hipStream_t st);
+                              hipStream_t st, const Codebook8* cb8 = nullptr);
+hipError_t launch_absmax_dequant(const uint8_t* codes, const float* scales, const float* mean,
+                                 int64_t nb, const Codebook8& cb8, float* out, hipStream_t st);
 // LoRA dropout: Xd = bf16(x * scale) where Philox4x32-10 keeps the element,
 // 0 elsewhere; one mask bit per element.  numel % 32 == 0.
 hipError_t launch_lora_dropout(const uint16_t* X, int64_t numel, uint32_t threshold, float scale,

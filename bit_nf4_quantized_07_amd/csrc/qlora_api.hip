@@ -220,6 +220,33 @@ const qlk::Timing* to_timing(const qlora_timing* t, qlk::Timing& out) {
   return &out;
 }
 
+// A second-level table from the caller: 2..256 finite, strictly ascending
+// levels (HOST memory).
+int check_table8(const float* levels, int n) {
+  if (!levels) return QLORA_ERR_NULL;
+  if (n < 2 || n > 256) return QLORA_ERR_ARG;
+  for (int i = 0; i < n; ++i)
+    if (!isfinite(levels[i]) || (i > 0 && !(levels[i - 1] < levels[i]))) return QLORA_ERR_ARG;
+  return QLORA_OK;
+}
+
+// The 8-bit-float second-level levels: every finite value of the 8-bit float
+// with 4 exponent bits (bias 7) and 3 mantissa bits (the all-ones pattern is
+// NaN, there are no infinities), divided by its largest value 448, the fp64
+// quotient rounded once to fp32; ascending, 253 levels, zero at index 126.
+int float8_levels(float* out) {
+  double v[128];
+  int n = 0;
+  for (int b = 0; b < 127; ++b) {          // the non-negative patterns, ascending
+    const int e = (b >> 3) & 15, m = b & 7;
+    v[n++] = e == 0 ? (m / 8.0) * ldexp(1.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+  }
+  int k = 0;
+  for (int i = n - 1; i >= 1; --i) out[k++] = (float)(-v[i] / 448.0);
+  for (int i = 0; i < n; ++i) out[k++] = (float)(v[i] / 448.0);
+  return k;
+}
+
 bool valid_p(double p) { return p >= 0.0 && p < 1.0; }   // false for NaN
 uint32_t dropout_threshold(double p) { return (uint32_t)floor(p * 4294967296.0); }
 float dropout_scale(double p) { return (float)(1.0 / (1.0 - p)); }
@@ -315,6 +342,59 @@ int double_quant(const float* absmax, int64_t nblocks, int dq_blocksize, uint8_t
     return QLORA_ERR_ALIGN;
   return launch_status(qlk::launch_double_quant(absmax, nblocks, codes, scales, mean,
                                                 as_stream(stream)));
+}
+
+int double_quant_table(const float* absmax, int64_t nblocks, int dq_blocksize,
+                       const float* levels, int nlevels, uint8_t* codes, float* scales, float* mean,
+                       void* stream) {
+  int st = check_table8(levels, nlevels);
+  if (st) return st;
+  if (!absmax || !codes || !scales || !mean) return QLORA_ERR_NULL;
+  if (dq_blocksize != kDQBlock) return QLORA_ERR_UNSUPPORTED;
+  if (nblocks <= 0 || (nblocks + kDQBlock - 1) / kDQBlock > 0x7fffffff) return QLORA_ERR_SHAPE;
+  if (!aligned16(absmax) || !aligned16(codes) || !aligned16(scales) || !aligned16(mean))
+    return QLORA_ERR_ALIGN;
+  const qlk::Codebook8 cb8 = qlk::make_codebook8(levels, nlevels);
+  return launch_status(qlk::launch_double_quant(absmax, nblocks, codes, scales, mean,
+                                                as_stream(stream), &cb8));
+}
+
+int absmax_dequant(const uint8_t* codes, const float* scales, const float* mean, int64_t nblocks,
+                   int dq_blocksize, const float* levels, int nlevels, float* out, void* stream) {
+  int st = check_table8(levels, nlevels);
+  if (st) return st;
+  if (!codes || !scales || !mean || !out) return QLORA_ERR_NULL;
+  if (dq_blocksize != kDQBlock) return QLORA_ERR_UNSUPPORTED;
+  if (nblocks <= 0 || (nblocks + 255) / 256 > 0x7fffffff) return QLORA_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(mean) || !aligned16(out))
+    return QLORA_ERR_ALIGN;
+  const qlk::Codebook8 cb8 = qlk::make_codebook8(levels, nlevels);
+  return launch_status(qlk::launch_absmax_dequant(codes, scales, mean, nblocks, cb8, out,
+                                                  as_stream(stream)));
+}
+
+int dequant_tables(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                   const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
+                   const float* levels4, const float* levels8, int nlevels8, uint16_t* W_bf16,
+                   void* stream) {
+  int st = check_table8(levels8, nlevels8);
+  if (st) return st;
+  if (levels4) {
+    st = check_codebook(levels4);
+    if (st) return st;
+  }
+  if (!packed || !codes || !scales || !mean || !W_bf16) return QLORA_ERR_NULL;
+  if (blocksize != kBlock || dq_blocksize != kDQBlock) return QLORA_ERR_UNSUPPORTED;
+  st = check_weight_shape(N, K);
+  if (st) return st;
+  if (N * K / 32 / 256 > 0x7fffffff) return QLORA_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(codes) || !aligned16(scales) || !aligned16(mean) ||
+      !aligned16(W_bf16))
+    return QLORA_ERR_ALIGN;
+  const qlk::Codebook8 cb8 = qlk::make_codebook8(levels8, nlevels8);
+  const qlk::Codebook4 cb4 = levels4 ? qlk::make_codebook(levels4) : qlk::nf4_codebook4();
+  return launch_status(qlk::launch_nf4_dequant(packed, codes, scales, mean, N * K, cb4, W_bf16,
+                                               as_stream(stream), &cb8));
 }
 
 int nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
@@ -581,6 +661,13 @@ int dq_codebook(float* out256, int* n) {
   if (!out256 || !n) return QLORA_ERR_NULL;
   for (int i = 0; i < 256; ++i) out256[i] = (i < 255) ? (float)(i - 127) / 127.0f : 0.0f;
   *n = 255;
+  return QLORA_OK;
+}
+
+int dq_float8_codebook(float* out256, int* n) {
+  if (!out256 || !n) return QLORA_ERR_NULL;
+  for (int i = 0; i < 256; ++i) out256[i] = 0.0f;
+  *n = float8_levels(out256);
   return QLORA_OK;
 }
 

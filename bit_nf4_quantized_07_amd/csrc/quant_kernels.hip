@@ -169,6 +169,51 @@ k_dq_codes(const float* __restrict__ absmax, int64_t nb, const float* __restrict
   if (threadIdx.x == 0) scales[blockIdx.x] = s;
 }
 
+// double_quant with a second-level table passed as data (the same rules: the
+// code is the number of thresholds strictly below fp32(c / s_g), so ties go
+// to the lower index and a group with s_g = 0 gets the index of the level
+// nearest zero).
+__global__ void __launch_bounds__(256)
+k_dq_codes_table(const float* __restrict__ absmax, int64_t nb, const float* __restrict__ mean,
+                 Codebook8 cb, uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ float thr[255];
+  __shared__ float wmax[4];
+  const int nthr = cb.n - 1;
+  for (int i = threadIdx.x; i < nthr; i += blockDim.x) thr[i] = cb.thr[i];
+
+  const int64_t i = (int64_t)blockIdx.x * kDQBlock + threadIdx.x;
+  const bool valid = i < nb;
+  const float mu = mean[0];
+  const float c = valid ? absmax[i] - mu : 0.0f;
+  float m = fabsf(c);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float s = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float n2 = (s > 0.0f) ? c / s : 0.0f;
+  int lo = 0, hi = nthr;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (n2 > thr[mid]) lo = mid + 1; else hi = mid;
+  }
+  if (valid) codes[i] = (uint8_t)lo;
+  if (threadIdx.x == 0) scales[blockIdx.x] = s;
+}
+
+// a_hat of every block: fp32(fp32(levels[code] * s_g) + mean), one thread per
+// block, the table staged in LDS (codes past the table's end read 0).
+__global__ void __launch_bounds__(256)
+k_absmax_dequant(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+                 const float* __restrict__ mean, int64_t nb, Codebook8 cb, float* __restrict__ out) {
+  __shared__ float q8[256];
+  q8[threadIdx.x] = cb.lv[threadIdx.x];
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nb) return;
+  out[i] = absmax_decode_tab((int)codes[i], scales[i / kDQBlock], mean[0], q8);
+}
+
 // ---------------------------------------------------------------------------
 // nf4_dequant: a wave expands 2048 consecutive weights (1 KB packed, 4 KB
 // out) in four rounds; in round q lane L turns packed word 64 q + L (8
@@ -182,6 +227,17 @@ k_nf4_dequant(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ co
   nf4_dequant_block(packed, codes, scales, mean, nwords, cb, out, blockIdx.x);
 }
 
+// The same with the 8-bit levels from a table (staged in LDS).
+__global__ void __launch_bounds__(256)
+k_dequant_tables(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
+                 const float* __restrict__ scales, const float* __restrict__ mean, int64_t nwords,
+                 Codebook4 cb, Codebook8 cb8, uint16_t* __restrict__ out) {
+  __shared__ float q8[256];
+  q8[threadIdx.x] = cb8.lv[threadIdx.x];
+  __syncthreads();
+  nf4_dequant_block(packed, codes, scales, mean, nwords, cb, out, blockIdx.x, q8);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -189,6 +245,21 @@ Codebook4 make_codebook(const float* levels16) {
   Codebook4 cb;
   for (int i = 0; i < 16; ++i) cb.lv[i] = levels16[i];
   for (int i = 0; i < 15; ++i) {
+    const double m = ((double)cb.lv[i] + (double)cb.lv[i + 1]) * 0.5;   // exact in fp64
+    float t = (float)m;
+    if ((double)t > m) t = nextafterf(t, -INFINITY);                    // round toward -inf
+    cb.thr[i] = t;
+  }
+  return cb;
+}
+
+Codebook8 make_codebook8(const float* levels, int n) {
+  Codebook8 cb;
+  cb.n = n;
+  for (int i = 0; i < 256; ++i) cb.lv[i] = i < n ? levels[i] : 0.0f;
+  for (int i = 0; i < 255; ++i) {
+    cb.thr[i] = 0.0f;
+    if (i + 1 >= n) continue;
     const double m = ((double)cb.lv[i] + (double)cb.lv[i + 1]) * 0.5;   // exact in fp64
     float t = (float)m;
     if ((double)t > m) t = nextafterf(t, -INFINITY);                    // round toward -inf
@@ -214,7 +285,7 @@ hipError_t launch_nf4_quantize(const float* W, int64_t numel, const Codebook4& c
 }
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, float* scales,
-                               float* mean, hipStream_t st) {
+                               float* mean, hipStream_t st, const Codebook8* cb8) {
   const int64_t ng = (nb + kDQBlock - 1) / kDQBlock;
   if (ng == 1) {
     hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(1024), 0, st, absmax, nb, mean);
@@ -230,17 +301,33 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* codes, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_dq_codes, dim3((unsigned)ng), dim3(256), 0, st, absmax, nb, mean, codes, scales);
+  if (cb8)
+    hipLaunchKernelGGL(k_dq_codes_table, dim3((unsigned)ng), dim3(256), 0, st, absmax, nb, mean,
+                       *cb8, codes, scales);
+  else
+    hipLaunchKernelGGL(k_dq_codes, dim3((unsigned)ng), dim3(256), 0, st, absmax, nb, mean, codes,
+                       scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax_dequant(const uint8_t* codes, const float* scales, const float* mean,
+                                 int64_t nb, const Codebook8& cb8, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_absmax_dequant, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, codes,
+                     scales, mean, nb, cb8, out);
   return hipGetLastError();
 }
 
 hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const float* scales,
                               const float* mean, int64_t numel, const Codebook4& cb, uint16_t* out,
-                              hipStream_t st) {
+                              hipStream_t st, const Codebook8* cb8) {
   const int64_t nwords = numel / 8;                  // numel % 64 == 0
   const int64_t grid = (nwords + 1023) / 1024;        // 4 waves x 256 words
-  hipLaunchKernelGGL(k_nf4_dequant, dim3((unsigned)grid), dim3(256), 0, st, packed, codes, scales,
-                     mean, nwords, cb, out);
+  if (cb8)
+    hipLaunchKernelGGL(k_dequant_tables, dim3((unsigned)grid), dim3(256), 0, st, packed, codes,
+                       scales, mean, nwords, cb, *cb8, out);
+  else
+    hipLaunchKernelGGL(k_nf4_dequant, dim3((unsigned)grid), dim3(256), 0, st, packed, codes,
+                       scales, mean, nwords, cb, out);
   return hipGetLastError();
 }
 

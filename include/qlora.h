@@ -122,6 +122,36 @@ int codebook_dequant(const uint8_t* packed, const uint8_t* codes, const float* s
                      const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
                      const float* levels, uint16_t* W_bf16, void* stream);
 
+/* ---- other 8-bit codes for the second level ------------------------------ */
+
+/* The pages give the second level only as "8 bits" (auryth.ai "QLoRA",
+ * Dubbele Quantisatie box; llm-compass "QLoRA", 方法与公式 item 2).  The layer
+ * uses the linear code Q8[i] = (i - 127) / 127; these calls take any
+ * second-level table as data, e.g. the 8-bit-float table of
+ * dq_float8_codebook, whose levels are dense near zero, so the ordinary
+ * constants of a group whose scale an outlier sets keep their precision.
+ *   levels   HOST memory, 2 <= nlevels <= 256 finite values, strictly
+ *            ascending (QLORA_ERR_ARG otherwise); code byte = index
+ * Rules as double_quant (mean, centring, per-256 scale, nearest level with
+ * ties to the lower index; a group with scale 0 gets the level nearest 0).
+ * Bit-exact; with the linear table the codes equal double_quant's. */
+int double_quant_table(const float* absmax, int64_t nblocks, int dq_blocksize,
+                       const float* levels, int nlevels, uint8_t* codes, float* scales,
+                       float* mean, void* stream);
+
+/* a_hat[b] = fp32(fp32(levels[codes[b]] * scales[b / 256]) + mean), fp32
+ * [nblocks] (codes from nlevels on read 0).  Bit-exact. */
+int absmax_dequant(const uint8_t* codes, const float* scales, const float* mean,
+                   int64_t nblocks, int dq_blocksize, const float* levels, int nlevels,
+                   float* out, void* stream);
+
+/* nf4_dequant (or codebook_dequant with levels4; NULL = NF4) with the second
+ * level decoded from levels8.  Bit-exact. */
+int dequant_tables(const uint8_t* packed, const uint8_t* codes, const float* scales,
+                   const float* mean, int64_t N, int64_t K, int blocksize, int dq_blocksize,
+                   const float* levels4, const float* levels8, int nlevels8, uint16_t* W_bf16,
+                   void* stream);
+
 /* ---- the linear layer --------------------------------------------------- */
 
 /* Forward  Y = X W_hat^T + s (X A^T) B^T,  s = fp32(alpha / r)
@@ -389,6 +419,12 @@ int nf4_codebook(float* out16);
 
 /* The 8-bit levels the kernels use (HOST memory, 256 floats; *n = 255). */
 int dq_codebook(float* out256, int* n);
+
+/* The 8-bit-float second-level table (HOST memory, 256 floats; *n = 253):
+ * every finite value of the 8-bit float with 4 exponent bits (bias 7) and 3
+ * mantissa bits, divided by its largest value 448 (each quotient rounded once
+ * to fp32), ascending, zero at index 126; entries from 253 on are 0. */
+int dq_float8_codebook(float* out256, int* n);
 
 /* Static text for a status code. */
 const char* qlora_strerror(int status);

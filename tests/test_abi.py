@@ -49,6 +49,33 @@ def test_codebooks_match_oracle_bits():
     assert np.array_equal(got8.view(np.uint32), oracle.dq_codebook().view(np.uint32))
 
 
+def test_float8_table_matches_oracle_bits():
+    got = np.array(q.dq_float8_levels(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.dq_float8_codebook().view(np.uint32))
+
+
+def test_second_level_table_validation():
+    lv = (ctypes.c_float * 253)(*q.dq_float8_levels())
+    bad = (ctypes.c_float * 3)(0.0, -1.0, 1.0)
+    P = ctypes.cast(lv, ctypes.c_void_p)
+    B = ctypes.cast(bad, ctypes.c_void_p)
+    dq, ad, dt = lib.double_quant_table, lib.absmax_dequant, lib.dequant_tables
+    assert dq(D, 100, 256, None, 253, D, D, D, None) == q.ERR_NULL
+    assert dq(D, 100, 256, P, 1, D, D, D, None) == q.ERR_ARG          # too few levels
+    assert dq(D, 100, 256, P, 257, D, D, D, None) == q.ERR_ARG
+    assert dq(D, 100, 256, B, 3, D, D, D, None) == q.ERR_ARG          # not ascending
+    assert dq(D, 100, 128, P, 253, D, D, D, None) == q.ERR_UNSUPPORTED
+    assert dq(D, 0, 256, P, 253, D, D, D, None) == q.ERR_SHAPE
+    assert dq(D, 100, 256, P, 253, D, D, MIS, None) == q.ERR_ALIGN
+    assert ad(D, D, D, 100, 256, P, 253, None, None) == q.ERR_NULL
+    assert ad(D, D, D, 100, 256, B, 3, D, None) == q.ERR_ARG
+    assert ad(D, D, D, 100, 256, P, 253, MIS, None) == q.ERR_ALIGN
+    assert dt(D, D, D, D, 4, 64, 64, 256, None, P, 253, None, None) == q.ERR_NULL
+    assert dt(D, D, D, D, 4, 64, 64, 256, None, B, 3, D, None) == q.ERR_ARG
+    assert dt(D, D, D, D, 4, 65, 64, 256, None, P, 253, D, None) == q.ERR_SHAPE
+    assert dt(D, D, D, D, 4, 64, 64, 256, B, P, 253, D, None) == q.ERR_ARG   # levels4 read as 16
+
+
 def test_strerror_and_version():
     for code in range(0, -9, -1):
         s = lib.qlora_strerror(code).decode()
