@@ -7,7 +7,10 @@
 // Two kernels:
 //  1. k_lora_down_partial: T = X A^T split over K into kTSplits partial sums
 //     (fp32, workspace), one workgroup per (32 adapter rows, K slice).
-//  2. k_gemv_nf4: workgroup = 4 waves = 64 weight rows (two groups of 32).
+//  2. the weight stream, which adds the partials in a fixed order: the split
+//     kernel k_gemv_split further below where its shapes allow, else
+//     k_gemv_dma / k_gemv_nf4.
+//     k_gemv_nf4: workgroup = 4 waves = 64 weight rows (two groups of 32).
 //     The four waves split K into quarters and reduce their partial products
 //     through LDS in a fixed order.  Per 64-weight block, each lane loads the
 //     16 contiguous packed bytes (32 nibbles) of one row that its lane group
@@ -395,13 +398,16 @@ k_gemv_dma(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __re
 }
 
 // Partial sums of T = X A^T for M <= 16 over kTSplits slices of K: workgroup
-// (jt, z) covers adapter rows 32*jt .. +31 and K slice z; its four waves take
-// a quarter of the slice each and are reduced through LDS in a fixed order.
-// MFMA rows = tokens (zero-padded), columns = adapter rows.
-__global__ void __launch_bounds__(256)
+// (jt, z) covers adapter rows 32*jt .. +31 and K slice z; its eight waves
+// take an eighth of the slice each (one 64-block on K = 8192, so every load
+// of the kernel is in flight at once) and are reduced through LDS in a fixed
+// order.  MFMA rows = tokens (zero-padded), columns = adapter rows.
+constexpr int kTWaves = 8;
+
+__global__ void __launch_bounds__(64 * kTWaves)
 k_lora_down_partial(const uint16_t* __restrict__ X, int M, int64_t K, const uint16_t* __restrict__ A,
                     int r, float* __restrict__ Tpart) {
-  __shared__ float red[4][8][64];
+  __shared__ float red[kTWaves][8][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, h = lane >> 5;
   const int j = blockIdx.x * 32 + c;
@@ -409,7 +415,7 @@ k_lora_down_partial(const uint16_t* __restrict__ X, int M, int64_t K, const uint
   const bool jvalid = j < r, mvalid = c < M;
   const int64_t nkb = K / kBlock;
   const int64_t zb0 = z * nkb / kTSplits, zb1 = (z + 1) * nkb / kTSplits;
-  const int64_t kb0 = zb0 + wave * (zb1 - zb0) / 4, kb1 = zb0 + (wave + 1) * (zb1 - zb0) / 4;
+  const int64_t kb0 = zb0 + wave * (zb1 - zb0) / kTWaves, kb1 = zb0 + (wave + 1) * (zb1 - zb0) / kTWaves;
   const uint16_t* xrow = X + (int64_t)(mvalid ? c : 0) * K + 32 * h;
   const uint16_t* arow = A + (int64_t)(jvalid ? j : 0) * K + 32 * h;
   f32x16_t acc;
@@ -434,7 +440,8 @@ k_lora_down_partial(const uint16_t* __restrict__ X, int M, int64_t K, const uint
     for (int v = 0; v < 8; ++v) {
       const int m = (v >> 2) * 8 + 4 * h + (v & 3);
       if (m < M && jvalid) {
-        const float sum = ((red[0][v][lane] + red[1][v][lane]) + red[2][v][lane]) + red[3][v][lane];
+        float sum = red[0][v][lane];
+        for (int ww = 1; ww < kTWaves; ++ww) sum += red[ww][v][lane];
         Tpart[((int64_t)z * M + m) * r + j] = sum;
       }
     }
@@ -472,15 +479,14 @@ k_lora_down_partial(const uint16_t* __restrict__ X, int M, int64_t K, const uint
 //    MFMA's 16 token rows hold the tokens of block b in rows 0-7 and those of
 //    block b + 1 in rows 8-15 (each half's activations are zero in the other
 //    block's lanes), so two blocks with different a_hat share one MFMA chain;
-//  * T = Xa A^T: every workgroup computes the same T from A (bf16, through
-//    L2) on its wave slices before the weight loop, adds the slices in a fixed
-//    order at the end and rounds it to bf16; the adapter term s T B^T of each
-//    row group is one more MFMA chain over r, and Y is rounded once.  For
-//    M <= 8 each 16-row A tile is loaded as 64 contiguous bytes per row and
-//    instruction and put into the activations' contraction order by a 4 x 4
-//    exchange between the lane groups (v_permlane32_swap, v_permlane16_swap).
-//    Workgroup 0 writes T; every workgroup computes the same T in the same
-//    order, so the result does not depend on which one wrote it.
+//  * T = Xa A^T comes from the 16 K-slice partials of k_lora_down_partial,
+//    launched just before (16 small workgroups, one round trip of loads):
+//    each workgroup adds them in a fixed order and rounds T once to bf16
+//    before its weight stream starts, and workgroup 0 writes T.  Computing T
+//    in every workgroup instead (all of A, 256 KB on K = 8192, through L2 in
+//    eight dependent rounds per wave) held the weight stream back by 6 us;
+//  * the adapter term s T B^T of each row group is one more MFMA chain over
+//    r, and Y is rounded once.
 //
 //   Y = X W_hat^T + s T B^T,   T = Xa A^T   (llm-compass "QLoRA", 方法与公式,
 //                                            the equation; Xa = X unless the
@@ -500,45 +506,17 @@ struct GsShape {
   static constexpr int D = NU < kGsRing ? NU : kGsRing;
 };
 
-// 4 x 4 exchange of 16-byte pieces between the four lane groups (lanes
-// 16 g .. 16 g + 15): on return, register j of lane group g holds what
-// register g of lane group j held.
-__device__ __forceinline__ void lane_group_transpose4(bf16x8_t (&v)[4]) {
-  uint32_t d[4][4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 x = __builtin_bit_cast(uint4, v[q]);
-    d[q][0] = x.x; d[q][1] = x.y; d[q][2] = x.z; d[q][3] = x.w;
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    // lane groups 2-3 of registers 0, 1 <-> lane groups 0-1 of registers 2, 3
-    auto s02 = __builtin_amdgcn_permlane32_swap(d[0][e], d[2][e], false, false);
-    d[0][e] = s02[0]; d[2][e] = s02[1];
-    auto s13 = __builtin_amdgcn_permlane32_swap(d[1][e], d[3][e], false, false);
-    d[1][e] = s13[0]; d[3][e] = s13[1];
-    // then within each pair of lane groups: odd group of register 2i <-> even
-    // group of register 2i + 1
-    auto s01 = __builtin_amdgcn_permlane16_swap(d[0][e], d[1][e], false, false);
-    d[0][e] = s01[0]; d[1][e] = s01[1];
-    auto s23 = __builtin_amdgcn_permlane16_swap(d[2][e], d[3][e], false, false);
-    d[2][e] = s23[0]; d[3][e] = s23[1];
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = __builtin_bit_cast(bf16x8_t, make_uint4(d[q][0], d[q][1], d[q][2], d[q][3]));
-}
-
 template <int S, bool PAIR, int MI, int RT>
 __global__ void __launch_bounds__(kGsThreads)
-k_gemv_split(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Xa, int M, NF4Weight w,
-             const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
-             uint16_t* __restrict__ Y, uint16_t* __restrict__ T_out, int rows_wg) {
+k_gemv_split(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __restrict__ Tpart,
+             const uint16_t* __restrict__ B, int r, float s, uint16_t* __restrict__ Y,
+             uint16_t* __restrict__ T_out, int rows_wg) {
   using Sh = GsShape<S, PAIR>;
   constexpr int NU = Sh::NU, MF = Sh::MF, CW = Sh::CW, D = Sh::D;
   constexpr int PARTW = kGsWaves * 64 * MI;      // floats of one row group's partials
   __shared__ __attribute__((aligned(16))) uint32_t tbl[kGsTable];           // 64 KB
   __shared__ __attribute__((aligned(16))) float part[kGsMaxRG * PARTW];     // 16 or 64 KB
-  __shared__ __attribute__((aligned(16))) float tpart[RT * kGsWaves * 64 * 4];
+  __shared__ __attribute__((aligned(16))) uint16_t tl[kGemvMaxM * 16 * RT];   // T, bf16 [M][r]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -640,45 +618,17 @@ k_gemv_split(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Xa, in
         xop[u][j] = __builtin_bit_cast(bf16x8_t, bload128s(rx, off, 0));
       }
   };
-  load_x(Xa);
+  load_x(X);
 
-  // --- T partials of the slice, 16 adapter rows per tile -------------------
-  {
-    const __amdgpu_buffer_rsrc_t ra = rsrc_whole(A, (uint32_t)((int64_t)r * K * 2));
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int ri = rt * 16 + col;
-      f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        bf16x8_t av[MF];
-        if constexpr (PAIR) {
-          // instruction q: lane group g loads 16-byte piece 4 q + g of the
-          // row's two-block run; the unit's operand for MFMA j in lane group g
-          // is piece 4 g + j
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t off = ri < r ? (uint32_t)(((int64_t)ri * K + (int64_t)(kb0 + 2 * u) * kBlock) * 2 +
-                                                     64 * q + 16 * g)
-                                        : kOOB;
-            av[q] = __builtin_bit_cast(bf16x8_t, bload128s(ra, off, 0));
-          }
-          lane_group_transpose4(av);
-        } else {
-#pragma unroll
-          for (int j = 0; j < MF; ++j) {
-            const uint32_t off = ri < r ? (uint32_t)(((int64_t)ri * K + (int64_t)(kb0 + u) * kBlock + 16 * g + 8 * j) * 2)
-                                        : kOOB;
-            av[j] = __builtin_bit_cast(bf16x8_t, bload128s(ra, off, 0));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < MF; ++j) c = mfma_16x16x32(xop[u][j], av[j], c);
-      }
-      *reinterpret_cast<f32x4_t*>(&tpart[((rt * kGsWaves + wave) * 64 + lane) * 4]) = c;
-    }
+  // --- T = the sum of the partials (fixed order), rounded once to bf16 ------
+  for (int i = tid; i < M * r; i += kGsThreads) {
+    float t = 0.0f;
+    for (int z = 0; z < kTSplits; ++z) t += Tpart[(int64_t)z * M * r + i];
+    const uint16_t tb = f32_to_bf16(t);
+    tl[i] = tb;
+    if (blockIdx.x == 0) T_out[i] = tb;
   }
-  if (Xa != X) load_x(X);
+  __syncthreads();   // the level table (each wave fills entries every wave reads) and T
 
   // --- the weight stream -----------------------------------------------------
   for (int jr = 0; jr < rgs; ++jr) {
@@ -725,31 +675,8 @@ k_gemv_split(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Xa, in
   }
   __syncthreads();
 
-  // --- T, the adapter term, Y (the table's space is free now) ---------------
-  uint16_t* tl = reinterpret_cast<uint16_t*>(tbl);            // T bf16 [M][r]
-  float* ad = reinterpret_cast<float*>(tbl) + 2048;           // (T B^T)[16 jr + row][m]
-  // C row 4 g + i of a slice's MFMA is token (4 g + i) % 8 of block half
-  // (4 g + i) / 8 (M <= 8) or token 4 g + i; slices and halves are added in a
-  // fixed order.
-  for (int i = tid; i < RT * 16 * M; i += kGsThreads) {
-    const int rt = i / (16 * M), m = (i / 16) % M, cc = i % 16;
-    const int rr = rt * 16 + cc;
-    float t = 0.0f;
-    for (int ww = 0; ww < kGsWaves; ++ww) {
-      const float* tp = tpart + (rt * kGsWaves + ww) * 64 * 4;
-      if (PAIR) {
-        for (int h = 0; h < 2; ++h) t += tp[(cc + 16 * (2 * h + (m >> 2))) * 4 + (m & 3)];
-      } else {
-        t += tp[(cc + 16 * (m >> 2)) * 4 + (m & 3)];
-      }
-    }
-    if (rr < r) {
-      const uint16_t tb = f32_to_bf16(t);
-      tl[m * r + rr] = tb;
-      if (blockIdx.x == 0) T_out[m * r + rr] = tb;
-    }
-  }
-  __syncthreads();
+  // --- the adapter term and Y (the table's space is free now) --------------
+  float* ad = reinterpret_cast<float*>(tbl);                  // (T B^T)[16 jr + row][m]
   if (wave < rgs) {   // wave w: adapter term of row group w, tokens x rows
     f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -793,55 +720,53 @@ static int gemv_split_rows(int64_t N, int64_t K, int r) {
 }
 
 template <int S, int RT>
-static void launch_gemv_split_rt(const uint16_t* X, const uint16_t* Xa, int M, const NF4Weight& w,
-                                 const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                                 uint16_t* T, int rows_wg, hipStream_t st) {
+static void launch_gemv_split_rt(const uint16_t* X, int M, const NF4Weight& w, const float* Tpart,
+                                 const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T,
+                                 int rows_wg, hipStream_t st) {
   const dim3 grid((unsigned)((w.N + rows_wg - 1) / rows_wg));
   if (M == 1)
-    hipLaunchKernelGGL((k_gemv_split<S, true, 1, RT>), grid, dim3(kGsThreads), 0, st, X, Xa, M, w,
-                       A, B, r, s, Y, T, rows_wg);
+    hipLaunchKernelGGL((k_gemv_split<S, true, 1, RT>), grid, dim3(kGsThreads), 0, st, X, M, w,
+                       Tpart, B, r, s, Y, T, rows_wg);
   else if (M <= 8)
-    hipLaunchKernelGGL((k_gemv_split<S, true, 4, RT>), grid, dim3(kGsThreads), 0, st, X, Xa, M, w,
-                       A, B, r, s, Y, T, rows_wg);
+    hipLaunchKernelGGL((k_gemv_split<S, true, 4, RT>), grid, dim3(kGsThreads), 0, st, X, M, w,
+                       Tpart, B, r, s, Y, T, rows_wg);
   else
-    hipLaunchKernelGGL((k_gemv_split<S, false, 4, RT>), grid, dim3(kGsThreads), 0, st, X, Xa, M, w,
-                       A, B, r, s, Y, T, rows_wg);
+    hipLaunchKernelGGL((k_gemv_split<S, false, 4, RT>), grid, dim3(kGsThreads), 0, st, X, M, w,
+                       Tpart, B, r, s, Y, T, rows_wg);
 }
 
 template <int S>
-static void launch_gemv_split_s(const uint16_t* X, const uint16_t* Xa, int M, const NF4Weight& w,
-                                const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
-                                uint16_t* T, int rows_wg, hipStream_t st) {
-  if (r <= 16) launch_gemv_split_rt<S, 1>(X, Xa, M, w, A, B, r, s, Y, T, rows_wg, st);
-  else if (r <= 32) launch_gemv_split_rt<S, 2>(X, Xa, M, w, A, B, r, s, Y, T, rows_wg, st);
-  else launch_gemv_split_rt<S, 4>(X, Xa, M, w, A, B, r, s, Y, T, rows_wg, st);
+static void launch_gemv_split_s(const uint16_t* X, int M, const NF4Weight& w, const float* Tpart,
+                                const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T,
+                                int rows_wg, hipStream_t st) {
+  if (r <= 16) launch_gemv_split_rt<S, 1>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st);
+  else if (r <= 32) launch_gemv_split_rt<S, 2>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st);
+  else launch_gemv_split_rt<S, 4>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st);
 }
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
                        const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T, float* Tpart,
                        hipStream_t st, const uint16_t* Xa, const Timing* tm) {
   if (!Xa) Xa = X;
+  // The timed interval covers the whole small-M forward: the T partials and
+  // the weight stream.
+  timer_begin(tm, TK_GEMV, st);
+  hipLaunchKernelGGL(k_lora_down_partial, dim3((r + 31) / 32, kTSplits), dim3(64 * kTWaves), 0, st,
+                     Xa, (int)M, w.K, A, r, Tpart);
   const int rows_wg = gemv_split_rows(w.N, w.K, r);
   if (rows_wg > 0) {
-    timer_begin(tm, TK_GEMV, st);
     switch (w.K / kBlock) {
-      case 32: launch_gemv_split_s<4>(X, Xa, (int)M, w, A, B, r, s, Y, T, rows_wg, st); break;
-      case 64: launch_gemv_split_s<8>(X, Xa, (int)M, w, A, B, r, s, Y, T, rows_wg, st); break;
-      default: launch_gemv_split_s<16>(X, Xa, (int)M, w, A, B, r, s, Y, T, rows_wg, st); break;
+      case 32: launch_gemv_split_s<4>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st); break;
+      case 64: launch_gemv_split_s<8>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st); break;
+      default: launch_gemv_split_s<16>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st); break;
     }
-    timer_end(tm, TK_GEMV, st);
-    return hipGetLastError();
+  } else {
+    const unsigned grid = (unsigned)((w.N + 63) / 64);
+    if ((w.K / kBlock) % (4 * kGemvSS) == 0)
+      hipLaunchKernelGGL(k_gemv_dma<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
+    else
+      hipLaunchKernelGGL(k_gemv_nf4<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
   }
-  hipLaunchKernelGGL(k_lora_down_partial, dim3((r + 31) / 32, kTSplits), dim3(256), 0, st,
-                     Xa, (int)M, w.K, A, r, Tpart);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((w.N + 63) / 64);
-  timer_begin(tm, TK_GEMV, st);
-  if ((w.K / kBlock) % (4 * kGemvSS) == 0)
-    hipLaunchKernelGGL(k_gemv_dma<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
-  else
-    hipLaunchKernelGGL(k_gemv_nf4<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
   timer_end(tm, TK_GEMV, st);
   return hipGetLastError();
 }
