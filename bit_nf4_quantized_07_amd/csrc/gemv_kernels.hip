@@ -581,14 +581,12 @@ k_gemv_split(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __
     bpre[c] = bload128s(rb, bvalid && 32 * c + 8 * g < r ? (uint32_t)((bn * r + 32 * c + 8 * g) * 2) : kOOB, 0);
 
   // --- the byte -> (level of the high nibble, level of the low nibble)
-  // table, one column per lane.  Thread t fills entries e = t / 64 + 8 k of
-  // its lane's column: the high nibble of e is k / 2, the low t / 64 + 8 (k & 1).
-  {
-    const int e0 = tid >> 6;
-    const float lo0 = nf4_level(e0), lo1 = nf4_level(e0 + 8);
+  // table, one column per lane.  Thread t fills entries e = 8 k + t / 64 of
+  // its lane's column.
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
-      tbl[k * kGsThreads + tid] = pack_bf16x2(nf4_level(k >> 1), (k & 1) ? lo1 : lo0);
+  for (int k = 0; k < 256 / kGsWaves; ++k) {
+    const int e = kGsWaves * k + (tid >> 6);
+    tbl[k * kGsThreads + tid] = pack_bf16x2(nf4_level(e >> 4), nf4_level(e & 15));
   }
   const uint32_t lane4 = (uint32_t)lane * 4u;
 
@@ -657,9 +655,9 @@ k_gemv_split(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __
         uint32_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // byte e of the word: address = byte * 256 + 4 * lane
+          // byte e of the word: byte address = byte * 256 + 4 * lane
           const uint32_t addr = __builtin_amdgcn_perm(words[j], lane4, 0x0C0C0400u | ((4u + e) << 8));
-          o[e] = tbl[addr >> 2];
+          o[e] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(tbl) + addr);
         }
         c = mfma_16x16x32(xop[u][j], __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3])), c);
       }
