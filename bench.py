@@ -54,6 +54,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "bit_nf4_quantized_07_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DURATIONS_FILE = os.path.join(ROOT, "profiles", "kernel_durations.json")
 
 
 def err(*a):
@@ -76,7 +77,7 @@ def source_hash(files=None) -> str:
 PROFILED = {
     "dx_gemm": ("k_dx_nf4<true, false>", "dx_kernels.hip", "c2_linear_4096"),
     "fwd_gemm": ("k_fwd_nf4<false>", "fwd_kernels.hip", "c2_linear_4096"),
-    "gemv": ("k_gemv_dma", "gemv_kernels.hip", "c4_gemv_28672x8192"),
+    "gemv": ("k_gemv_split", "gemv_kernels.hip", "c4_gemv_28672x8192"),
     "dx_prep": ("k_rank16_and_dequant", "adapter_kernels.hip+dequant_block.h", "c2_linear_4096"),
 }
 
@@ -143,6 +144,25 @@ def gemv_bytes(M, N, K, r):
     nb = N * K // 64
     return (N * K // 2 + nb + 4 * ((nb + 255) // 256) + 4 + 2 * M * K + 2 * N * r
             + 2 * M * r + 2 * M * N)
+
+
+def profile_duration(kernel: str, workload: str):
+    """Average dispatch duration (us) of a kernel on a workload in the committed
+    rocprofv3 kernel trace, if it was taken on the current kernel sources; else
+    None.  Reported next to the event-timed average of the same kernel (an
+    event record around a kernel adds a few us and breaks back-to-back
+    dispatch)."""
+    try:
+        with open(DURATIONS_FILE) as fh:
+            d = json.load(fh).get("kernels", {}).get(kernel)
+    except Exception:
+        return None
+    if not d or d.get("workload") != workload:
+        return None
+    src = PROFILED[kernel][1]
+    if d.get("source_hash") != source_hash(src.split("+")):
+        return None
+    return d["avg_us"]
 
 
 def traffic_for(kernel: str, launch_units: dict):
@@ -278,6 +298,11 @@ def run_linear(args, q, torch, wl, lib, ev):
                     frac=round(kd["tflops"] / PEAK_BF16_TFLOPS, 4),
                     traffic=traffic_for(dom, units),
                     avg_us=round(kd["avg_us"], 2))
+    prof = profile_duration(dom, cfg.name)
+    if prof:
+        roofline.update(profile_avg_us=round(prof, 2),
+                        profile_frac=round(kd["flops_per_launch"] / (prof * 1e-6) / 1e12
+                                           / PEAK_BF16_TFLOPS, 4))
     value = flops / (ms * 1e-3) / 1e12
     config = dict(workload=cfg.name, M=M, N=lin.N, K=lin.K, r=lin.r, alpha=lin.alpha,
                   blocksize=64, dq_blocksize=256, input_sets=args.sets,
@@ -320,6 +345,34 @@ def run_linear(args, q, torch, wl, lib, ev):
                         step_over_plain_step=round(ms_drop / ms, 4))
     return dict(value=value, ms=ms, config=config, roofline=roofline, lora_bf16=lora_bf16,
                 lora_dropout=lora_dropout, kernels=kernels)
+
+
+def run_c1(args, q, torch, wl):
+    """Configuration 1 (16 tokens, 256 x 256, r = 8): the latency of one
+    fwd + bwd step.  Wall clock per step over back-to-back steps (host
+    launch-bound at this size), and the GPU time between events around the
+    same loop."""
+    cfg = wl.workloads()["c1_linear_256"]
+    lin = cfg.linears[0]
+    M = cfg.M
+    sets = make_linear_sets(q, torch, wl, cfg.name, 0, M, 2)
+    ws = q.Workspace("cuda")
+    ws.get(max(q.workspace_bytes(M, lin.K, lin.N, lin.r, b) for b in (False, True)))
+    for i in range(20):
+        linear_step(q, sets[i % 2], ws)
+    torch.cuda.synchronize()
+    n = 200
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for i in range(n):
+        linear_step(q, sets[i % 2], ws)
+    b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return dict(workload=cfg.name, M=M, N=lin.N, K=lin.K, r=lin.r,
+                us_per_step=round((t1 - t0) / n * 1e6, 2),
+                gpu_us_per_step=round(a.elapsed_time(b) * 1e3 / n, 2))
 
 
 def run_gemv(args, q, torch, wl, lib, ev):
@@ -439,7 +492,7 @@ def _linears(q, torch, wl, cfg, names):
     return out
 
 
-def run_blocks(args, q, torch, wl):
+def run_blocks(args, q, torch, wl, ev):
     """Whole workloads, forward and backward, in TFLOP/s of 4MNK + 6Mr(N+K)
     per linear:
       c3: the 11008-wide SiLU-gated MLP block (fused gate/up forward, down
@@ -502,7 +555,48 @@ def run_blocks(args, q, torch, wl):
     res["c5_decoder_layer"] = dict(ms_per_step=round(ms, 4), gflop=round(flops(c5) / 1e9, 2),
                                    tflops=round(flops(c5) / (ms * 1e-3) / 1e12, 1),
                                    frac_bf16_peak=round(flops(c5) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    res["c5_decoder_layer"]["kernels"] = c5_kernels(q, torch, wl, c5, L5, ws, dev_bf16, ev)
     return res
+
+
+def c5_kernels(q, torch, wl, c5, L5, ws, dev_bf16, ev):
+    """The decoder layer's GEMM kernels one projection at a time (layer calls
+    with the library's HIP events around the forward GEMM, the dX GEMM and the
+    U + dequantisation launch): average time per launch and, for the dominant
+    kernel (the largest time per step), its roofline."""
+    M = c5.M
+    shapes = {l.name: l for l in c5.linears}
+    per = {}
+    for n in ("q", "k", "v", "o", "gate", "up", "down"):
+        lin = shapes[n]
+        X = dev_bf16(wl.activations(1, c5.cfg_id, M, lin.K, sub=10))
+        dY = dev_bf16(wl.grad_output(1, c5.cfg_id, M, lin.N, sub=10))
+        qw, A, B, alpha = L5[n]
+        reps = 3
+        slots = (q.KERNEL_FWD_GEMM, q.KERNEL_DX_GEMM, q.KERNEL_DX_DEQUANT)
+        evs = {k: (ev.create(reps), ev.create(reps)) for k in slots}
+        for i in range(reps + 1):
+            t = None
+            if i > 0:
+                t = timing_for(q, {k: (a[i - 1], b[i - 1]) for k, (a, b) in evs.items()})
+            _, T = q.linear_fwd(X, qw, A, B, alpha, workspace=ws, timing=t)
+            q.linear_bwd(dY, X, qw, A, B, alpha, T=T, workspace=ws, timing=t)
+        torch.cuda.synchronize()
+        kfl = {q.KERNEL_FWD_GEMM: ("fwd_gemm", 2.0 * M * lin.N * (lin.K + lin.r)),
+               q.KERNEL_DX_GEMM: ("dx_gemm", 2.0 * M * lin.K * (lin.N + lin.r))}
+        for k, (name, fl) in kfl.items():
+            a, b = evs[k]
+            us = float(np.mean([ev.elapsed_ms(a[i], b[i]) for i in range(reps)])) * 1e3
+            per[f"{n}.{name}"] = dict(shape=f"{M}x{lin.N}x{lin.K}", avg_us=round(us, 1),
+                                      tflops=round(fl / (us * 1e-6) / 1e12, 1))
+        for a, b in evs.values():
+            ev.destroy(a + b)
+        del X, dY
+    dom = max(per, key=lambda key: per[key]["avg_us"])   # each runs once per layer step
+    d = per[dom]
+    roof = dict(bound="mfma", kernel=dom, achieved=d["tflops"], peak=PEAK_BF16_TFLOPS,
+                unit="TFLOP/s", frac=round(d["tflops"] / PEAK_BF16_TFLOPS, 4), avg_us=d["avg_us"])
+    return dict(per_launch=per, roofline=roof)
 
 
 def run_standalone(args, q, torch, lib, ev):
@@ -685,6 +779,42 @@ def run_cpu_baseline(budget_s: float):
                           blas=blas_backend()))
 
 
+def run_cpu_gemv_baseline(budget_s: float):
+    """The oracle's small-M forward (dequantisation of the rows it needs, then
+    Y = X W_hat^T + s T B^T in fp64) on a bounded row sample of the
+    28672 x 8192 weight, for M = 1, 4, 16: bytes of the sample as the GPU path
+    counts them (packed nibbles, codes, scales, X, B, T, Y) per second."""
+    import oracle
+    import qlora_workloads as wl
+    cfg = wl.workloads()["c4_gemv_28672x8192"]
+    lin = cfg.linears[0]
+    rows = 2048
+    # the first `rows` rows of the weight (the generator fills it row by row;
+    # this weight has no outliers)
+    g = wl.rng(0, cfg.cfg_id, wl.T_W, 0)
+    W = g.standard_normal((rows, lin.K), dtype=np.float32) * np.float32(lin.w_std)
+    c4, am = oracle.quantize_nf4(W, 64)
+    packed = oracle.pack_nibbles(c4)
+    c8, sc, mu = oracle.double_quant(am, 256)
+    A, B = wl.adapters(0, cfg.cfg_id, 0, lin)
+    Af, Bf = oracle.bf16_bits_to_f64(A), oracle.bf16_bits_to_f64(B)[:rows]
+    out = {}
+    for M in (1, 4, 16):
+        X = oracle.bf16_bits_to_f64(wl.activations(0, cfg.cfg_id, M, lin.K))
+        n, spent = 0, 0.0
+        while spent < budget_s / 3 or n == 0:
+            t0 = time.perf_counter()
+            _, wb = oracle.dequant_nf4(packed, c8, sc, mu, rows, lin.K)
+            oracle.forward(X, oracle.bf16_bits_to_f64(wb), Af, Bf, lin.alpha, lin.r)
+            spent += time.perf_counter() - t0
+            n += 1
+        nbytes = gemv_bytes(M, rows, lin.K, lin.r)
+        out[f"M{M}"] = dict(GBps=round(nbytes * n / spent / 1e9, 4), seconds=round(spent, 2),
+                            calls=n)
+    return dict(unit="GB/s", kind="oracle", workload=cfg.name,
+                sample=f"rows 0..{rows - 1} of {lin.N} (bytes of the sample per call)", **out)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -824,6 +954,24 @@ def summarize(out: str):
                 sym, key, grid, len(ds), float(np.mean(ds)), float(np.min(ds)), float(np.max(ds))))
     md += ["", "On the 2048 x 4096 x 4096 layer the forward kernel runs 256 workgroups of 256 "
            "work-items (grid 65536) and the dX kernel 256 of 512 (grid 131072)."]
+    # Average dispatch durations on the workloads the bench line reports (the
+    # c2 launch shape of each GEMM; M = 1 of the small-M forward), with the
+    # sources they were taken on, for the bench line's roofline.
+    c2_grid = {"fwd_gemm": 65536, "dx_gemm": 131072, "dx_prep": 786432}
+    durations = {}
+    for key, (sym, src, wk) in PROFILED.items():
+        ds = [(int(r["Grid_Size_X"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+              for r in trace if sym in r["Kernel_Name"]]
+        if key == "gemv":
+            ds = ds[:len(ds) // 3]   # M = 1 (the run takes M = 1, 4, 16 in order)
+        else:
+            ds = [d for d in ds if d[0] == c2_grid[key]]
+        if ds:
+            durations[key] = dict(kernel=sym, workload=wk, grid=ds[0][0], calls=len(ds),
+                                  avg_us=round(float(np.mean([d[1] for d in ds])), 3),
+                                  source_hash=source_hash(src.split("+")))
+    with open(DURATIONS_FILE, "w") as fh:
+        json.dump(dict(command=cmds["kt"], kernels=durations), fh, indent=1)
     with open(os.path.join(prof, "kernel_stats_default_bench.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
 
@@ -1010,6 +1158,8 @@ def main():
     err(f"[bench] device {torch.cuda.get_device_name(0)}; linear fwd+bwd ...")
     lin = run_linear(args, q, torch, wl, lib, ev)
     err(f"[bench] {lin['ms']:.3f} ms/step, kernels {lin['kernels']}")
+    c1 = run_c1(args, q, torch, wl)
+    err(f"[bench] c1 {c1}")
     gemv = None
     if not args.no_gemv:
         err("[bench] small-M forward ...")
@@ -1023,7 +1173,7 @@ def main():
     blocks = None
     if not args.no_blocks:
         err("[bench] MLP block and decoder layer ...")
-        blocks = run_blocks(args, q, torch, wl)
+        blocks = run_blocks(args, q, torch, wl, ev)
         err(f"[bench] blocks {blocks}")
     standalone = None
     if not args.no_standalone:
@@ -1037,6 +1187,8 @@ def main():
     if not args.no_cpu_baseline:
         err("[bench] CPU oracle baseline ...")
         cpu = run_cpu_baseline(args.cpu_budget)
+        if not args.no_gemv:
+            cpu["gemv"] = run_cpu_gemv_baseline(args.cpu_budget / 3)
         err(f"[bench] cpu {cpu}")
     line = dict(metric=METRIC, value=round(lin["value"], 2), unit="TFLOP/s", n_gpus=1,
                 steps=args.steps, warmup=args.warmup, ms_per_step=round(lin["ms"], 4),
@@ -1044,7 +1196,7 @@ def main():
                 data="synthetic", config=lin["config"], roofline=lin["roofline"],
                 cpu_baseline=cpu, kernels=lin["kernels"], lora_bf16_base=lin["lora_bf16"],
                 lora_dropout=lin["lora_dropout"],
-                gemv=gemv, mlp_gate_up=mlp, blocks=blocks, standalone=standalone,
+                c1=c1, gemv=gemv, mlp_gate_up=mlp, blocks=blocks, standalone=standalone,
                 source_hash=source_hash())
     if library:
         line["context_library_bf16_gemm"] = library

@@ -214,7 +214,7 @@ hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, co
   const int tiles = (r + 15) / 16;
   auto go = [&](auto rt, auto nw) {
     constexpr int RT = decltype(rt)::value, NW = decltype(nw)::value;
-    const int64_t dq_blocks = (nwords + NW * 256 - 1) / (NW * 256);
+    const int64_t dq_blocks = (nwords + NW * kDqWaveWords - 1) / (NW * kDqWaveWords);
     hipLaunchKernelGGL((k_rank16_and_dequant<RT, NW>), dim3((unsigned)(rank_blocks + dq_blocks)),
                        dim3(NW * 64), 0, st, S, (int)M, C, W, r, rows, out, rank_blocks, w.packed,
                        w.codes, w.scales, w.mean, nwords, cb, wout);

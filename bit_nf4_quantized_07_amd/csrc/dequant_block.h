@@ -1,6 +1,7 @@
 // Body of the dequantiser, shared by its own kernel and the backward's
 // combined kernel (U = dY B next to the one-off dequantisation).  One wave
-// handles 256 packed words (2048 weights) in four rounds: in round q lane L
+// handles 64 kDqRounds packed words in kDqRounds rounds (eight: 512 words,
+// 4096 weights, loads of eight words per lane in flight): in round q lane L
 // takes word 64 q + L of the wave's range, so every load and store
 // instruction of the wave covers one contiguous range.  The block's waves
 // take consecutive ranges; `blk` is the block's index in the dequant grid.
@@ -10,6 +11,9 @@
 #include "kernels.h"
 
 namespace qlk {
+
+constexpr int kDqRounds = 8;                      // rounds per wave (words per lane)
+constexpr int kDqWaveWords = 64 * kDqRounds;      // packed words per wave
 
 __device__ __forceinline__ void nf4_dequant_block(const uint8_t* __restrict__ packed,
                                                   const uint8_t* __restrict__ codes,
@@ -27,16 +31,17 @@ __device__ __forceinline__ void nf4_dequant_block(const uint8_t* __restrict__ pa
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t w0 = (blk_index * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 256;  // first word of the wave
+  const int64_t w0 = (blk_index * (blockDim.x >> 6) + (threadIdx.x >> 6)) * kDqWaveWords;  // first word of the wave
   const float mu = mean[0];
   const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed);
-  // All four rounds' loads first (an out-of-range word loads word 0 and is
-  // not stored), so that a wave has its twelve loads in flight together.
-  uint32_t p[4], cd[4];
-  float sc[4];
-  bool ok[4];
+  // All rounds' loads first (an out-of-range word loads word 0 and is
+  // not stored), so that all of a wave's loads (three per round) are in flight
+  // together.
+  uint32_t p[kDqRounds], cd[kDqRounds];
+  float sc[kDqRounds];
+  bool ok[kDqRounds];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kDqRounds; ++q) {
     const int64_t wd = w0 + 64 * q + lane;   // packed word: weights 8 wd .. 8 wd + 7
     ok[q] = wd < nwords;
     const int64_t wc = ok[q] ? wd : 0;
@@ -46,7 +51,7 @@ __device__ __forceinline__ void nf4_dequant_block(const uint8_t* __restrict__ pa
     sc[q] = scales[blk / kDQBlock];
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kDqRounds; ++q) {
     if (!ok[q]) continue;
     // 8-bit levels: the linear code computed, or a table (in LDS)
     const float ah = q8 ? absmax_decode_tab((int)cd[q], sc[q], mu, q8) : absmax_decode(cd[q], sc[q], mu);

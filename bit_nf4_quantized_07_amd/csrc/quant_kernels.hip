@@ -321,7 +321,7 @@ hipError_t launch_nf4_dequant(const uint8_t* packed, const uint8_t* codes, const
                               const float* mean, int64_t numel, const Codebook4& cb, uint16_t* out,
                               hipStream_t st, const Codebook8* cb8) {
   const int64_t nwords = numel / 8;                  // numel % 64 == 0
-  const int64_t grid = (nwords + 1023) / 1024;        // 4 waves x 256 words
+  const int64_t grid = (nwords + 4 * kDqWaveWords - 1) / (4 * kDqWaveWords);   // 4 waves
   if (cb8)
     hipLaunchKernelGGL(k_dequant_tables, dim3((unsigned)grid), dim3(256), 0, st, packed, codes,
                        scales, mean, nwords, cb, *cb8, out);
