@@ -414,6 +414,10 @@ def run_gemv(args, q, torch, wl, lib, ev):
                             call_us=round((t1 - t0) / n * 1e6, 2))
         if M == 1:
             out["M1"]["traffic"] = traffic_for("gemv", dict(workload=cfg.name))
+            prof = profile_duration("gemv", cfg.name)
+            if prof:
+                out["M1"].update(profile_kernel_us=round(prof, 2),
+                                 profile_frac_hbm=round(nbytes / (prof * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4))
     return dict(workload=cfg.name, N=lin.N, K=lin.K, r=lin.r, peak_GBps=PEAK_HBM_GBPS, **out)
 
 
@@ -957,15 +961,16 @@ def summarize(out: str):
     # Average dispatch durations on the workloads the bench line reports (the
     # c2 launch shape of each GEMM; M = 1 of the small-M forward), with the
     # sources they were taken on, for the bench line's roofline.
-    c2_grid = {"fwd_gemm": 65536, "dx_gemm": 131072, "dx_prep": 786432}
+    # The default run starts with the 2048 x 4096 x 4096 layer, so a GEMM's
+    # first dispatch has that layer's launch shape.
     durations = {}
     for key, (sym, src, wk) in PROFILED.items():
         ds = [(int(r["Grid_Size_X"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
               for r in trace if sym in r["Kernel_Name"]]
         if key == "gemv":
             ds = ds[:len(ds) // 3]   # M = 1 (the run takes M = 1, 4, 16 in order)
-        else:
-            ds = [d for d in ds if d[0] == c2_grid[key]]
+        elif ds:
+            ds = [d for d in ds if d[0] == ds[0][0]]
         if ds:
             durations[key] = dict(kernel=sym, workload=wk, grid=ds[0][0], calls=len(ds),
                                   avg_us=round(float(np.mean([d[1] for d in ds])), 3),
