@@ -290,19 +290,23 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
     load_wbi(1, wtb[0], kz0);
 #pragma unroll
     for (int j = 0; j < 3; ++j) load_dy(dyb[j], min(kz0 + j, kz1 - 1));
-    __builtin_amdgcn_s_waitcnt(dx_wait(8, 0));   // W(0) and dY(0) arrived
+    // W(0), dY(0) and dY(1) arrived (dY(2) may still be in flight): the last
+    // slot of step 0 reads the first operands of step 1, which other waves
+    // loaded.
+    __builtin_amdgcn_s_waitcnt(dx_wait(4, 0));
   } else {
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       load_dy(dyb[j], min(kz0 + j, kz1 - 1));
       load_w(wr[j], min(kz0 + j, kz1 - 1));
     }
-    // Only step 0's seven loads must have arrived (those of steps 1 and 2
-    // may still be in flight) before its weight is decoded and the barrier
-    // publishes dY(0) and W(0).
+    // Step 0's seven loads must have arrived before its weight is decoded;
+    // steps 0 and 1 (step 2's loads may still be in flight) before the
+    // barrier publishes dY(0), dY(1) and W(0): the last slot of step 0 reads
+    // the first operands of step 1, which other waves loaded.
     __builtin_amdgcn_s_waitcnt(dx_wait(14, 0));
     decode_all(wr[0], wtb[0]);
-    __builtin_amdgcn_s_waitcnt(dx_wait(14, 0));
+    __builtin_amdgcn_s_waitcnt(dx_wait(7, 0));
   }
   __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -528,6 +532,271 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   }
 }
 
+// ------------------------------------------------------------------------
+// Wide tile for large token counts on a bf16 weight (the dequantised copy):
+// one workgroup computes a 256 x 256 tile of dX (tokens x features) with
+// four waves, one per SIMD, each a 128 x 128 quarter: sixteen accumulators
+// of v_mfma_f32_32x32x16_bf16.  Every operand fragment read from LDS feeds
+// four MFMAs (two in the 256 x 128 tile above), so the LDS bytes read per
+// flop are half those of the eight-wave tile.  The contraction advances 32
+// weight rows per step through four LDS stages of 32 KB (a 256 x 32 dY tile
+// and a 32 x 256 weight tile each), filled by buffer loads that write LDS
+// directly, three steps ahead.
+//  * dY tile: rows of 64 bytes, the four 16-byte pieces of row m
+//    XOR-swizzled by (m >> 2) & 3: the operand reads (16 rows per bank
+//    cycle) are conflict-free.
+//  * Weight tile: rows n of 512 bytes (256 features), pieces XOR-swizzled by
+//    4 (n & 3), so that the transpose reads (4 rows x 4 pieces per bank
+//    cycle) are conflict-free.
+//  * The fp32 tile goes out through the stages in four passes of 64 tokens.
+constexpr int kWdBM = 256;                    // tokens per tile
+constexpr int kWdBK = 256;                    // features per tile
+constexpr int kWdStepN = 32;                  // contraction per step
+constexpr int kWdYTile = kWdBM * kWdStepN;    // elements per dY stage
+constexpr int kWdWTile = kWdStepN * kWdBK;    // elements per weight stage
+constexpr int kWdUnroll = 4;                  // steps per loop iteration (= stages)
+constexpr int kWdLoads = 8;                   // global loads per wave per step
+
+__global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t y0[kWdYTile];
+  __shared__ __attribute__((aligned(16))) uint16_t y1[kWdYTile];
+  __shared__ __attribute__((aligned(16))) uint16_t y2[kWdYTile];
+  __shared__ __attribute__((aligned(16))) uint16_t y3[kWdYTile];
+  __shared__ __attribute__((aligned(16))) uint16_t w0[kWdWTile];
+  __shared__ __attribute__((aligned(16))) uint16_t w1[kWdWTile];
+  __shared__ __attribute__((aligned(16))) uint16_t w2[kWdWTile];
+  __shared__ __attribute__((aligned(16))) uint16_t w3[kWdWTile];
+  uint16_t* const yb[4] = {y0, y1, y2, y3};
+  uint16_t* const wb[4] = {w0, w1, w2, w3};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  const int fg = wave & 1, tq = wave >> 1;   // feature half, token half
+
+  int tm, tk;
+  tile_coords((int)blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
+  const int m0 = tm * kWdBM;
+  const int64_t k0 = (int64_t)tk * kWdBK;
+  const int64_t N = g.w.N, K = g.w.K;
+  const int nsteps = (int)(N / kWdStepN);
+
+  // dY loads: load i of wave w fills rows 64 w + 16 i .. +15 (1 KB); lane L
+  // lands at row 64 w + 16 i + L / 4, physical piece L % 4, which holds
+  // logical piece (L % 4) ^ ((row >> 2) & 3).
+  const __amdgpu_buffer_rsrc_t rdy = rsrc_whole(g.dY, (uint32_t)((int64_t)g.M * N * 2));
+  uint32_t yoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 64 * wave + 16 * i + (lane >> 2);
+    const int piece = (lane & 3) ^ ((row >> 2) & 3);
+    yoff[i] = m0 + row < g.M ? (uint32_t)(((int64_t)(m0 + row) * N + piece * 8) * 2) : kOOB;
+  }
+  // Weight loads: load i of wave w fills rows 8 w + 2 i, +1 of the step
+  // (1 KB); lane L lands at row 8 w + 2 i + L / 32, physical piece L % 32,
+  // which holds logical piece (L % 32) ^ (4 (row & 3)).
+  const __amdgpu_buffer_rsrc_t rw = rsrc_whole(g.w.bf16, (uint32_t)(N * K * 2));
+  uint32_t woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * wave + 2 * i + (lane >> 5);
+    const int64_t col = k0 + 8 * ((lane & 31) ^ (4 * (row & 3)));
+    woff[i] = col < K ? (uint32_t)(((int64_t)row * K + col) * 2) : kOOB;
+  }
+  auto load_j = [&](int j, int buf, int kb) {
+    const uint32_t kbs = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
+    if (j < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rdy, (__attribute__((address_space(3))) void*)(yb[buf] + (64 * wave + 16 * j) * kWdStepN),
+          16, yoff[j], kbs * (kWdStepN * 2), 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(wb[buf] + (8 * wave + 2 * (j - 4)) * kWdBK),
+          16, woff[j - 4], kbs * kWdStepN * (uint32_t)K * 2u, 0, 0);
+    }
+  };
+  // dY operand of token block i (32 tokens) of this wave's half, MFMA step
+  // t: row 128 tq + 32 i + c, logical piece 2 t + h.
+  int yrd[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) yrd[t] = c * kWdStepN + (((2 * t + h) ^ ((c >> 2) & 3)) * 8);
+  auto yfrag = [&](int buf, int i, int t) -> bf16x8_t {
+    return *reinterpret_cast<const bf16x8_t*>(yb[buf] + (128 * tq + 32 * i) * kWdStepN + yrd[t]);
+  };
+  // Weight operand of feature block j (32 features) of this wave's half,
+  // MFMA step t: features 128 fg + 32 j + c, rows 16 t + 8 h + 0..7, by two
+  // transpose reads of four rows each.
+  const int grp = lane >> 4, gi = lane & 15;
+  int wrd[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int n = 16 * t + 8 * (grp >> 1) + 4 * half + (gi >> 2);
+      const int col = 128 * fg + 16 * (grp & 1) + 4 * (gi & 3);   // + 32 j
+      wrd[t][half] = n * kWdBK + (((col >> 3) ^ (4 * (n & 3))) << 3) + (col & 7);
+    }
+  auto wfrag = [&](int buf, int j, int t) -> bf16x8_t {
+    // Feature block j sets bits 2..3 of the logical piece (0 at j = 0), the
+    // bits the swizzle XORs: the physical offset is the j = 0 one XOR 32 j.
+    const uint16_t* base = wb[buf];
+    const v4s_t lo = lds_read_tr16(base + (wrd[t][0] ^ (32 * j)));
+    const v4s_t hi = lds_read_tr16(base + (wrd[t][1] ^ (32 * j)));
+    typedef short v8s_t __attribute__((ext_vector_type(8)));
+    const v8s_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+
+  f32x16_t acc[4][4];   // [feature block][token block]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+
+  bf16x8_t a[2][4], b[2][4];   // [MFMA step parity][block]
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int j = 0; j < kWdLoads; ++j) load_j(j, s, min(s, nsteps - 1));
+  // Steps 0 and 1 in LDS (step 2's loads may still be in flight) before the
+  // barrier: the last slots of step 0 read the first operands of step 1.
+  __builtin_amdgcn_s_waitcnt(dx_wait(kWdLoads, 0));
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[0][j] = wfrag(0, j, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[0][i] = yfrag(0, i, 0);
+
+  // One step: 32 MFMA slots (MFMA step t = u / 16, feature block
+  // (u % 16) / 4, token block u % 4).  The loads of step kb+3 go out one per
+  // slot in slots 0..7; the operands of MFMA step 1 are read in slots 0..7,
+  // those of the next step's MFMA step 0 in slots 16..23.
+  auto step = [&](auto Pc, int kb) {
+    constexpr int P = decltype(Pc)::value;
+    constexpr int nxt = (P + 1) % 4, ld = (P + 3) % 4;
+    const int kload = min(kb + 3, nsteps - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int t = u / 16, j = (u % 16) / 4, i = u % 4;
+      acc[j][i] = mfma_32x32x16(a[t][j], b[t][i], acc[j][i]);
+      if (u < kWdLoads) load_j(u, ld, kload);
+      if (u < 4) b[1][u] = yfrag(P, u, 1);
+      else if (u < 8) a[1][u - 4] = wfrag(P, u - 4, 1);
+      else if (u >= 16 && u < 20) b[0][u - 16] = yfrag(nxt, u - 16, 0);
+      else if (u >= 20 && u < 24) a[0][u - 20] = wfrag(nxt, u - 20, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Step kb+2's stages (loaded during step kb-1) complete in every wave
+    // before step kb+1, which reads them in its last slots: at most this
+    // step's loads outstanding, then the barrier.
+    __builtin_amdgcn_s_waitcnt(dx_wait(kWdLoads, 0xF));
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int kb = 0; kb < nsteps; kb += kWdUnroll) {
+    step(std::integral_constant<int, 0>(), kb);
+    step(std::integral_constant<int, 1>(), kb + 1);
+    step(std::integral_constant<int, 2>(), kb + 2);
+    step(std::integral_constant<int, 3>(), kb + 3);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
+
+  // Adapter term: (s A)^T U^T over r in steps of 16 into the accumulators.
+  const int64_t kw = k0 + 128 * fg;   // first feature of this wave
+  const int mw = m0 + 128 * tq;       // first token of this wave
+  for (int r0 = 0; r0 < g.r; r0 += 16) {
+    const int rr = r0 + 8 * h;
+    bf16x8_t uop[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mw + 32 * i + c;
+      uint4 uv = make_uint4(0, 0, 0, 0);
+      if (m < g.M && rr < g.r) uv = *reinterpret_cast<const uint4*>(g.U + (int64_t)m * g.r + rr);
+      uop[i] = __builtin_bit_cast(bf16x8_t, uv);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t kf = kw + 32 * j + c;
+      uint32_t av[4] = {0u, 0u, 0u, 0u};
+      if (kf < K && rr < g.r) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
+          const float hi = bf16_to_f32(g.A[(int64_t)(rr + 2 * q + 1) * K + kf]) * g.s;
+          av[q] = pack_bf16x2(lo, hi);
+        }
+      }
+      const bf16x8_t afr = __builtin_bit_cast(bf16x8_t, make_uint4(av[0], av[1], av[2], av[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = mfma_32x32x16(afr, uop[i], acc[j][i]);
+    }
+  }
+
+  // Accumulator [j][i]: lane holds token mw + 32 i + c and features
+  // kw + 32 j + 8 (v / 4) + 4 h + (v % 4).  Four passes of 64 tokens: pass p
+  // takes token blocks 2 (p % 2), +1 of the waves with tq == p / 2; row
+  // 32 i' + c of the pass (i' = i - 2 (p % 2)) lies in stage y[2 i' + c / 16]
+  // at row c % 16, rows of 256 floats whose 16-byte pieces are XOR-swizzled
+  // by row % 16.  Then each thread takes 8 consecutive features of a token
+  // (adds the old dX when accumulating, rounds once) and stores 16 bytes.
+  __syncthreads();   // every wave's loads into the stages have landed
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if (tq == p / 2) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * (p % 2) + ii;
+        float* const st = reinterpret_cast<float*>(
+            (c >> 4) ? (ii ? y3 : y1) : (ii ? y2 : y0)) + (c & 15) * kWdBK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int piece = (32 * fg + 8 * j + 2 * q + h) ^ (c & 15);
+            *reinterpret_cast<float4*>(st + piece * 4) =
+                make_float4(acc[j][i][4 * q + 0], acc[j][i][4 * q + 1], acc[j][i][4 * q + 2],
+                            acc[j][i][4 * q + 3]);
+          }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // rows 8 e + tid / 32 of the pass (stage e / 2), features 8 (tid % 32) .. +7
+      const int row = 8 * e + (tid >> 5), op = tid & 31, rl = row & 15;
+      const float* ld = reinterpret_cast<const float*>(yb[e >> 1]) + rl * kWdBK;
+      const float4 lo = *reinterpret_cast<const float4*>(ld + ((2 * op) ^ rl) * 4);
+      const float4 hi = *reinterpret_cast<const float4*>(ld + ((2 * op + 1) ^ rl) * 4);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const int m = m0 + 128 * (p / 2) + 64 * (p % 2) + row;
+      const int64_t k = k0 + 8 * op;
+      if (m < g.M && k < K) {   // K % 8 == 0: a piece is all in or all out
+        uint4* dst = reinterpret_cast<uint4*>(g.dX + (int64_t)m * K + k);
+        if (g.accumulate) {
+          const uint4 old = *dst;
+          const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] += bf16_to_f32(ow[q] & 0xffffu);
+            v[2 * q + 1] += bf16_to_f32(ow[q] >> 16);
+          }
+        }
+        *dst = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7]));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// The wide tile pays when its tiles alone fill the device.
+static bool dx_wide_fits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + kWdBM - 1) / kWdBM) * ((K + kWdBK - 1) / kWdBK);
+  return tiles >= 256 && N % (kWdStepN * kWdUnroll) == 0 && N * K * 2 < ((int64_t)1 << 31) &&
+         M * N * 2 < ((int64_t)1 << 31);
+}
+
 bool dx_nf4_supported(int64_t N) { return N % (kDxStepN * kDxUnroll) == 0; }
 
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
@@ -543,6 +812,13 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
   g.tiles_k = (int)((w.K + kDxBK - 1) / kDxBK);
   g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2,
                         (double)kDxBK * w.N * (w.bf16 ? 2.0 : 0.52));
+  if (w.bf16 && mask == nullptr && dx_wide_fits(M, w.N, w.K)) {
+    g.tiles_m = (int)((M + kWdBM - 1) / kWdBM);
+    g.tiles_k = (int)((w.K + kWdBK - 1) / kWdBK);
+    g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kWdBM * w.N * 2, (double)kWdBK * w.N * 2);
+    hipLaunchKernelGGL(k_dx_wide, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
   const int nsteps = (int)(w.N / kDxStepN);
   const int splits = (part != nullptr && kz_len > 0) ? (nsteps + kz_len - 1) / kz_len : 1;
   if (splits > 1) {

@@ -247,10 +247,11 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   }
   crun_cur = crun_next;
   srun_cur = srun_next;
-  // Only step 0's loads must have arrived (those of steps 1 and 2 may still
-  // be in flight) before the barrier publishes X(0).
+  // The loads of steps 0 and 1 must have arrived (step 2's may still be in
+  // flight) before the barrier publishes X(0) and X(1): the last slots of
+  // step 0 read the first operands of step 1, which other waves loaded.
   decode_all(wr[0], bf[0], crun_cur & 0xffu, srun_cur);
-  __builtin_amdgcn_s_waitcnt(wait_vm(2 * kLoads, 0));
+  __builtin_amdgcn_s_waitcnt(wait_vm(kLoads, 0));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[0][i] = xfrag(xbuf[0], i, 0);

@@ -189,6 +189,42 @@ def test_dequant_once_dx_equals_in_tile_decode(N, K):
         assert np.array_equal(a, b), f"dropout={mask_p}"
 
 
+def test_wide_dx_tile_matches_narrow_tile_and_oracle():
+    """Once 256 x 256 tiles of dX fill the device, the dX kernel on the bf16
+    weight copy takes four 128 x 128 waves per tile instead of eight 64 x 64
+    ones.  Both run the same MFMAs on every accumulator in the same order
+    (contraction blocks of 16 in increasing order, then the adapter steps), so
+    the first 1024 rows of a 4136-token backward (wide tile: 17 x 17 tiles,
+    ragged in tokens and features) equal a 1024-token backward of those rows
+    (eight-wave tile) bit for bit, also when accumulating into dX; sampled
+    rows, the ragged last token tile among them, against the oracle."""
+    t = pytest.importorskip("torch")
+    M, N, K, small = 4136, 1024, 4160, 1024
+    log(f"[wide dX] M={M} N={N} K={K}")
+    case = wl.linear_case(13, M, N, K, 16, 32.0)
+    qw = q.quantize(dev_f32(case["W"]))
+    X, A, B, dY = (dev_bf16(case[k]) for k in ("X", "A", "B", "dY"))
+    base = dev_bf16(wl.activations(14, 100, M, K))
+    dX_big, _, _ = q.linear_bwd(dY, X, qw, A, B, 32.0)
+    dX_small, _, _ = q.linear_bwd(dY[:small].contiguous(), X[:small].contiguous(), qw, A, B, 32.0)
+    acc_big = base.clone()
+    q.linear_bwd(dY, X, qw, A, B, 32.0, accumulate_into=acc_big)
+    acc_small = base[:small].clone()
+    q.linear_bwd(dY[:small].contiguous(), X[:small].contiguous(), qw, A, B, 32.0,
+                 accumulate_into=acc_small)
+    t.cuda.synchronize()
+    bits = lambda v: v.contiguous().view(t.int16).cpu().numpy()
+    assert np.array_equal(bits(dX_big[:small]), bits(dX_small)), "dX wide vs eight-wave tile"
+    assert np.array_equal(bits(acc_big[:small]), bits(acc_small)), "accumulated dX"
+    rows = np.unique(np.concatenate([sample_rows(M, 24, seed=5), np.arange(M - 40, M)]))
+    Wh = f64(OracleWeight(case["W"]).w_bf16())
+    dYr = f64(case["dY"])[rows]
+    s = oracle.lora_scale(32.0, 16)
+    ref = dYr @ Wh + s * ((dYr @ f64(case["B"])) @ f64(case["A"]))
+    assert_close(host_bf16_f64(dX_big)[rows], ref, "dX sampled rows")
+    assert_close(host_bf16_f64(acc_big)[rows], host_bf16_f64(base)[rows] + ref, "accumulated dX rows")
+
+
 # ---------------------------- full-size configs ------------------------------
 
 def _full_linear(cfg, idx, M=None, rows=48):
