@@ -460,17 +460,23 @@ def run_mlp(args, q, torch, wl, lib, ev):
         q.mlp_bwd(dH, X, lin_args["gate"], lin_args["up"], out["G"], out["U"], out["Tg"],
                   out["Tu"], workspace=ws)
 
-    def timed(fn):
+    # The three are timed in alternation over several rounds (medians), so
+    # that clock ramps and drifts fall on all of them alike.
+    fns = (fused, composed, backward)
+    for fn in fns:
         for _ in range(max(args.warmup, 3)):
             fn()
-        torch.cuda.synchronize()
-        n = max(args.steps // 2, 5)
-        t0 = time.perf_counter()
-        for _ in range(n):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / n
-    ms_f, ms_c, ms_b = timed(fused), timed(composed), timed(backward)
+    torch.cuda.synchronize()
+    n = max(args.steps // 4, 5)
+    runs = [[] for _ in fns]
+    for _ in range(5):
+        for i, fn in enumerate(fns):
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            runs[i].append((time.perf_counter() - t0) * 1e3 / n)
+    ms_f, ms_c, ms_b = (sorted(v)[len(v) // 2] for v in runs)
     r = lins["gate"].r
     flops = 2 * (2.0 * M * I * K + 2.0 * M * r * (I + K))        # two forwards
     bflops = 2 * (2.0 * M * I * K + 4.0 * M * r * (I + K))       # dX, dA, dB of both
