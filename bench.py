@@ -1076,11 +1076,15 @@ def summarize(out: str):
                   ("k_fwd_nf4<false>", 262144): "c5 q/k/v/o and down forward",
                   ("k_fwd_nf4<true>", 1409024): "c5 gate/up (fused)",
                   ("k_dx_nf4<true, false>", 1409024): "c5 down dX",
-                  ("k_dx_nf4<true, false>", 524288): "c5 q/k/v/o and gate/up dX"}
+                  ("k_dx_nf4<true, false>", 524288): "c5 q/k/v/o and gate/up dX",
+                  ("k_dx_wide", 65536): "c3 gate/up dX",
+                  ("k_dx_wide", 176128): "c3 down dX",
+                  ("k_dx_wide", 131072): "c5 q/k/v/o and gate/up dX",
+                  ("k_dx_wide", 352256): "c5 down dX"}
         groups = {}
         for r in _csv(p2b):
             name = r["Kernel_Name"]
-            for sym in ("k_fwd_nf4<false>", "k_fwd_nf4<true>", "k_dx_nf4<true, false>"):
+            for sym in ("k_fwd_nf4<false>", "k_fwd_nf4<true>", "k_dx_nf4<true, false>", "k_dx_wide"):
                 if sym in name:
                     key = (sym, int(r["Grid_Size"]))
                     d = groups.setdefault(key, {}).setdefault(
