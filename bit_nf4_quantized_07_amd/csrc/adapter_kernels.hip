@@ -206,7 +206,7 @@ static hipError_t rank16_dispatch(const uint16_t* S, int64_t M, int64_t C, const
 
 hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W,
                                      int r, uint16_t* out, const NF4Weight& w, uint16_t* wout,
-                                     hipStream_t st) {
+                                     hipStream_t st, Span sp) {
   const int rows = (M + kRankRows - 1) / kRankRows < 256 ? 8 : kRankRows;
   const int rank_blocks = (int)((M + rows - 1) / rows);
   const int64_t nwords = w.N * w.K / 8;
@@ -215,9 +215,9 @@ hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, co
   auto go = [&](auto rt, auto nw) {
     constexpr int RT = decltype(rt)::value, NW = decltype(nw)::value;
     const int64_t dq_blocks = (nwords + NW * kDqWaveWords - 1) / (NW * kDqWaveWords);
-    hipLaunchKernelGGL((k_rank16_and_dequant<RT, NW>), dim3((unsigned)(rank_blocks + dq_blocks)),
-                       dim3(NW * 64), 0, st, S, (int)M, C, W, r, rows, out, rank_blocks, w.packed,
-                       w.codes, w.scales, w.mean, nwords, cb, wout);
+    hipExtLaunchKernelGGL((k_rank16_and_dequant<RT, NW>), dim3((unsigned)(rank_blocks + dq_blocks)),
+                          dim3(NW * 64), 0, st, sp.start, sp.stop, 0, S, (int)M, C, W, r, rows, out,
+                          rank_blocks, w.packed, w.codes, w.scales, w.mean, nwords, cb, wout);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;

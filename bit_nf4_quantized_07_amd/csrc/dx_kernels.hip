@@ -802,7 +802,7 @@ bool dx_nf4_supported(int64_t N) { return N % (kDxStepN * kDxUnroll) == 0; }
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
                          const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
                          hipStream_t st, const uint32_t* mask, float keep_scale, float* part,
-                         int kz_len) {
+                         int kz_len, Span sp) {
   if (!dx_nf4_supported(w.N)) return hipErrorInvalidValue;
   DxArgs g{};
   g.dY = dY; g.M = (int)M; g.w = w; g.U = U; g.A = A; g.r = r; g.s = s; g.dX = dX;
@@ -816,7 +816,8 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
     g.tiles_m = (int)((M + kWdBM - 1) / kWdBM);
     g.tiles_k = (int)((w.K + kWdBK - 1) / kWdBK);
     g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kWdBM * w.N * 2, (double)kWdBK * w.N * 2);
-    hipLaunchKernelGGL(k_dx_wide, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, g);
+    hipExtLaunchKernelGGL(k_dx_wide, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, sp.start, sp.stop, 0,
+                          g);
     return hipGetLastError();
   }
   const int nsteps = (int)(w.N / kDxStepN);
@@ -826,11 +827,12 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
     g.kz_len = kz_len;
   }
   const dim3 grid(g.tiles_m * g.tiles_k * splits);
+  hipEvent_t stop = splits > 1 ? nullptr : sp.stop;
   if (w.bf16)
-    hipLaunchKernelGGL(k_dx_nf4<true>, grid, dim3(64 * kDxWaves), 0, st, g);
+    hipExtLaunchKernelGGL(k_dx_nf4<true>, grid, dim3(64 * kDxWaves), 0, st, sp.start, stop, 0, g);
   else
-    hipLaunchKernelGGL(k_dx_nf4<false>, grid, dim3(64 * kDxWaves), 0, st, g);
-  if (splits > 1) return launch_split_reduce(part, splits, M * w.K, dX, accumulate, st);
+    hipExtLaunchKernelGGL(k_dx_nf4<false>, grid, dim3(64 * kDxWaves), 0, st, sp.start, stop, 0, g);
+  if (splits > 1) return launch_split_reduce(part, splits, M * w.K, dX, accumulate, st, sp.stop);
   return hipGetLastError();
 }
 

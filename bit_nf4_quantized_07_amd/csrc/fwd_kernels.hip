@@ -501,10 +501,10 @@ k_split_reduce(const float* __restrict__ part, int splits, int64_t stride, int64
 }
 
 hipError_t launch_split_reduce(const float* part, int splits, int64_t stride, uint16_t* out,
-                               bool accumulate, hipStream_t st) {
+                               bool accumulate, hipStream_t st, hipEvent_t stop) {
   const int64_t n8 = stride / 8;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part,
-                     splits, stride, n8, out, accumulate ? 1 : 0);
+  hipExtLaunchKernelGGL(k_split_reduce, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                        nullptr, stop, 0, part, splits, stride, n8, out, accumulate ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -538,7 +538,7 @@ hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, c
 
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st,
-                          float* part, int kz_len) {
+                          float* part, int kz_len, Span sp) {
   if (!fwd_nf4_supported(w.K) || w.bf16) return hipErrorInvalidValue;
   FwdArgs g{};
   g.X = X; g.M = (int)M; g.w = w; g.T = T; g.B = B; g.r = r; g.s = s; g.Y = Y;
@@ -552,8 +552,9 @@ hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, cons
     g.part = part;
     g.kz_len = kz_len;
   }
-  hipLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n * splits), dim3(256), 0, st, g);
-  if (splits > 1) return launch_split_reduce(part, splits, M * w.N, Y, false, st);
+  hipExtLaunchKernelGGL(k_fwd_nf4<false>, dim3(g.tiles_m * g.tiles_n * splits), dim3(256), 0, st,
+                        sp.start, splits > 1 ? nullptr : sp.stop, 0, g);
+  if (splits > 1) return launch_split_reduce(part, splits, M * w.N, Y, false, st, sp.stop);
   return hipGetLastError();
 }
 

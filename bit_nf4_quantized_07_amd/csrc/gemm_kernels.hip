@@ -730,13 +730,16 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   g.P = (int)M; g.Q = (int)N;
   g.c1_len = (int)K; g.c1_split = (int)K; g.c2_len = r;
   g.out = Y; g.ldo = N; g.accumulate = 0;
-  timer_begin(tm, TK_FWD_GEMM, st);
   hipError_t e;
   if (fwd_nf4_supported(K)) {
+    // timed by the launches themselves
     e = launch_fwd_nf4(X, M, w, T, B, r, s, Y, st,
                        plan.fwd_kz_len ? reinterpret_cast<float*>(base + plan.off_fpart) : nullptr,
-                       plan.fwd_kz_len);
-  } else if (w.bf16) {
+                       plan.fwd_kz_len, span_of(tm, TK_FWD_GEMM));
+    return e;
+  }
+  timer_begin(tm, TK_FWD_GEMM, st);
+  if (w.bf16) {
     g.b1 = opnd(w.bf16, K, (int)N, N);
     e = launch_gemm<128, 128, kBK, LdBF16K<128, kBK, false>, LdBF16K<128, kBK, false>,
                     LdBF16K<128, kBK, false>, LdBF16K<128, kBK, true>, EPI_BF16>(
@@ -787,9 +790,7 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
   NF4Weight wx = w;
   if (dX && !w.bf16 && plan.dequant_dx) {
     uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
-    timer_begin(tm, TK_DX_DEQUANT, st);
-    QLK_TRY(launch_rank16_and_dequant(dY, M, N, B, r, U, w, wb, st));
-    timer_end(tm, TK_DX_DEQUANT, st);
+    QLK_TRY(launch_rank16_and_dequant(dY, M, N, B, r, U, w, wb, st, span_of(tm, TK_DX_DEQUANT)));
     wx.bf16 = wb;
   } else {
     QLK_TRY(launch_rank16(dY, M, N, B, true, r, U, st));
@@ -805,12 +806,13 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     g.P = (int)M; g.Q = (int)K;
     g.c1_len = (int)N; g.c1_split = (int)N; g.c2_len = r;
     g.out = dX; g.ldo = K; g.accumulate = accumulate_dx ? 1 : 0;
-    timer_begin(tm, TK_DX_GEMM, st);
     hipError_t e;
-    if (dx_nf4_supported(N)) {
+    const bool own = dx_nf4_supported(N);   // timed by its launches; the others around them
+    if (!own) timer_begin(tm, TK_DX_GEMM, st);
+    if (own) {
       e = launch_dx_nf4(dY, M, wx, U, A, r, s, dX, accumulate_dx, st, mask, keep_scale,
                         plan.dx_kz_len ? reinterpret_cast<float*>(base + plan.off_dxpart) : nullptr,
-                        plan.dx_kz_len);
+                        plan.dx_kz_len, span_of(tm, TK_DX_GEMM));
     } else if (mask) {
       // Tile engine with a dropout mask: the masked adapter term is written
       // (or added) first, then dY W_hat is accumulated on top of it.
@@ -843,7 +845,7 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
                       LdBF16T<kDxBN, kBK, true>, EPI_BF16>(
           g, 1, (double)kDxBM * N * 2, (double)kDxBN * N * 0.52, st);
     }
-    timer_end(tm, TK_DX_GEMM, st);
+    if (!own) timer_end(tm, TK_DX_GEMM, st);
     QLK_TRY(e);
   }
   // dA = s U^T X: rows j (U^T, transposed), cols k (X^T, transposed), and

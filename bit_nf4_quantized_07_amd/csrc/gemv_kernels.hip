@@ -720,26 +720,26 @@ static int gemv_split_rows(int64_t N, int64_t K, int r) {
 template <int S, int RT>
 static void launch_gemv_split_rt(const uint16_t* X, int M, const NF4Weight& w, const float* Tpart,
                                  const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T,
-                                 int rows_wg, hipStream_t st) {
+                                 int rows_wg, hipStream_t st, Span sp) {
   const dim3 grid((unsigned)((w.N + rows_wg - 1) / rows_wg));
   if (M == 1)
-    hipLaunchKernelGGL((k_gemv_split<S, true, 1, RT>), grid, dim3(kGsThreads), 0, st, X, M, w,
-                       Tpart, B, r, s, Y, T, rows_wg);
+    hipExtLaunchKernelGGL((k_gemv_split<S, true, 1, RT>), grid, dim3(kGsThreads), 0, st, sp.start,
+                          sp.stop, 0, X, M, w, Tpart, B, r, s, Y, T, rows_wg);
   else if (M <= 8)
-    hipLaunchKernelGGL((k_gemv_split<S, true, 4, RT>), grid, dim3(kGsThreads), 0, st, X, M, w,
-                       Tpart, B, r, s, Y, T, rows_wg);
+    hipExtLaunchKernelGGL((k_gemv_split<S, true, 4, RT>), grid, dim3(kGsThreads), 0, st, sp.start,
+                          sp.stop, 0, X, M, w, Tpart, B, r, s, Y, T, rows_wg);
   else
-    hipLaunchKernelGGL((k_gemv_split<S, false, 4, RT>), grid, dim3(kGsThreads), 0, st, X, M, w,
-                       Tpart, B, r, s, Y, T, rows_wg);
+    hipExtLaunchKernelGGL((k_gemv_split<S, false, 4, RT>), grid, dim3(kGsThreads), 0, st, sp.start,
+                          sp.stop, 0, X, M, w, Tpart, B, r, s, Y, T, rows_wg);
 }
 
 template <int S>
 static void launch_gemv_split_s(const uint16_t* X, int M, const NF4Weight& w, const float* Tpart,
                                 const uint16_t* B, int r, float s, uint16_t* Y, uint16_t* T,
-                                int rows_wg, hipStream_t st) {
-  if (r <= 16) launch_gemv_split_rt<S, 1>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st);
-  else if (r <= 32) launch_gemv_split_rt<S, 2>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st);
-  else launch_gemv_split_rt<S, 4>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st);
+                                int rows_wg, hipStream_t st, Span sp) {
+  if (r <= 16) launch_gemv_split_rt<S, 1>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st, sp);
+  else if (r <= 32) launch_gemv_split_rt<S, 2>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st, sp);
+  else launch_gemv_split_rt<S, 4>(X, M, w, Tpart, B, r, s, Y, T, rows_wg, st, sp);
 }
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* A,
@@ -748,24 +748,26 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, const NF4Weight& w, const u
   if (!Xa) Xa = X;
   hipLaunchKernelGGL(k_lora_down_partial, dim3((r + 31) / 32, kTSplits), dim3(64 * kTWaves), 0, st,
                      Xa, (int)M, w.K, A, r, Tpart);
-  // The timed interval is the weight stream (the layer's dominant kernel);
-  // the T partials before it are a separate, short launch.
-  timer_begin(tm, TK_GEMV, st);
+  // The timed interval is the weight stream (the layer's dominant kernel),
+  // recorded by its launch; the T partials before it are a separate, short
+  // launch.
+  const Span sp = span_of(tm, TK_GEMV);
   const int rows_wg = gemv_split_rows(w.N, w.K, r);
   if (rows_wg > 0) {
     switch (w.K / kBlock) {
-      case 32: launch_gemv_split_s<4>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st); break;
-      case 64: launch_gemv_split_s<8>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st); break;
-      default: launch_gemv_split_s<16>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st); break;
+      case 32: launch_gemv_split_s<4>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st, sp); break;
+      case 64: launch_gemv_split_s<8>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st, sp); break;
+      default: launch_gemv_split_s<16>(X, (int)M, w, Tpart, B, r, s, Y, T, rows_wg, st, sp); break;
     }
   } else {
     const unsigned grid = (unsigned)((w.N + 63) / 64);
     if ((w.K / kBlock) % (4 * kGemvSS) == 0)
-      hipLaunchKernelGGL(k_gemv_dma<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
+      hipExtLaunchKernelGGL(k_gemv_dma<16>, dim3(grid), dim3(256), 0, st, sp.start, sp.stop, 0, X,
+                            (int)M, w, Tpart, B, r, s, Y, T);
     else
-      hipLaunchKernelGGL(k_gemv_nf4<16>, dim3(grid), dim3(256), 0, st, X, (int)M, w, Tpart, B, r, s, Y, T);
+      hipExtLaunchKernelGGL(k_gemv_nf4<16>, dim3(grid), dim3(256), 0, st, sp.start, sp.stop, 0, X,
+                            (int)M, w, Tpart, B, r, s, Y, T);
   }
-  timer_end(tm, TK_GEMV, st);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Internal launcher declarations (host side) of the QLoRA NF4 kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace qlk {
@@ -53,6 +54,22 @@ inline void timer_begin(const Timing* t, int kernel, hipStream_t st) {
 }
 inline void timer_end(const Timing* t, int kernel, hipStream_t st) {
   if (t && t->stop[kernel]) (void)hipEventRecord(t->stop[kernel], st);
+}
+// The events of one timed interval recorded by the launches themselves
+// (hipExtLaunchKernel): the interval's first kernel records `start` as it
+// begins, its last kernel records `stop` as it ends, so the interval holds
+// the kernels' execution and no gap of an event record around a launch.
+struct Span {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+inline Span span_of(const Timing* t, int kernel) {
+  Span s;
+  if (t) {
+    s.start = t->start[kernel];
+    s.stop = t->stop[kernel];
+  }
+  return s;
 }
 
 // Base weight [N, K] as stored: NF4 (packed, codes, scales, mean) or, for
@@ -117,7 +134,7 @@ int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes
 bool fwd_nf4_supported(int64_t K);
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st,
-                          float* part = nullptr, int kz_len = 0);
+                          float* part = nullptr, int kz_len = 0, Span sp = Span());
 // K-steps per split of the forward's contraction for this shape (0: none).
 int fwd_split_len(int64_t M, int64_t K, int64_t N);
 // Fused gate/up projections of a SiLU-gated MLP (M > kGemvMaxM, K / 64 a
@@ -148,13 +165,13 @@ bool dx_nf4_supported(int64_t N);
 hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, const uint16_t* U,
                          const uint16_t* A, int r, float s, uint16_t* dX, bool accumulate,
                          hipStream_t st, const uint32_t* mask = nullptr, float keep_scale = 1.0f,
-                         float* part = nullptr, int kz_len = 0);
+                         float* part = nullptr, int kz_len = 0, Span sp = Span());
 // Steps per split of the dX kernel's contraction for this shape (0: none).
 int dx_split_len(int64_t M, int64_t K, int64_t N);
 // out (bf16, stride values per split) = the fixed-order sum of the fp32
 // split partials, plus out's own values when accumulating; one rounding.
 hipError_t launch_split_reduce(const float* part, int splits, int64_t stride, uint16_t* out,
-                               bool accumulate, hipStream_t st);
+                               bool accumulate, hipStream_t st, hipEvent_t stop = nullptr);
 // dX (+)= bf16(mask * keep_scale * s U A): the adapter term alone, for the
 // tile-engine fallback of the dropout backward.
 hipError_t launch_dx_adapter_masked(const uint16_t* U, const uint16_t* A, int64_t M, int64_t K,
@@ -165,7 +182,7 @@ hipError_t launch_dx_adapter_masked(const uint16_t* U, const uint16_t* A, int64_
 // in one launch.
 hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W,
                                      int r, uint16_t* out, const NF4Weight& w, uint16_t* wout,
-                                     hipStream_t st);
+                                     hipStream_t st, Span sp = Span());
 // Y = X wb^T + s T B^T on a bf16 base weight wb [N, K] (the dX kernel in its
 // forward form), for K a multiple of 256.
 hipError_t launch_fwd_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N, int64_t K,
