@@ -388,18 +388,22 @@ int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int6
 #define QLORA_KERNEL_COUNT      5
 
 /* Caller-owned HIP events (hipEvent_t as void*), indexed by the kernel ids
- * above (slot 0 unused).  A timed call records start[k] and stop[k] on its
- * stream right before and after each launch of kernel k; NULL slots record
- * nothing.  The struct is read during the call only. */
+ * above (slot 0 unused).  In a timed call, start[k] marks the beginning of
+ * kernel k's execution and stop[k] its end (with a split contraction, the end
+ * of the reduction that follows it): the dedicated kernels record the events
+ * as part of their own launch (hipExtLaunchKernel), the generic tile engine
+ * has them recorded on the stream right before and after its launch.  NULL
+ * slots record nothing.  The struct is read during the call only. */
 typedef struct qlora_timing {
   void* start[QLORA_KERNEL_COUNT];
   void* stop[QLORA_KERNEL_COUNT];
 } qlora_timing;
 
-/* qlora_linear_fwd / qlora_linear_bwd with the launches of their dominant
- * kernels bracketed by the caller's events (for benchmarks: an event record
- * between two kernels breaks their back-to-back dispatch).  Same arguments,
- * results and status codes; timing == NULL makes them the plain calls. */
+/* qlora_linear_fwd / qlora_linear_bwd with the execution of their dominant
+ * kernels marked by the caller's events (for benchmarks: events between two
+ * kernels can delay the second one's dispatch, so a step's own time is best
+ * taken from untimed calls).  Same arguments, results and status codes;
+ * timing == NULL makes them the plain calls. */
 int qlora_linear_fwd_timed(const uint16_t* X, int64_t M, int64_t K, int64_t N,
                            const uint8_t* packed, const uint8_t* codes, const float* scales,
                            const float* mean, const uint16_t* A, const uint16_t* B, int r,
