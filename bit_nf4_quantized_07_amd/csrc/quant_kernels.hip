@@ -49,9 +49,19 @@ k_nf4_quantize(const float* __restrict__ W, int64_t nblocks, Codebook4 cb,
     // IEEE division (correctly rounded); an all-zero block has n = 0 (the
     // NF4 zero level, index 7).
     const float n = (m > 0.0f) ? w[i] / m : 0.0f;
-    uint32_t c = 0;
-#pragma unroll
-    for (int t = 0; t < 15; ++t) c += (n > thr[t]) ? 1u : 0u;
+    // The number of thresholds strictly below n, by a binary search over the
+    // ascending thresholds (the same count as comparing with all 15): each
+    // step picks the threshold to compare with by selects, no indexing.
+    uint32_t c = n > thr[7] ? 8u : 0u;
+    {
+      const float t4 = c ? thr[11] : thr[3];
+      c += n > t4 ? 4u : 0u;
+      const float t2 = (c & 8u) ? ((c & 4u) ? thr[13] : thr[9]) : ((c & 4u) ? thr[5] : thr[1]);
+      c += n > t2 ? 2u : 0u;
+      const float ta = (c & 2u) ? ((c & 4u) ? thr[6] : thr[2]) : ((c & 4u) ? thr[4] : thr[0]);
+      const float tb = (c & 2u) ? ((c & 4u) ? thr[14] : thr[10]) : ((c & 4u) ? thr[12] : thr[8]);
+      c += n > ((c & 8u) ? tb : ta) ? 1u : 0u;
+    }
     // element 2j -> high nibble of byte j; bytes little-endian in the word
     const int byte = i >> 1;
     const int shift = byte * 8 + ((i & 1) ? 0 : 4);
