@@ -45,6 +45,26 @@ k_merge(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
   if (tid < 16) q4[tid] = nf4_level(tid);
   const int64_t k0 = (int64_t)blockIdx.x * kMgK, n0 = (int64_t)blockIdx.y * kMgN;
 
+  // The stored weight of this thread's four runs of 8 (step 3) is loaded
+  // first, so that its latency overlaps the adapter product.  In round q
+  // thread t takes row 16 q + t / 16 and columns 8 (t % 16) .. +7 of the
+  // tile (runs outside the weight load nothing and are not stored).
+  const int64_t nkb = K / kBlock;
+  uint32_t pword[4], pcode[4];
+  float pscale[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rn = 16 * q + (tid >> 4), kc = 8 * (tid & 15);
+    const int64_t n = n0 + rn, k = k0 + kc;
+    pword[q] = 0u; pcode[q] = 0u; pscale[q] = 0.0f;
+    if (n < N && k < K) {
+      const int64_t blk = n * nkb + k / kBlock;
+      pword[q] = *reinterpret_cast<const uint32_t*>(packed + (n * K + k) / 2);
+      pcode[q] = codes[blk];
+      pscale[q] = scales[blk / kDQBlock];
+    }
+  }
+
   // Transpose-read addresses for the B-operand (A^T chunk: 16 r x 32 k of
   // this wave): group of 16 lanes = columns 32 w + 16 (grp & 1) .. +15,
   // rows 8 (grp >> 1) + 4 half .. +3.
@@ -105,24 +125,21 @@ k_merge(const uint8_t* __restrict__ packed, const uint8_t* __restrict__ codes,
       prod[(32 * nb + 8 * (v >> 2) + 4 * h + (v & 3)) * kMgLdP + 32 * wave + c] = acc[nb][v];
   __syncthreads();
 
-  // Eight weights per thread and round: in round q thread t takes row
-  // 16 q + t / 16 and columns 8 (t % 16) .. +7 of the tile, so each store
-  // instruction of a wave writes four whole 256-byte row segments.
-  const int64_t nkb = K / kBlock;
+  // Eight weights per thread and round (the runs loaded above), so each
+  // store instruction of a wave writes four whole 256-byte row segments.
   const float mu = mean_p[0];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int rn = 16 * q + (tid >> 4), kc = 8 * (tid & 15);
     const int64_t n = n0 + rn, k = k0 + kc;
     if (n >= N || k >= K) continue;
-    const int64_t blk = n * nkb + k / kBlock;
     float ah;
     {
 #pragma clang fp contract(off)
-      const float p = dq_level((int)codes[blk]) * scales[blk / kDQBlock];
+      const float p = dq_level((int)pcode[q]) * pscale[q];
       ah = p + mu;
     }
-    const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + (n * K + k) / 2);
+    const uint32_t word = pword[q];
     const float* prow = prod + rn * kMgLdP + kc;
     const float4 p0 = *reinterpret_cast<const float4*>(prow);
     const float4 p1 = *reinterpret_cast<const float4*>(prow + 4);
