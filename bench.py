@@ -24,8 +24,10 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                    input (mask drawn every step), and its ratio to the step
   gemv             the small-M forward (W0 28672x8192, M = 1, 4, 16): bytes
                    the GEMV kernel must move over its average duration vs HBM
-  mlp_gate_up      the 11008-wide MLP's gate/up projections (4096 tokens):
-                   the fused forward vs the composition, and the backward
+  mlp_gate_up      the 11008-wide MLP's gate/up projections: the forward call
+                   vs the composition at 4096 tokens (the call composes there)
+                   and at 1024 (the call runs the fused kernel), and the
+                   backward at 4096
   blocks           whole workloads forward + backward: the 11008-wide MLP
                    block and the 65B-shaped decoder layer (TFLOP/s)
   standalone       the load-time kernels (quantize, double quant, dequant), the
@@ -100,6 +102,9 @@ class HipEvents:
             assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
             out.append(e.value)
         return out
+
+    def record(self, e, stream: int):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
 
     def elapsed_ms(self, a, b) -> float:
         f = ctypes.c_float()
@@ -454,13 +459,17 @@ def run_gemv(args, q, torch, wl, lib, ev):
 
 
 def run_mlp(args, q, torch, wl, lib, ev):
-    """The gate/up projections of the 11008-wide MLP (4096 tokens, 11008 x
-    4096 NF4 weights, r = 64): the fused forward (qlora_mlp_fwd: one kernel
-    writes G, U and H) against the composition (two layer forwards and the
-    elementwise gating), and the backward (qlora_mlp_bwd) from dH."""
+    """The gate/up projections of the 11008-wide MLP (11008 x 4096 NF4
+    weights, r = 64): the forward call (qlora_mlp_fwd) against the
+    composition (two layer forwards and the elementwise gating) at 4096
+    tokens, where the call composes the two projections (each on its
+    dequantised copy), and at 1024 tokens, where it runs the fused kernel (one
+    kernel writes G, U and H); and the backward (qlora_mlp_bwd) from dH at
+    4096 tokens."""
     cfg = wl.workloads()["c3_mlp_11008"]
     lins = {l.name: l for l in cfg.linears}
     M, K, I = cfg.M, lins["gate"].K, lins["gate"].N
+    Ms = 1024
     dev_bf16 = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
     lin_args = {}
     for j, name in enumerate(("gate", "up")):
@@ -473,28 +482,34 @@ def run_mlp(args, q, torch, wl, lib, ev):
     X = dev_bf16(wl.activations(0, cfg.cfg_id, M, K))
     dH = dev_bf16(wl.grad_output(0, cfg.cfg_id, M, I))
     ws = q.Workspace("cuda")
-    out = {n: torch.empty(M, I, dtype=torch.bfloat16, device="cuda") for n in ("G", "U", "H")}
-    out["Tg"] = torch.empty(M, lins["gate"].r, dtype=torch.bfloat16, device="cuda")
-    out["Tu"] = torch.empty(M, lins["up"].r, dtype=torch.bfloat16, device="cuda")
-    G2 = torch.empty_like(out["G"])
-    U2 = torch.empty_like(out["U"])
-    H2 = torch.empty_like(out["H"])
 
-    def fused():
-        q.mlp_fwd(X, lin_args["gate"], lin_args["up"], out=out, workspace=ws)
+    def buffers(m):
+        o = {n: torch.empty(m, I, dtype=torch.bfloat16, device="cuda") for n in ("G", "U", "H")}
+        o["Tg"] = torch.empty(m, lins["gate"].r, dtype=torch.bfloat16, device="cuda")
+        o["Tu"] = torch.empty(m, lins["up"].r, dtype=torch.bfloat16, device="cuda")
+        return o
 
-    def composed():
-        q.linear_fwd(X, *lin_args["gate"], out=G2, T_out=out["Tg"], workspace=ws)
-        q.linear_fwd(X, *lin_args["up"], out=U2, T_out=out["Tu"], workspace=ws)
-        q.silu_mul_fwd(G2, U2, out=H2)
+    out, out2 = buffers(M), buffers(M)
+    outs, outs2 = buffers(Ms), buffers(Ms)
+    Xs = X[:Ms]
+
+    def call(x, o):
+        return lambda: q.mlp_fwd(x, lin_args["gate"], lin_args["up"], out=o, workspace=ws)
+
+    def composed(x, o):
+        def fn():
+            q.linear_fwd(x, *lin_args["gate"], out=o["G"], T_out=o["Tg"], workspace=ws)
+            q.linear_fwd(x, *lin_args["up"], out=o["U"], T_out=o["Tu"], workspace=ws)
+            q.silu_mul_fwd(o["G"], o["U"], out=o["H"])
+        return fn
 
     def backward():
         q.mlp_bwd(dH, X, lin_args["gate"], lin_args["up"], out["G"], out["U"], out["Tg"],
                   out["Tu"], workspace=ws)
 
-    # The three are timed in alternation over several rounds (medians), so
-    # that clock ramps and drifts fall on all of them alike.
-    fns = (fused, composed, backward)
+    # All are timed in alternation over several rounds (medians), so that
+    # clock ramps and drifts fall on all of them alike.
+    fns = (call(X, out), composed(X, out2), call(Xs, outs), composed(Xs, outs2), backward)
     for fn in fns:
         for _ in range(max(args.warmup, 3)):
             fn()
@@ -508,14 +523,16 @@ def run_mlp(args, q, torch, wl, lib, ev):
                 fn()
             torch.cuda.synchronize()
             runs[i].append((time.perf_counter() - t0) * 1e3 / n)
-    ms_f, ms_c, ms_b = (sorted(v)[len(v) // 2] for v in runs)
+    ms_call, ms_c, ms_fs, ms_cs, ms_b = (sorted(v)[len(v) // 2] for v in runs)
     r = lins["gate"].r
-    flops = 2 * (2.0 * M * I * K + 2.0 * M * r * (I + K))        # two forwards
-    bflops = 2 * (2.0 * M * I * K + 4.0 * M * r * (I + K))       # dX, dA, dB of both
+    fwd_flops = lambda m: 2 * (2.0 * m * I * K + 2.0 * m * r * (I + K))   # two forwards
+    bflops = 2 * (2.0 * M * I * K + 4.0 * M * r * (I + K))                # dX, dA, dB of both
     return dict(workload=cfg.name, M=M, K=K, I=I, r=r,
-                fwd_fused_ms=round(ms_f, 4), fwd_composed_ms=round(ms_c, 4),
-                fwd_fused_tflops=round(flops / (ms_f * 1e-3) / 1e12, 1),
-                composed_over_fused=round(ms_c / ms_f, 4),
+                fwd_call_ms=round(ms_call, 4), fwd_composed_ms=round(ms_c, 4),
+                fwd_call_tflops=round(fwd_flops(M) / (ms_call * 1e-3) / 1e12, 1),
+                fused_at_1024=dict(M=Ms, fwd_fused_ms=round(ms_fs, 4),
+                                   fwd_composed_ms=round(ms_cs, 4),
+                                   composed_over_fused=round(ms_cs / ms_fs, 4)),
                 bwd_ms=round(ms_b, 4),
                 bwd_tflops=round(bflops / (ms_b * 1e-3) / 1e12, 1))
 
@@ -604,22 +621,28 @@ def run_blocks(args, q, torch, wl, ev):
 def c5_kernels(q, torch, wl, c5, L5, ws, dev_bf16, ev):
     """The decoder layer's GEMM kernels one projection at a time (layer calls
     with the library's HIP events around the forward GEMM, the dX GEMM and the
-    U + dequantisation launch): average time per launch and, for the dominant
-    kernel (the largest time per step), its roofline."""
+    two T/U + dequantisation launches): average time per launch and, for the
+    dominant kernel (the largest time per step), its roofline."""
     M = c5.M
     shapes = {l.name: l for l in c5.linears}
-    per = {}
+    per, prep = {}, {}
     for n in ("q", "k", "v", "o", "gate", "up", "down"):
         lin = shapes[n]
         X = dev_bf16(wl.activations(1, c5.cfg_id, M, lin.K, sub=10))
         dY = dev_bf16(wl.grad_output(1, c5.cfg_id, M, lin.N, sub=10))
         qw, A, B, alpha = L5[n]
         reps = 3
-        slots = (q.KERNEL_FWD_GEMM, q.KERNEL_DX_GEMM, q.KERNEL_DX_DEQUANT)
+        slots = (q.KERNEL_FWD_GEMM, q.KERNEL_DX_GEMM, q.KERNEL_DX_DEQUANT, q.KERNEL_FWD_DEQUANT)
         evs = {k: (ev.create(reps), ev.create(reps)) for k in slots}
+        stream = torch.cuda.current_stream().cuda_stream
         for i in range(reps + 1):
             t = None
             if i > 0:
+                # a dequantisation the call does not launch keeps these marks,
+                # stop before start: a negative interval
+                for k in (q.KERNEL_FWD_DEQUANT, q.KERNEL_DX_DEQUANT):
+                    ev.record(evs[k][1][i - 1], stream)
+                    ev.record(evs[k][0][i - 1], stream)
                 t = timing_for(q, {k: (a[i - 1], b[i - 1]) for k, (a, b) in evs.items()})
             _, T = q.linear_fwd(X, qw, A, B, alpha, workspace=ws, timing=t)
             q.linear_bwd(dY, X, qw, A, B, alpha, T=T, workspace=ws, timing=t)
@@ -631,6 +654,13 @@ def c5_kernels(q, torch, wl, c5, L5, ws, dev_bf16, ev):
             us = float(np.mean([ev.elapsed_ms(a[i], b[i]) for i in range(reps)])) * 1e3
             per[f"{n}.{name}"] = dict(shape=f"{M}x{lin.N}x{lin.K}", avg_us=round(us, 1),
                                       tflops=round(fl / (us * 1e-6) / 1e12, 1))
+        # the one-off dequantisations beside them (T = X A^T, U = dY B in the
+        # same launches), where the call makes them
+        for k, name in ((q.KERNEL_FWD_DEQUANT, "fwd_prep"), (q.KERNEL_DX_DEQUANT, "dx_prep")):
+            a, b = evs[k]
+            us = float(np.mean([ev.elapsed_ms(a[i], b[i]) for i in range(reps)])) * 1e3
+            if us > 0.0:
+                prep[f"{n}.{name}"] = round(us, 1)
         for a, b in evs.values():
             ev.destroy(a + b)
         del X, dY
@@ -638,7 +668,7 @@ def c5_kernels(q, torch, wl, c5, L5, ws, dev_bf16, ev):
     d = per[dom]
     roof = dict(bound="mfma", kernel=dom, achieved=d["tflops"], peak=PEAK_BF16_TFLOPS,
                 unit="TFLOP/s", frac=round(d["tflops"] / PEAK_BF16_TFLOPS, 4), avg_us=d["avg_us"])
-    return dict(per_launch=per, roofline=roof)
+    return dict(per_launch=per, prep_us=prep, roofline=roof)
 
 
 def run_standalone(args, q, torch, lib, ev):
@@ -1101,14 +1131,10 @@ def summarize(out: str):
                "|---|---:|---|---:|---:|---:|"]
         shapes = {("k_fwd_nf4<false>", 65536): "c2 forward",
                   ("k_dx_nf4<true, false>", 131072): "c2 dX",
-                  ("k_fwd_nf4<true>", 704512): "c3 gate/up (fused)",
-                  ("k_fwd_nf4<false>", 131072): "c3 down forward",
-                  ("k_dx_nf4<true, false>", 262144): "c3 gate/up dX",
-                  ("k_dx_nf4<true, false>", 704512): "c3 down dX",
-                  ("k_fwd_nf4<false>", 262144): "c5 q/k/v/o and down forward",
-                  ("k_fwd_nf4<true>", 1409024): "c5 gate/up (fused)",
-                  ("k_dx_nf4<true, false>", 1409024): "c5 down dX",
-                  ("k_dx_nf4<true, false>", 524288): "c5 q/k/v/o and gate/up dX",
+                  ("k_fwd_wide_bf16", 176128): "c3 gate/up forward",
+                  ("k_fwd_wide_bf16", 65536): "c3 down forward",
+                  ("k_fwd_wide_bf16", 131072): "c5 q/k/v/o and down forward",
+                  ("k_fwd_wide_bf16", 352256): "c5 gate/up forward",
                   ("k_dx_wide", 65536): "c3 gate/up dX",
                   ("k_dx_wide", 176128): "c3 down dX",
                   ("k_dx_wide", 131072): "c5 q/k/v/o and gate/up dX",
@@ -1116,7 +1142,8 @@ def summarize(out: str):
         groups = {}
         for r in _csv(p2b):
             name = r["Kernel_Name"]
-            for sym in ("k_fwd_nf4<false>", "k_fwd_nf4<true>", "k_dx_nf4<true, false>", "k_dx_wide"):
+            for sym in ("k_fwd_nf4<false>", "k_fwd_nf4<true>", "k_dx_nf4<true, false>", "k_dx_wide",
+                        "k_fwd_wide_bf16"):
                 if sym in name:
                     key = (sym, int(r["Grid_Size"]))
                     d = groups.setdefault(key, {}).setdefault(

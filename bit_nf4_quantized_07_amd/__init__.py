@@ -31,8 +31,8 @@ _I64 = ctypes.c_int64
 _I = ctypes.c_int
 _F = ctypes.c_float
 
-KERNEL_FWD_GEMM, KERNEL_DX_GEMM, KERNEL_GEMV, KERNEL_DX_DEQUANT = 1, 2, 3, 4
-KERNEL_COUNT = 5
+KERNEL_FWD_GEMM, KERNEL_DX_GEMM, KERNEL_GEMV, KERNEL_DX_DEQUANT, KERNEL_FWD_DEQUANT = 1, 2, 3, 4, 5
+KERNEL_COUNT = 6
 
 
 class TimingC(ctypes.Structure):

@@ -173,7 +173,7 @@ k_rank16(const uint16_t* __restrict__ S, int M, int64_t C, const uint16_t* __res
 // runs both, the first `rank_blocks` workgroups computing U and the rest
 // dequantising (each workgroup does one or the other, so the barriers inside
 // each body see all of its threads).
-template <int RT, int NW>
+template <bool WT, int RT, int NW>
 __global__ void __launch_bounds__(NW * 64)
 k_rank16_and_dequant(const uint16_t* __restrict__ S, int M, int64_t C,
                      const uint16_t* __restrict__ W, int r, int rows, uint16_t* __restrict__ out,
@@ -182,7 +182,7 @@ k_rank16_and_dequant(const uint16_t* __restrict__ S, int M, int64_t C,
                      const float* __restrict__ mean, int64_t nwords, Codebook4 cb,
                      uint16_t* __restrict__ wout) {
   if ((int)blockIdx.x < rank_blocks)
-    rank16_block<true, RT, NW, rank_batch_shared<RT>()>(S, M, C, W, r, rows, out, blockIdx.x);
+    rank16_block<WT, RT, NW, rank_batch_shared<RT>()>(S, M, C, W, r, rows, out, blockIdx.x);
   else
     nf4_dequant_block(packed, codes, scales, mean, nwords, cb, wout,
                       (int64_t)blockIdx.x - rank_blocks);
@@ -205,8 +205,8 @@ static hipError_t rank16_dispatch(const uint16_t* S, int64_t M, int64_t C, const
 }
 
 hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W,
-                                     int r, uint16_t* out, const NF4Weight& w, uint16_t* wout,
-                                     hipStream_t st, Span sp) {
+                                     bool transposed, int r, uint16_t* out, const NF4Weight& w,
+                                     uint16_t* wout, hipStream_t st, Span sp) {
   const int rows = (M + kRankRows - 1) / kRankRows < 256 ? 8 : kRankRows;
   const int rank_blocks = (int)((M + rows - 1) / rows);
   const int64_t nwords = w.N * w.K / 8;
@@ -215,9 +215,15 @@ hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, co
   auto go = [&](auto rt, auto nw) {
     constexpr int RT = decltype(rt)::value, NW = decltype(nw)::value;
     const int64_t dq_blocks = (nwords + NW * kDqWaveWords - 1) / (NW * kDqWaveWords);
-    hipExtLaunchKernelGGL((k_rank16_and_dequant<RT, NW>), dim3((unsigned)(rank_blocks + dq_blocks)),
-                          dim3(NW * 64), 0, st, sp.start, sp.stop, 0, S, (int)M, C, W, r, rows, out,
-                          rank_blocks, w.packed, w.codes, w.scales, w.mean, nwords, cb, wout);
+    const dim3 grid((unsigned)(rank_blocks + dq_blocks));
+    if (transposed)
+      hipExtLaunchKernelGGL((k_rank16_and_dequant<true, RT, NW>), grid, dim3(NW * 64), 0, st,
+                            sp.start, sp.stop, 0, S, (int)M, C, W, r, rows, out, rank_blocks,
+                            w.packed, w.codes, w.scales, w.mean, nwords, cb, wout);
+    else
+      hipExtLaunchKernelGGL((k_rank16_and_dequant<false, RT, NW>), grid, dim3(NW * 64), 0, st,
+                            sp.start, sp.stop, 0, S, (int)M, C, W, r, rows, out, rank_blocks,
+                            w.packed, w.codes, w.scales, w.mean, nwords, cb, wout);
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;

@@ -549,6 +549,13 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
 //    4 (n & 3), so that the transpose reads (4 rows x 4 pieces per bank
 //    cycle) are conflict-free.
 //  * The fp32 tile goes out through the stages in four passes of 64 tokens.
+// NT: the same tile computes the forward Y = X W_hat^T + s T B^T on the
+// dequantised weight ([N, K], rows = outputs): the weight tile is then 256
+// weight rows x 32 contraction values, stored and read exactly like the X
+// (dY) tile.  The contraction runs in the register-decoded forward's order
+// (step 2j holds pieces {0, 1, 4, 5} of 64-block j, step 2j+1 pieces
+// {2, 3, 6, 7}; MFMA step t takes logical pieces t and 2 + t), so that Y is
+// bit-identical to that kernel's.
 constexpr int kWdBM = 256;                    // tokens per tile
 constexpr int kWdBK = 256;                    // features per tile
 constexpr int kWdStepN = 32;                  // contraction per step
@@ -557,7 +564,8 @@ constexpr int kWdWTile = kWdStepN * kWdBK;    // elements per weight stage
 constexpr int kWdUnroll = 4;                  // steps per loop iteration (= stages)
 constexpr int kWdLoads = 8;                   // global loads per wave per step
 
-__global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
+template <bool NT>
+__device__ __forceinline__ void dx_wide_tile(const DxArgs& g) {
   __shared__ __attribute__((aligned(16))) uint16_t y0[kWdYTile];
   __shared__ __attribute__((aligned(16))) uint16_t y1[kWdYTile];
   __shared__ __attribute__((aligned(16))) uint16_t y2[kWdYTile];
@@ -577,11 +585,20 @@ __global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
   tile_coords((int)blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
   const int m0 = tm * kWdBM;
   const int64_t k0 = (int64_t)tk * kWdBK;
-  const int64_t N = g.w.N, K = g.w.K;
+  // N: contraction length; K: output features (dX columns, or Y columns and
+  // weight rows in the forward form).
+  const int64_t N = NT ? g.w.K : g.w.N, K = NT ? g.w.N : g.w.K;
   const int nsteps = (int)(N / kWdStepN);
 
-  // dY loads: load i of wave w fills rows 64 w + 16 i .. +15 (1 KB); lane L
-  // lands at row 64 w + 16 i + L / 4, physical piece L % 4, which holds
+  // Element offset of logical piece l (8 values) within a step, and the
+  // byte offset of step k along a row: natural order for dX, the forward's
+  // permuted order for NT.
+  auto piece_off = [](int l) { return NT ? 8 * ((l & 1) + 4 * (l >> 1)) : 8 * l; };
+  auto step_bytes = [](uint32_t k) {
+    return NT ? (k >> 1) * (kBlock * 2) + (k & 1) * 32 : k * (kWdStepN * 2);
+  };
+  // dY (X) loads: load i of wave w fills rows 64 w + 16 i .. +15 (1 KB); lane
+  // L lands at row 64 w + 16 i + L / 4, physical piece L % 4, which holds
   // logical piece (L % 4) ^ ((row >> 2) & 3).
   const __amdgpu_buffer_rsrc_t rdy = rsrc_whole(g.dY, (uint32_t)((int64_t)g.M * N * 2));
   uint32_t yoff[4];
@@ -589,36 +606,50 @@ __global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
   for (int i = 0; i < 4; ++i) {
     const int row = 64 * wave + 16 * i + (lane >> 2);
     const int piece = (lane & 3) ^ ((row >> 2) & 3);
-    yoff[i] = m0 + row < g.M ? (uint32_t)(((int64_t)(m0 + row) * N + piece * 8) * 2) : kOOB;
+    yoff[i] = m0 + row < g.M ? (uint32_t)(((int64_t)(m0 + row) * N + piece_off(piece)) * 2) : kOOB;
   }
-  // Weight loads: load i of wave w fills rows 8 w + 2 i, +1 of the step
+  // Weight loads.  dX: load i of wave w fills rows 8 w + 2 i, +1 of the step
   // (1 KB); lane L lands at row 8 w + 2 i + L / 32, physical piece L % 32,
-  // which holds logical piece (L % 32) ^ (4 (row & 3)).
+  // which holds logical piece (L % 32) ^ (4 (row & 3)).  NT: as the X loads,
+  // for weight rows k0 + 64 w + 16 i + L / 4.
   const __amdgpu_buffer_rsrc_t rw = rsrc_whole(g.w.bf16, (uint32_t)(N * K * 2));
   uint32_t woff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = 8 * wave + 2 * i + (lane >> 5);
-    const int64_t col = k0 + 8 * ((lane & 31) ^ (4 * (row & 3)));
-    woff[i] = col < K ? (uint32_t)(((int64_t)row * K + col) * 2) : kOOB;
+    if constexpr (NT) {
+      const int row = 64 * wave + 16 * i + (lane >> 2);
+      const int piece = (lane & 3) ^ ((row >> 2) & 3);
+      woff[i] = k0 + row < K ? (uint32_t)(((k0 + row) * N + piece_off(piece)) * 2) : kOOB;
+    } else {
+      const int row = 8 * wave + 2 * i + (lane >> 5);
+      const int64_t col = k0 + 8 * ((lane & 31) ^ (4 * (row & 3)));
+      woff[i] = col < K ? (uint32_t)(((int64_t)row * K + col) * 2) : kOOB;
+    }
   }
   auto load_j = [&](int j, int buf, int kb) {
     const uint32_t kbs = (uint32_t)__builtin_amdgcn_readfirstlane(kb);
     if (j < 4) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rdy, (__attribute__((address_space(3))) void*)(yb[buf] + (64 * wave + 16 * j) * kWdStepN),
-          16, yoff[j], kbs * (kWdStepN * 2), 0, 0);
+          16, yoff[j], step_bytes(kbs), 0, 0);
+    } else if constexpr (NT) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(wb[buf] + (64 * wave + 16 * (j - 4)) * kWdStepN),
+          16, woff[j - 4], step_bytes(kbs), 0, 0);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, (__attribute__((address_space(3))) void*)(wb[buf] + (8 * wave + 2 * (j - 4)) * kWdBK),
           16, woff[j - 4], kbs * kWdStepN * (uint32_t)K * 2u, 0, 0);
     }
   };
-  // dY operand of token block i (32 tokens) of this wave's half, MFMA step
-  // t: row 128 tq + 32 i + c, logical piece 2 t + h.
+  // dY (X) operand of token block i (32 tokens) of this wave's half, MFMA
+  // step t: row 128 tq + 32 i + c, logical piece 2 t + h (NT: t + 2 h).
   int yrd[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) yrd[t] = c * kWdStepN + (((2 * t + h) ^ ((c >> 2) & 3)) * 8);
+  for (int t = 0; t < 2; ++t) {
+    const int l = NT ? t + 2 * h : 2 * t + h;
+    yrd[t] = c * kWdStepN + ((l ^ ((c >> 2) & 3)) * 8);
+  }
   auto yfrag = [&](int buf, int i, int t) -> bf16x8_t {
     return *reinterpret_cast<const bf16x8_t*>(yb[buf] + (128 * tq + 32 * i) * kWdStepN + yrd[t]);
   };
@@ -636,6 +667,8 @@ __global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
       wrd[t][half] = n * kWdBK + (((col >> 3) ^ (4 * (n & 3))) << 3) + (col & 7);
     }
   auto wfrag = [&](int buf, int j, int t) -> bf16x8_t {
+    if constexpr (NT)   // weight row 128 fg + 32 j + c of the tile, like the X operand
+      return *reinterpret_cast<const bf16x8_t*>(wb[buf] + (128 * fg + 32 * j) * kWdStepN + yrd[t]);
     // Feature block j sets bits 2..3 of the logical piece (0 at j = 0), the
     // bits the swizzle XORs: the physical offset is the j = 0 one XOR 32 j.
     const uint16_t* base = wb[buf];
@@ -702,7 +735,8 @@ __global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the loop
 
-  // Adapter term: (s A)^T U^T over r in steps of 16 into the accumulators.
+  // Adapter term: (s A)^T U^T over r in steps of 16 into the accumulators
+  // (NT: (s B) T^T, B [K, r] row-major).
   const int64_t kw = k0 + 128 * fg;   // first feature of this wave
   const int mw = m0 + 128 * tq;       // first token of this wave
   for (int r0 = 0; r0 < g.r; r0 += 16) {
@@ -719,7 +753,13 @@ __global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
     for (int j = 0; j < 4; ++j) {
       const int64_t kf = kw + 32 * j + c;
       uint32_t av[4] = {0u, 0u, 0u, 0u};
-      if (kf < K && rr < g.r) {
+      if (NT && kf < K && rr < g.r) {
+        const uint4 bv = *reinterpret_cast<const uint4*>(g.A + kf * g.r + rr);
+        const uint32_t wv[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          av[q] = pack_bf16x2(bf16_to_f32(wv[q] & 0xffffu) * g.s, bf16_to_f32(wv[q] >> 16) * g.s);
+      } else if (!NT && kf < K && rr < g.r) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float lo = bf16_to_f32(g.A[(int64_t)(rr + 2 * q) * K + kf]) * g.s;
@@ -790,6 +830,11 @@ __global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) {
   }
 }
 
+// The host pass does not keep a kernel template whose body calls these
+// loads from a lambda: one plain kernel per form.
+__global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) { dx_wide_tile<false>(g); }
+__global__ void __launch_bounds__(256) k_fwd_wide_bf16(DxArgs g) { dx_wide_tile<true>(g); }
+
 // The wide tile pays when its tiles alone fill the device.
 static bool dx_wide_fits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + kWdBM - 1) / kWdBM) * ((K + kWdBK - 1) / kWdBK);
@@ -845,6 +890,31 @@ int dx_split_len(int64_t M, int64_t K, int64_t N) {
   if (splits < 2) return 0;
   const int64_t per = (nsteps + splits - 1) / splits;
   return (int)(((per + kDxUnroll - 1) / kDxUnroll) * kDxUnroll);
+}
+
+// The forward form of the wide tile: 256 x 256 tiles of Y that alone fill
+// the device, K in whole 64-blocks and steps of four, 32-bit offsets.
+bool fwd_wide_bf16_fits(int64_t M, int64_t K, int64_t N) {
+  const int64_t tiles = ((M + kWdBM - 1) / kWdBM) * ((N + kWdBK - 1) / kWdBK);
+  return tiles >= 256 && K % (kWdStepN * kWdUnroll) == 0 && N * K * 2 < ((int64_t)1 << 31) &&
+         M * K * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_fwd_wide_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N,
+                                int64_t K, const uint16_t* T, const uint16_t* B, int r, float s,
+                                uint16_t* Y, hipStream_t st, Span sp) {
+  if (!fwd_wide_bf16_fits(M, K, N)) return hipErrorInvalidValue;
+  DxArgs g{};
+  g.dY = X; g.M = (int)M; g.U = T; g.A = B; g.r = r; g.s = s; g.dX = Y;
+  g.w.N = N; g.w.K = K; g.w.bf16 = wb;
+  g.accumulate = 0;
+  g.mask = nullptr; g.keep_scale = 1.0f;
+  g.tiles_m = (int)((M + kWdBM - 1) / kWdBM);
+  g.tiles_k = (int)((N + kWdBK - 1) / kWdBK);
+  g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kWdBM * K * 2, (double)kWdBK * K * 2);
+  hipExtLaunchKernelGGL(k_fwd_wide_bf16, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, sp.start,
+                        sp.stop, 0, g);
+  return hipGetLastError();
 }
 
 // Forward on a bf16 weight wb ([N, K]): Y = X wb^T + s T B^T.

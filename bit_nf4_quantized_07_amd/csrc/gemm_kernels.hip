@@ -561,6 +561,12 @@ FwdPlan plan_fwd(int64_t M, int64_t K, int64_t N, int r, bool nf4) {
     const int64_t splits = (K / kBlock + p.fwd_kz_len - 1) / p.fwd_kz_len;
     off += align256((size_t)splits * M * N * 4);
   }
+  // Once 256 x 256 tiles of Y fill the device, dequantising the weight once
+  // and running the wide bf16 tile beats decoding it in each of the M / 256
+  // token tiles (the two give the same bits).
+  p.dequant_fwd = nf4 && !p.gemv && fwd_wide_bf16_fits(M, K, N);
+  p.off_wbf16 = off;
+  if (p.dequant_fwd) off += align256((size_t)N * K * 2);
   p.bytes = off;
   return p;
 }
@@ -696,7 +702,6 @@ static hipError_t skinny_pair(int rt, const Operand& aa, const Operand& ba, int 
 
 #define QLK_TRY(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) return e_; } while (0)
 
-// T = X A^T (bf16 [M, r]) through split partials + fixed-order reduction.
 // T = X A^T (bf16 [M, r]) in one pass over X.
 static hipError_t compute_T(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int r,
                             uint16_t* T, hipStream_t st) {
@@ -713,6 +718,13 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   float* part = reinterpret_cast<float*>(base + plan.off_part);
   if (!Xa) Xa = X;
   if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st, Xa, tm);
+  if (plan.dequant_fwd && !w.bf16) {
+    // T = X A^T next to the dequantisation, then the wide tile on the copy
+    uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
+    QLK_TRY(launch_rank16_and_dequant(Xa, M, K, A, false, r, T, w, wb, st,
+                                      span_of(tm, TK_FWD_DEQUANT)));
+    return launch_fwd_wide_bf16(X, M, wb, N, K, T, B, r, s, Y, st, span_of(tm, TK_FWD_GEMM));
+  }
   QLK_TRY(compute_T(Xa, M, K, A, r, T, st));
   // A bf16 base: the dX kernel's forward form.
   if (w.bf16 && dx_nf4_supported(K)) {
@@ -752,13 +764,15 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   return e;
 }
 
-bool mlp_fwd_fused(int64_t M, int64_t K) { return M > kGemvMaxM && fwd_nf4_supported(K); }
+bool mlp_fwd_fused(int64_t M, int64_t K, int64_t I) {
+  return M > kGemvMaxM && fwd_nf4_supported(K) && !fwd_wide_bf16_fits(M, K, I);
+}
 
 hipError_t launch_mlp_fwd(const uint16_t* X, int64_t M, const LoraLinear& gate,
                           const LoraLinear& up, uint16_t* G, uint16_t* U, uint16_t* H,
                           uint16_t* Tg, uint16_t* Tu, hipStream_t st) {
   const int64_t K = gate.w.K;
-  if (!mlp_fwd_fused(M, K)) return hipErrorInvalidValue;
+  if (!mlp_fwd_fused(M, K, gate.w.N)) return hipErrorInvalidValue;
   QLK_TRY(compute_T(X, M, K, gate.A, gate.r, Tg, st));
   QLK_TRY(compute_T(X, M, K, up.A, up.r, Tu, st));
   return launch_fwd_gated(X, M, gate.w, Tg, gate.B, gate.r, gate.s, up.w, Tu, up.B, up.r, up.s,
@@ -790,7 +804,7 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
   NF4Weight wx = w;
   if (dX && !w.bf16 && plan.dequant_dx) {
     uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
-    QLK_TRY(launch_rank16_and_dequant(dY, M, N, B, r, U, w, wb, st, span_of(tm, TK_DX_DEQUANT)));
+    QLK_TRY(launch_rank16_and_dequant(dY, M, N, B, true, r, U, w, wb, st, span_of(tm, TK_DX_DEQUANT)));
     wx.bf16 = wb;
   } else {
     QLK_TRY(launch_rank16(dY, M, N, B, true, r, U, st));

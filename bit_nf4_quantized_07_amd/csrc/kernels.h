@@ -44,7 +44,7 @@ hipError_t launch_lora_dropout(const uint16_t* X, int64_t numel, uint32_t thresh
 // individual launches (a null event records nothing; a null Timing times
 // nothing).  Passed down per call: the library keeps no timing state.
 enum TimedKernel { TK_NONE = 0, TK_FWD_GEMM = 1, TK_DX_GEMM = 2, TK_GEMV = 3, TK_DX_DEQUANT = 4,
-                   TK_COUNT = 5 };
+                   TK_FWD_DEQUANT = 5, TK_COUNT = 6 };
 struct Timing {
   hipEvent_t start[TK_COUNT];
   hipEvent_t stop[TK_COUNT];
@@ -99,6 +99,10 @@ struct FwdPlan {
   // fill the device: K-steps per split (0: none) and the fp32 partials.
   int fwd_kz_len;
   size_t off_fpart;
+  // Large M: the forward on a bf16 copy of the weight dequantised once per
+  // call (at off_wbf16, 2 N K bytes), read by every token tile.
+  bool dequant_fwd;
+  size_t off_wbf16;
 };
 struct BwdPlan {
   int u_splits, t_splits, m_splits_a, m_splits_b;
@@ -145,8 +149,10 @@ hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, c
                             const uint16_t* Tu, const uint16_t* Bu, int ru, float su, uint16_t* G,
                             uint16_t* U, uint16_t* H, hipStream_t st);
 // The gated MLP's gate/up forward in one kernel (with the two T launches
-// before it), taken when mlp_fwd_fused(M, K); the caller composes the two
-// layer forwards and the gating otherwise.  Needs no workspace.
+// before it), taken when mlp_fwd_fused(M, K, I); the caller composes the two
+// layer forwards and the gating otherwise (also where each projection runs
+// the wide tile on a dequantised copy, which beats the fused tile).  Needs no
+// workspace.
 struct LoraLinear {
   NF4Weight w;
   const uint16_t* A;
@@ -154,7 +160,7 @@ struct LoraLinear {
   int r;
   float s;
 };
-bool mlp_fwd_fused(int64_t M, int64_t K);
+bool mlp_fwd_fused(int64_t M, int64_t K, int64_t I);
 hipError_t launch_mlp_fwd(const uint16_t* X, int64_t M, const LoraLinear& gate,
                           const LoraLinear& up, uint16_t* G, uint16_t* U, uint16_t* H,
                           uint16_t* Tg, uint16_t* Tu, hipStream_t st);
@@ -177,12 +183,20 @@ hipError_t launch_split_reduce(const float* part, int splits, int64_t stride, ui
 hipError_t launch_dx_adapter_masked(const uint16_t* U, const uint16_t* A, int64_t M, int64_t K,
                                     int r, float s, const uint32_t* mask, float keep_scale,
                                     uint16_t* dX, bool accumulate, hipStream_t st);
-// U = S B (B [C, r] read transposed, as launch_rank16 with transposed = true)
-// and the dequantisation of w into wout (bf16 [N, K], as launch_nf4_dequant),
-// in one launch.
+// out = S W^T (as launch_rank16: W = [r, C] or, transposed, [C, r]) and the
+// dequantisation of w into wout (bf16 [N, K], as launch_nf4_dequant), in one
+// launch: the backward's U = dY B, the wide forward's T = X A^T.
 hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W,
-                                     int r, uint16_t* out, const NF4Weight& w, uint16_t* wout,
-                                     hipStream_t st, Span sp = Span());
+                                     bool transposed, int r, uint16_t* out, const NF4Weight& w,
+                                     uint16_t* wout, hipStream_t st, Span sp = Span());
+// Y = X wb^T + s T B^T on a bf16 weight wb [N, K] with 256 x 256 tiles of
+// four 128 x 128 waves (the wide dX tile in its forward form), in the
+// register-decoded forward's contraction order; for shapes where
+// fwd_wide_bf16_fits.
+bool fwd_wide_bf16_fits(int64_t M, int64_t K, int64_t N);
+hipError_t launch_fwd_wide_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N,
+                                int64_t K, const uint16_t* T, const uint16_t* B, int r, float s,
+                                uint16_t* Y, hipStream_t st, Span sp = Span());
 // Y = X wb^T + s T B^T on a bf16 base weight wb [N, K] (the dX kernel in its
 // forward form), for K a multiple of 256.
 hipError_t launch_fwd_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N, int64_t K,

@@ -574,7 +574,7 @@ int qlora_mlp_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t I,
       (workspace && !aligned16(workspace)))
     return QLORA_ERR_ALIGN;
   const bool whole_rank = padded_rank(gate->r) == gate->r && padded_rank(up->r) == up->r;
-  if (whole_rank && qlk::mlp_fwd_fused(M, K)) {
+  if (whole_rank && qlk::mlp_fwd_fused(M, K, I)) {
     // One kernel for both projections and the gating; T of each projection
     // goes straight to Tg and Tu, so no workspace is needed.
     qlk::LoraLinear L[2];

@@ -161,8 +161,13 @@ int dequant_tables(const uint8_t* packed, const uint8_t* codes, const float* sca
  *   B  bf16 [N, r]     adapter up-projection
  *   Y  bf16 [M, N]     output
  *   T_out bf16 [M, r]  optional: X A^T for the backward (NULL = not stored)
- * W_hat is never written to memory: tiles are dequantised on the fly.
- * Accumulation is fp32; Y is rounded to bf16 once.  When Y has fewer than
+ * Below 256 output tiles of 256 x 256, W_hat is never written to memory:
+ * tiles are dequantised on the fly.  From 256 such tiles (e.g. 4096 tokens
+ * and 4096 outputs), with K % 128 == 0 and 2 N K < 2 GiB, the weight is
+ * dequantised once per call into the workspace (2 N K bytes of it, next to
+ * T = X A^T in the same launch) and a wide bf16 tile reads that copy (the
+ * pages' dequantise-then-matmul, llm-compass 直觉与动机); both paths give
+ * the same bits.  Accumulation is fp32; Y is rounded to bf16 once.  When Y has fewer than
  * 128 tiles of 256 tokens x 128 outputs, the contraction over K is split
  * into ranges whose fp32 partials pass through the workspace and are added
  * in a fixed order: still deterministic, though the bits can differ from a
@@ -318,8 +323,9 @@ typedef struct qlora_lora_linear {
  * qlora_linear_fwd on each projection and H to silu_mul_fwd(G, U).  For
  * M > 16, K % 256 == 0 and both ranks multiples of 8, one kernel computes G
  * and U tile by tile and writes H from the same tile (no second pass over G
- * and U) and needs no workspace; other shapes run the two layer forwards and
- * the elementwise gating.
+ * and U) and needs no workspace; other shapes, and those where
+ * qlora_linear_fwd dequantises the weight once (see there; faster than the
+ * fused tile), run the two layer forwards and the elementwise gating.
  * Requires the shape rules of qlora_linear_fwd for each projection (I plays
  * N), both weights [I, K], and workspace_bytes >= qlora_workspace_bytes(M, K,
  * I, r, 0) for both r (always sufficient). */
@@ -385,7 +391,9 @@ int silu_mul_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* Up, int6
 #define QLORA_KERNEL_GEMV       3  /* small-M dequant GEMV forward                    */
 #define QLORA_KERNEL_DX_DEQUANT 4  /* the backward's one-off dequantisation (M >= 1024),
                                        launched together with U = dY B                 */
-#define QLORA_KERNEL_COUNT      5
+#define QLORA_KERNEL_FWD_DEQUANT 5 /* the forward's one-off dequantisation (wide shapes),
+                                       launched together with T = X A^T                */
+#define QLORA_KERNEL_COUNT      6
 
 /* Caller-owned HIP events (hipEvent_t as void*), indexed by the kernel ids
  * above (slot 0 unused).  In a timed call, start[k] marks the beginning of

@@ -237,6 +237,23 @@ def test_workspace_sizes():
     assert small < 2 * 4096 * 4096
 
 
+def test_forward_workspace_holds_the_weight_copy_for_wide_shapes():
+    """Once 256 x 256 tiles of Y alone fill the device (256 of them), the
+    forward dequantises the weight once into the workspace (bf16, 2 N K
+    bytes) and runs the wide tile on that copy; below that it decodes in the
+    tile and needs no copy."""
+    K, N = 4096, 4096
+    wide = lib.qlora_workspace_bytes(4096, K, N, 16, 0)    # 16 x 16 tiles
+    narrow = lib.qlora_workspace_bytes(4095, K, N, 16, 0)  # 16 x 16 tiles too
+    assert wide >= 2 * N * K and narrow >= 2 * N * K
+    below = lib.qlora_workspace_bytes(3840, K, N, 16, 0)   # 15 x 16 tiles
+    assert below < 2 * N * K
+    # 22016 outputs of 8192 inputs: 4096 tokens fill the device (16 x 86)
+    assert lib.qlora_workspace_bytes(4096, 8192, 22016, 64, 0) >= 2 * 22016 * 8192
+    # a weight copy of 2 GiB or more is not made (32-bit buffer offsets)
+    assert lib.qlora_workspace_bytes(4096, 16384, 65536, 16, 0) < 2 * 65536 * 16384
+
+
 def test_workspace_holds_the_split_partials():
     """With fewer than 128 output tiles (256 tokens x 128 outputs) the forward
     and dX kernels split their contraction so that about 256 workgroups run,

@@ -225,6 +225,35 @@ def test_wide_dx_tile_matches_narrow_tile_and_oracle():
     assert_close(host_bf16_f64(acc_big)[rows], host_bf16_f64(base)[rows] + ref, "accumulated dX rows")
 
 
+def test_wide_forward_matches_narrow_tile_and_oracle():
+    """Once 256 x 256 tiles of Y fill the device, the forward dequantises the
+    weight once and runs the wide bf16 tile on the copy instead of the
+    256-token tile that decodes in registers.  Both run the same MFMAs on the
+    same operands in the same order, so the first 1280 rows of a 4136-token
+    forward (17 x 16 wide tiles, ragged in tokens and outputs) equal a
+    1280-token forward of those rows (256-token tile, no split) bit for bit;
+    sampled rows, the ragged last token tile among them, against the oracle."""
+    t = pytest.importorskip("torch")
+    M, N, K, small = 4136, 3848, 1024, 1280
+    log(f"[wide fwd] M={M} N={N} K={K}")
+    case = wl.linear_case(15, M, N, K, 16, 32.0)
+    qw = q.quantize(dev_f32(case["W"]))
+    X, A, B = (dev_bf16(case[k]) for k in ("X", "A", "B"))
+    Y_big, T_big = q.linear_fwd(X, qw, A, B, 32.0, save_T=True)
+    Y_small, T_small = q.linear_fwd(X[:small].contiguous(), qw, A, B, 32.0, save_T=True)
+    t.cuda.synchronize()
+    bits = lambda v: v.contiguous().view(t.int16).cpu().numpy()
+    assert np.array_equal(bits(T_big[:small]), bits(T_small)), "T next to the dequantisation"
+    assert np.array_equal(bits(Y_big[:small]), bits(Y_small)), "Y wide vs 256-token tile"
+    rows = np.unique(np.concatenate([sample_rows(M, 24, seed=6, tile=256), np.arange(M - 40, M)]))
+    Wh = f64(OracleWeight(case["W"]).w_bf16())
+    Xr = f64(case["X"])[rows]
+    Tr = Xr @ f64(case["A"]).T
+    ref = Xr @ Wh.T + oracle.lora_scale(32.0, 16) * (Tr @ f64(case["B"]).T)
+    assert_close(host_bf16_f64(Y_big)[rows], ref, "Y sampled rows")
+    assert_close(host_bf16_f64(T_big)[rows], Tr, "T sampled rows")
+
+
 # ---------------------------- full-size configs ------------------------------
 
 def _full_linear(cfg, idx, M=None, rows=48):

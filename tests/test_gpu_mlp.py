@@ -199,8 +199,12 @@ def test_fused_gate_up_equals_the_composition(M, K, I, r):
 
 @pytest.mark.timeout(400)
 def test_fused_gate_up_config3_full_shape():
-    """c3's gate/up at full size (4096 tokens, 11008 x 4096, r = 64): bit-exact
-    against the composition, and H on sampled tokens against the oracle."""
+    """c3's full gate/up weights (11008 x 4096, r = 64) at 1024 tokens, where
+    the fused kernel runs (fewer than 256 output tiles of 256 x 256; from
+    there on, as at c3's 4096 tokens, each projection runs the wide tile on a
+    dequantised copy and the call composes them) and the layer forward does
+    not split its contraction: bit-exact against the composition, and H on
+    sampled tokens against the oracle."""
     t = pytest.importorskip("torch")
     w = wl.workloads()["c3_mlp_11008"]
     lins = {l.name: l for l in w.linears}
@@ -211,14 +215,15 @@ def test_fused_gate_up_config3_full_shape():
         A, B = wl.adapters(0, w.cfg_id, j, lin)
         host_w[name] = (W, A, B, lin)
         dev_w[name] = (q.quantize(dev_f32(W)), dev_bf16(A), dev_bf16(B), lin.alpha)
-    X = wl.activations(0, w.cfg_id, w.M, lins["gate"].K)
+    M = 1024
+    X = np.ascontiguousarray(wl.activations(0, w.cfg_id, w.M, lins["gate"].K)[:M])
     Xd = dev_bf16(X)
     G, U, H, Tg, Tu = q.mlp_fwd(Xd, dev_w["gate"], dev_w["up"])
     G0, U0, H0, _, _ = composed_gate_up(Xd, dev_w["gate"], dev_w["up"])
     t.cuda.synchronize()
     for name, a, b in (("G", G, G0), ("U", U, U0), ("H", H, H0)):
         assert np.array_equal(host_bf16_bits(a), host_bf16_bits(b)), name
-    rows = sample_rows(w.M, 16, seed=11, tile=256)
+    rows = sample_rows(M, 16, seed=11, tile=256)
     ref = {}
     for n, (W, A, B, lin) in host_w.items():
         ref[n], _ = oracle.forward(f64(X[rows]), f64(OracleWeight(W).w_bf16()), f64(A), f64(B),
