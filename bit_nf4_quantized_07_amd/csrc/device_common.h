@@ -194,6 +194,7 @@ __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // ------------------------- workgroup -> tile order ---------------------------
 
 constexpr int kXCDs = 8;   // the hardware deals workgroup ids round-robin over 8 XCDs
+constexpr int kCUs = 256;  // compute units: one round of one-workgroup-per-CU tiles
 
 // Tile coordinates of workgroup `bid`: ids are first regrouped so that the
 // workgroups one XCD receives (bid = x, x+8, x+16, ...) get consecutive

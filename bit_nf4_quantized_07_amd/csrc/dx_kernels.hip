@@ -77,6 +77,7 @@ struct DxArgs {
   uint16_t* dX;         // [M, K] bf16
   int accumulate;
   int tiles_m, tiles_k, group_m;
+  int tk_base;          // first feature tile of this launch (a launch can cover the last columns only)
   const uint32_t* mask; // dropout of the adapter input: bit per element of dX, or null
   float keep_scale;     // 1 / (1 - p) for the kept elements
   // Split contraction (fewer tiles than the device has CUs): workgroup
@@ -115,6 +116,7 @@ __global__ void __launch_bounds__(64 * kDxWaves) k_dx_nf4(DxArgs g) {
   const int ntiles = g.tiles_m * g.tiles_k;
   const int zsplit = (int)blockIdx.x / ntiles;
   tile_coords((int)blockIdx.x % ntiles, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
+  tk += g.tk_base;
   const int m0 = tm * kDxBM;
   const int64_t k0 = (int64_t)tk * kDxBK;
   // N: contraction length; K: output features (dX columns, or Y columns and
@@ -583,6 +585,7 @@ __device__ __forceinline__ void dx_wide_tile(const DxArgs& g) {
 
   int tm, tk;
   tile_coords((int)blockIdx.x, g.tiles_m, g.tiles_k, g.group_m, tm, tk);
+  tk += g.tk_base;
   const int m0 = tm * kWdBM;
   const int64_t k0 = (int64_t)tk * kWdBK;
   // N: contraction length; K: output features (dX columns, or Y columns and
@@ -835,6 +838,31 @@ __device__ __forceinline__ void dx_wide_tile(const DxArgs& g) {
 __global__ void __launch_bounds__(256) k_dx_wide(DxArgs g) { dx_wide_tile<false>(g); }
 __global__ void __launch_bounds__(256) k_fwd_wide_bf16(DxArgs g) { dx_wide_tile<true>(g); }
 
+// Wide (256-column) tile columns to run before a narrow (128-column) tile
+// takes the rest of `width` columns: a wide launch whose last round only
+// part-fills the device pays a whole round for it, while narrow tiles, a
+// round of which costs about `narrow` of a wide round, can take those
+// columns in less.  Both tiles give the same bits.  Returns all the wide
+// columns where nothing is gained.
+int wide_columns(int tiles_m, int64_t width, double narrow) {
+  const int tw = (int)((width + 255) / 256);
+  auto rounds = [](int64_t tiles) { return (double)((tiles + kCUs - 1) / kCUs); };
+  double best = rounds((int64_t)tiles_m * tw);
+  int best_cw = tw;
+  for (int cw = tw - 1; cw >= 1 && cw >= tw - 64; --cw) {
+    const int64_t nt = (width - 256 * (int64_t)cw + 127) / 128;
+    const double cost = rounds((int64_t)tiles_m * cw) + narrow * rounds(tiles_m * nt) + 0.02;
+    if (cost < best) {
+      best = cost;
+      best_cw = cw;
+    }
+  }
+  return best_cw;
+}
+// A narrow round over a wide round (same contraction): the eight-wave dX
+// tile and the register-decoded forward tile, measured.
+constexpr double kNarrowRound = 0.6;
+
 // The wide tile pays when its tiles alone fill the device.
 static bool dx_wide_fits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + kWdBM - 1) / kWdBM) * ((K + kWdBK - 1) / kWdBK);
@@ -858,11 +886,23 @@ hipError_t launch_dx_nf4(const uint16_t* dY, int64_t M, const NF4Weight& w, cons
   g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2,
                         (double)kDxBK * w.N * (w.bf16 ? 2.0 : 0.52));
   if (w.bf16 && mask == nullptr && dx_wide_fits(M, w.N, w.K)) {
-    g.tiles_m = (int)((M + kWdBM - 1) / kWdBM);
-    g.tiles_k = (int)((w.K + kWdBK - 1) / kWdBK);
-    g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kWdBM * w.N * 2, (double)kWdBK * w.N * 2);
-    hipExtLaunchKernelGGL(k_dx_wide, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, sp.start, sp.stop, 0,
-                          g);
+    // wide tiles over the first cw feature columns, the eight-wave tile over
+    // the rest (same bits)
+    const int tm_n = (int)((M + kWdBM - 1) / kWdBM);
+    const int tw = (int)((w.K + kWdBK - 1) / kWdBK);
+    const int cw = wide_columns(tm_n, w.K, kNarrowRound);
+    DxArgs gw = g;
+    gw.tiles_m = tm_n;
+    gw.tiles_k = cw;
+    gw.group_m = group_for(gw.tiles_m, gw.tiles_k, (double)kWdBM * w.N * 2, (double)kWdBK * w.N * 2);
+    hipExtLaunchKernelGGL(k_dx_wide, dim3(gw.tiles_m * gw.tiles_k), dim3(256), 0, st, sp.start,
+                          cw == tw ? sp.stop : nullptr, 0, gw);
+    if (cw == tw) return hipGetLastError();
+    g.tk_base = cw * (kWdBK / kDxBK);
+    g.tiles_k = (int)((w.K - (int64_t)cw * kWdBK + kDxBK - 1) / kDxBK);
+    g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kDxBM * w.N * 2, (double)kDxBK * w.N * 2);
+    hipExtLaunchKernelGGL(k_dx_nf4<true>, dim3(g.tiles_m * g.tiles_k), dim3(64 * kDxWaves), 0, st,
+                          nullptr, sp.stop, 0, g);
     return hipGetLastError();
   }
   const int nsteps = (int)(w.N / kDxStepN);
@@ -900,17 +940,22 @@ bool fwd_wide_bf16_fits(int64_t M, int64_t K, int64_t N) {
          M * K * 2 < ((int64_t)1 << 31);
 }
 
+int fwd_wide_columns(int64_t M, int64_t N) {
+  return wide_columns((int)((M + kWdBM - 1) / kWdBM), N, kNarrowRound);
+}
+
 hipError_t launch_fwd_wide_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N,
                                 int64_t K, const uint16_t* T, const uint16_t* B, int r, float s,
-                                uint16_t* Y, hipStream_t st, Span sp) {
-  if (!fwd_wide_bf16_fits(M, K, N)) return hipErrorInvalidValue;
+                                uint16_t* Y, int cols, hipStream_t st, Span sp) {
+  if (!fwd_wide_bf16_fits(M, K, N) || cols < 1 || (int64_t)cols * kWdBK > N + kWdBK - 1)
+    return hipErrorInvalidValue;
   DxArgs g{};
   g.dY = X; g.M = (int)M; g.U = T; g.A = B; g.r = r; g.s = s; g.dX = Y;
   g.w.N = N; g.w.K = K; g.w.bf16 = wb;
   g.accumulate = 0;
   g.mask = nullptr; g.keep_scale = 1.0f;
   g.tiles_m = (int)((M + kWdBM - 1) / kWdBM);
-  g.tiles_k = (int)((N + kWdBK - 1) / kWdBK);
+  g.tiles_k = cols;
   g.group_m = group_for(g.tiles_m, g.tiles_k, (double)kWdBM * K * 2, (double)kWdBK * K * 2);
   hipExtLaunchKernelGGL(k_fwd_wide_bf16, dim3(g.tiles_m * g.tiles_k), dim3(256), 0, st, sp.start,
                         sp.stop, 0, g);

@@ -74,6 +74,7 @@ struct FwdArgs {
   float s;
   uint16_t* Y;
   int tiles_m, tiles_n, group_m;
+  int tn_base;          // first column tile of this launch (a launch can cover the last columns only)
   // gated variant: w/T/B/r/s/Y are the gate projection's (Y = G), these the
   // up projection's (Y2 = U); H = silu(G) U.
   NF4Weight w2;
@@ -125,6 +126,7 @@ __global__ void __launch_bounds__(256) k_fwd_nf4(FwdArgs g) {
   const int ntiles = g.tiles_m * g.tiles_n;
   const int zsplit = (int)blockIdx.x / ntiles;
   tile_coords((int)blockIdx.x % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  tn += g.tn_base;
   const int m0 = tm * kFwdBM;
   // This wave's weight (the up weight for waves 2-3 of the gated variant).
   const bool upw = GATED && wave >= 2;
@@ -538,12 +540,14 @@ hipError_t launch_fwd_gated(const uint16_t* X, int64_t M, const NF4Weight& wg, c
 
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st,
-                          float* part, int kz_len, Span sp) {
+                          float* part, int kz_len, Span sp, int tn_base) {
   if (!fwd_nf4_supported(w.K) || w.bf16) return hipErrorInvalidValue;
   FwdArgs g{};
   g.X = X; g.M = (int)M; g.w = w; g.T = T; g.B = B; g.r = r; g.s = s; g.Y = Y;
   g.tiles_m = (int)((M + kFwdBM - 1) / kFwdBM);
-  g.tiles_n = (int)((w.N + kFwdBN - 1) / kFwdBN);
+  g.tiles_n = (int)((w.N + kFwdBN - 1) / kFwdBN) - tn_base;
+  g.tn_base = tn_base;
+  if (tn_base < 0 || g.tiles_n < 1 || (tn_base > 0 && part != nullptr)) return hipErrorInvalidValue;
   g.group_m = group_for(g.tiles_m, g.tiles_n, (double)kFwdBM * w.K * 2,
                         (double)kFwdBN * w.K * 0.52);
   const int64_t nk = w.K / kBlock;

@@ -719,11 +719,21 @@ hipError_t launch_qlora_fwd(const uint16_t* X, int64_t M, const NF4Weight& w, co
   if (!Xa) Xa = X;
   if (plan.gemv && !w.bf16) return launch_gemv(X, M, w, A, B, r, s, Y, T, part, st, Xa, tm);
   if (plan.dequant_fwd && !w.bf16) {
-    // T = X A^T next to the dequantisation, then the wide tile on the copy
+    // T = X A^T next to the dequantisation of the weight rows the wide tile
+    // reads, then the wide tile on the copy over the first cw column tiles,
+    // and where the last wide round would only part-fill the device, the
+    // register-decoded tile over the remaining columns (same bits).
     uint16_t* wb = reinterpret_cast<uint16_t*>(base + plan.off_wbf16);
-    QLK_TRY(launch_rank16_and_dequant(Xa, M, K, A, false, r, T, w, wb, st,
+    const int tw = (int)ceil_div(N, 256);
+    const int cw = fwd_nf4_supported(K) ? fwd_wide_columns(M, N) : tw;
+    NF4Weight wrows = w;
+    wrows.N = (int64_t)cw * 256 < N ? (int64_t)cw * 256 : N;
+    QLK_TRY(launch_rank16_and_dequant(Xa, M, K, A, false, r, T, wrows, wb, st,
                                       span_of(tm, TK_FWD_DEQUANT)));
-    return launch_fwd_wide_bf16(X, M, wb, N, K, T, B, r, s, Y, st, span_of(tm, TK_FWD_GEMM));
+    const Span sp = span_of(tm, TK_FWD_GEMM);
+    if (cw == tw) return launch_fwd_wide_bf16(X, M, wb, N, K, T, B, r, s, Y, cw, st, sp);
+    QLK_TRY(launch_fwd_wide_bf16(X, M, wb, N, K, T, B, r, s, Y, cw, st, Span{sp.start, nullptr}));
+    return launch_fwd_nf4(X, M, w, T, B, r, s, Y, st, nullptr, 0, Span{nullptr, sp.stop}, 2 * cw);
   }
   QLK_TRY(compute_T(Xa, M, K, A, r, T, st));
   // A bf16 base: the dX kernel's forward form.

@@ -136,9 +136,12 @@ int group_for(int tiles_p, int tiles_q, double a_tile_bytes, double b_tile_bytes
 // Y = X W_hat^T + s T B^T for M > kGemvMaxM (T precomputed, bf16 [M, r]);
 // supported when K / 64 is a multiple of 4 (else the tile engine runs).
 bool fwd_nf4_supported(int64_t K);
+// tn_base: the launch covers column tiles (of 128 weight rows) tn_base ..
+// of Y only (no split then).
 hipError_t launch_fwd_nf4(const uint16_t* X, int64_t M, const NF4Weight& w, const uint16_t* T,
                           const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st,
-                          float* part = nullptr, int kz_len = 0, Span sp = Span());
+                          float* part = nullptr, int kz_len = 0, Span sp = Span(),
+                          int tn_base = 0);
 // K-steps per split of the forward's contraction for this shape (0: none).
 int fwd_split_len(int64_t M, int64_t K, int64_t N);
 // Fused gate/up projections of a SiLU-gated MLP (M > kGemvMaxM, K / 64 a
@@ -193,10 +196,15 @@ hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, co
 // four 128 x 128 waves (the wide dX tile in its forward form), in the
 // register-decoded forward's contraction order; for shapes where
 // fwd_wide_bf16_fits.
+// It covers the first `cols` 256-wide column tiles of Y (its weight rows
+// below 256 cols are read); fwd_wide_columns(M, N) is the count after which
+// the register-decoded tile (launch_fwd_nf4 with a first column tile) takes
+// the rest in fewer rounds of the device.
 bool fwd_wide_bf16_fits(int64_t M, int64_t K, int64_t N);
+int fwd_wide_columns(int64_t M, int64_t N);
 hipError_t launch_fwd_wide_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N,
                                 int64_t K, const uint16_t* T, const uint16_t* B, int r, float s,
-                                uint16_t* Y, hipStream_t st, Span sp = Span());
+                                uint16_t* Y, int cols, hipStream_t st, Span sp = Span());
 // Y = X wb^T + s T B^T on a bf16 base weight wb [N, K] (the dX kernel in its
 // forward form), for K a multiple of 256.
 hipError_t launch_fwd_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N, int64_t K,
