@@ -1134,11 +1134,13 @@ def summarize(out: str):
                   ("k_fwd_wide_bf16", 176128): "c3 gate/up forward",
                   ("k_fwd_wide_bf16", 65536): "c3 down forward",
                   ("k_fwd_wide_bf16", 131072): "c5 q/k/v/o and down forward",
-                  ("k_fwd_wide_bf16", 352256): "c5 gate/up forward",
+                  ("k_fwd_wide_bf16", 327680): "c5 gate/up forward, first 80 column tiles",
+                  ("k_fwd_nf4<false>", 49152): "c5 gate/up forward, last 1536 columns",
                   ("k_dx_wide", 65536): "c3 gate/up dX",
                   ("k_dx_wide", 176128): "c3 down dX",
                   ("k_dx_wide", 131072): "c5 q/k/v/o and gate/up dX",
-                  ("k_dx_wide", 352256): "c5 down dX"}
+                  ("k_dx_wide", 327680): "c5 down dX, first 80 column tiles",
+                  ("k_dx_nf4<true, false>", 98304): "c5 down dX, last 1536 columns"}
         groups = {}
         for r in _csv(p2b):
             name = r["Kernel_Name"]
