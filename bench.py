@@ -1120,7 +1120,12 @@ def summarize(out: str):
                 div(_med(bg, "SQ_INSTS_LDS"), mf), div(_med(bg, "SQ_ACTIVE_INST_VALU"), wc),
                 div(_med(ag, "SQ_WAIT_INST_ANY"), wc), div(_med(ag, "SQ_WAIT_INST_LDS"), wc),
                 div(_med(ag, "SQ_LDS_BANK_CONFLICT"), _med(ag, "SQ_ACTIVE_INST_LDS"))))
-    md += ["", "VALU instructions exclude the MFMAs (SQ_INSTS_VALU counts both)."]
+    md += ["", "VALU instructions exclude the MFMAs (SQ_INSTS_VALU counts both). The clock and "
+           "MFMA-busy columns hold for the GEMMs (70 us and more per dispatch); for the short "
+           "launches (the small-M stream, the dequantisation, under 30 us) GRBM_GUI_ACTIVE also "
+           "counts cycles of the counter window around the dispatch, so their clock reads above "
+           "the 2.4 GHz the chip can run and their MFMA busy reads low; their per-MFMA "
+           "instruction ratios and wave-cycle shares are unaffected."]
     # MFMA busy by launch shape over the run with the whole workloads
     p2b = os.path.join(out, "p2b", "p2b_counter_collection.csv")
     if os.path.exists(p2b):
