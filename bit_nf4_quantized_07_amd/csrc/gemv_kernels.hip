@@ -517,6 +517,7 @@ k_gemv_split(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __
   __shared__ __attribute__((aligned(16))) uint32_t tbl[kGsTable];           // 64 KB
   __shared__ __attribute__((aligned(16))) float part[kGsMaxRG * PARTW];     // 16 or 64 KB
   __shared__ __attribute__((aligned(16))) uint16_t tl[kGemvMaxM * 16 * RT];   // T, bf16 [M][r]
+  __shared__ float q8[256];                                                  // the 8-bit levels
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -580,6 +581,7 @@ k_gemv_split(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __
   for (int c = 0; c < BCH; ++c)
     bpre[c] = bload128s(rb, bvalid && 32 * c + 8 * g < r ? (uint32_t)((bn * r + 32 * c + 8 * g) * 2) : kOOB, 0);
 
+  if (tid < 256) q8[tid] = dq_level(tid);
   // --- the byte -> (level of the high nibble, level of the low nibble)
   // table, one column per lane.  Thread t fills entries e = 8 k + t / 64 of
   // its lane's column.
@@ -626,7 +628,7 @@ k_gemv_split(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __
     tl[i] = tb;
     if (blockIdx.x == 0) T_out[i] = tb;
   }
-  __syncthreads();   // the level table (each wave fills entries every wave reads) and T
+  __syncthreads();   // the level tables (each wave fills entries every wave reads) and T
 
   // --- the weight stream -----------------------------------------------------
   for (int jr = 0; jr < rgs; ++jr) {
@@ -644,7 +646,7 @@ k_gemv_split(const uint16_t* __restrict__ X, int M, NF4Weight w, const float* __
       const int b = PAIR ? 2 * u : u;
       const uint32_t sh = 8u * (uint32_t)(b & 3) + (PAIR ? 8u * (uint32_t)(g >> 1) : 0u);
       const int code = (int)((cwl[b >> 2] >> sh) & 0xffu);
-      const float ah = absmax_decode(code, scl, mean);
+      const float ah = absmax_decode_tab(code, scl, mean, q8);
       const uint4 pw = wu[u % D];
       if (u + D < NU) load_unit(jr, u + D);
       else if (jr + 1 < rgs) load_unit(jr + 1, u + D - NU);
