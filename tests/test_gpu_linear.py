@@ -254,6 +254,35 @@ def test_wide_forward_matches_narrow_tile_and_oracle():
     assert_close(host_bf16_f64(T_big)[rows], Tr, "T sampled rows")
 
 
+def test_wide_forward_alone_when_k_is_an_odd_multiple_of_128():
+    """K = 384 (a multiple of 128 but not of 256): the register-decoded tile
+    does not take it, so at 4096 tokens x 4096 outputs (256 tiles of
+    256 x 256) the wide tile on the dequantised copy covers every column
+    alone.  Sampled rows of Y and T against the oracle, with r = 24 (the
+    adapter term's steps of 16 end in a partial one), and the backward's dX
+    on the same rows."""
+    t = pytest.importorskip("torch")
+    M, N, K, r, alpha = 4096, 4096, 384, 24, 48.0
+    log(f"[wide fwd, K % 256 == 128] M={M} N={N} K={K} r={r}")
+    case = wl.linear_case(17, M, N, K, r, alpha)
+    qw = q.quantize(dev_f32(case["W"]))
+    X, A, B, dY = (dev_bf16(case[k]) for k in ("X", "A", "B", "dY"))
+    Y, T = q.linear_fwd(X, qw, A, B, alpha, save_T=True)
+    dX, dA, dB = q.linear_bwd(dY, X, qw, A, B, alpha, T=T)
+    t.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(M, 24, seed=8, tile=256), np.arange(M - 8, M)]))
+    Wh = f64(OracleWeight(case["W"]).w_bf16())
+    s = oracle.lora_scale(alpha, r)
+    Xr = f64(case["X"])[rows]
+    Tr = Xr @ f64(case["A"]).T
+    ref = Xr @ Wh.T + s * (Tr @ f64(case["B"]).T)
+    assert_close(host_bf16_f64(Y)[rows], ref, "Y sampled rows")
+    assert_close(host_bf16_f64(T)[rows], Tr, "T sampled rows")
+    dYr = f64(case["dY"])[rows]
+    refdx = dYr @ Wh + s * ((dYr @ f64(case["B"])) @ f64(case["A"]))
+    assert_close(host_bf16_f64(dX)[rows], refdx, "dX sampled rows")
+
+
 # ---------------------------- full-size configs ------------------------------
 
 def _full_linear(cfg, idx, M=None, rows=48):
