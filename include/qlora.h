@@ -166,8 +166,10 @@ int dequant_tables(const uint8_t* packed, const uint8_t* codes, const float* sca
  * and 4096 outputs), with K % 128 == 0 and 2 N K < 2 GiB, the weight is
  * dequantised once per call into the workspace (2 N K bytes of it, next to
  * T = X A^T in the same launch) and a wide bf16 tile reads that copy (the
- * pages' dequantise-then-matmul, llm-compass 直觉与动机); both paths give
- * the same bits.  Accumulation is fp32; Y is rounded to bf16 once.  When Y has fewer than
+ * pages' dequantise-then-matmul, llm-compass 直觉与动机); where the wide
+ * tiles' last round would only part-fill the device, the on-the-fly tile
+ * takes the last columns.  With K % 256 == 0 the two tiles give the same
+ * bits.  Accumulation is fp32; Y is rounded to bf16 once.  When Y has fewer than
  * 128 tiles of 256 tokens x 128 outputs, the contraction over K is split
  * into ranges whose fp32 partials pass through the workspace and are added
  * in a fixed order: still deterministic, though the bits can differ from a
