@@ -238,6 +238,225 @@ hipError_t launch_rank16_and_dequant(const uint16_t* S, int64_t M, int64_t C, co
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// The adapters' gradients for more than 16 tokens, both in one launch that
+// reads each operand once and writes the results directly:
+//
+//   dA = s U^T X   ([r, K]),   dB = s dY^T T   ([N, r])
+//                  (llm-compass "QLoRA", 方法与公式, the derivatives of the
+//                   equation with respect to A and B; U = dY B)
+//
+// Both contract over the M tokens: O[c][j] = sum_m P[m][c] Q[m][j], with
+// (P, Q) = (X, U) for dA (O = dA^T) and (dY, T) for dB (O = dB).  A
+// workgroup owns 32 columns c of P and all r outputs and contracts over every
+// token itself, so no partial sums go through memory and no second launch
+// adds them:
+//  * its four waves take every fourth 32-token chunk; lane L loads rows
+//    L / 4 and 16 + L / 4 of a chunk's 32 x 32 piece of P (16 bytes each, the
+//    four lanes of a row its 64 contiguous bytes) and 16 bytes of the chunk's
+//    32 x r piece of Q per 16 columns of r;
+//  * the pieces go through a per-wave LDS slab (row-major) and come back as
+//    MFMA operands with the transposing LDS read: lane (i, g) of
+//    v_mfma_f32_16x16x32_bf16 gets column i of rows 8 g .. 8 g + 7 of the
+//    chunk, the same token order for both operands;
+//  * a wave issues the loads of KB chunks together, and those of its next KB
+//    chunks before it multiplies the first ones (two register sets), so two
+//    batches are in flight per wave;
+//  * the four waves' sums are added through LDS in the order 0, 1, 2, 3, then
+//    scaled by s (one fp32 rounding each), so the result is reproducible;
+//  * slice numbers are dealt so that the workgroups one XCD receives take
+//    consecutive slices: the two 64-byte halves of a 128-byte line of P are
+//    read by workgroups on the same XCD.
+// Tokens past M and columns past the operand are loaded as zeros (r and the
+// column counts are multiples of 8, so a 16-byte piece lies wholly inside or
+// wholly outside).
+constexpr int kGradCols = 32;     // columns of P per workgroup
+constexpr int kGradChunk = 32;    // tokens per MFMA step
+constexpr int kGradWaves = 4;
+
+struct GradJob {
+  const uint16_t* P;   // [M, ld] bf16
+  int64_t ld;          // row length of P (elements)
+  int64_t cols;        // columns of P contracted (a multiple of 8)
+  const uint16_t* Q;   // [M, r] bf16
+  float* out;          // trans: [r, cols] (dA); else [cols, r] (dB)
+  int trans;
+  int slices;          // workgroups of this job: ceil(cols / 32)
+};
+
+template <int RT, int KB>
+__global__ void __launch_bounds__(kGradWaves * 64)
+k_adapter_grads(GradJob ja, GradJob jb, int M, int r, float s) {
+  constexpr int PE = kGradChunk * kGradCols;     // elements of a chunk's P piece
+  constexpr int QW = 16 * RT;                    // row length of the Q piece
+  constexpr int CE = PE + kGradChunk * QW;       // elements of a chunk in the slab
+  __shared__ __attribute__((aligned(16))) uint16_t slab[kGradWaves][KB * CE];
+  __shared__ __attribute__((aligned(16))) float red[kGradWaves - 1][2 * RT][64][4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const bool first = (int)blockIdx.x < ja.slices;
+  const uint16_t* const P = first ? ja.P : jb.P;
+  const uint16_t* const Q = first ? ja.Q : jb.Q;
+  float* const out = first ? ja.out : jb.out;
+  const int64_t ld = first ? ja.ld : jb.ld, cols = first ? ja.cols : jb.cols;
+  const int trans = first ? ja.trans : jb.trans;
+  const int nsl = first ? ja.slices : jb.slices;
+  const int lb = first ? (int)blockIdx.x : (int)blockIdx.x - ja.slices;
+  const int full = (nsl / kXCDs) * kXCDs;
+  const int sl = lb < full ? (lb % kXCDs) * (full / kXCDs) + lb / kXCDs : lb;
+  const int64_t c0 = (int64_t)sl * kGradCols;
+
+  const __amdgpu_buffer_rsrc_t rp = rsrc_whole(P, (uint32_t)((int64_t)M * ld * 2));
+  const __amdgpu_buffer_rsrc_t rq = rsrc_whole(Q, (uint32_t)((int64_t)M * r * 2));
+  // this lane's pieces within a chunk
+  const int prow = lane >> 2;                    // + 16 h
+  const int64_t pcol = c0 + 8 * (lane & 3);
+  const bool pcol_ok = pcol < cols;
+  uint16_t* const my = slab[wave];
+
+  const int nchunks = (M + kGradChunk - 1) / kGradChunk;
+  const int per_wave = (nchunks + kGradWaves - 1) / kGradWaves;
+  const int nb = (per_wave + KB - 1) / KB;      // batches, the same for every wave
+
+  f32x4_t acc[2][RT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[h][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto load = [&](int b, uint4 (&pv)[KB][2], uint4 (&qv)[KB][RT]) {
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      const int m0 = ((b * KB + q) * kGradWaves + wave) * kGradChunk;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = m0 + 16 * h + prow;
+        const bool ok = m < M && pcol_ok;
+        pv[q][h] = bload128s(rp, ok ? (uint32_t)(((int64_t)m * ld + pcol) * 2) : kOOB, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int p = 64 * t + lane;             // piece p: row p / (2 RT), columns 8 (p % (2 RT))
+        const int m = m0 + p / (2 * RT);
+        const int j = 8 * (p % (2 * RT));
+        const bool ok = m < M && j < r;
+        qv[q][t] = bload128s(rq, ok ? (uint32_t)(((int64_t)m * r + j) * 2) : kOOB, 0);
+      }
+    }
+  };
+  auto consume = [&](const uint4 (&pv)[KB][2], const uint4 (&qv)[KB][RT]) {
+    // A wave's LDS operations run in issue order: these stores land after the
+    // previous batch's reads and before this batch's reads.
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      uint16_t* const c = my + q * CE;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<uint4*>(c + (16 * h + prow) * kGradCols + 8 * (lane & 3)) = pv[q][h];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int p = 64 * t + lane;
+        *reinterpret_cast<uint4*>(c + PE + (p / (2 * RT)) * QW + 8 * (p % (2 * RT))) = qv[q][t];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    typedef short v8s_t __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      const uint16_t* const c = my + q * CE;
+      // source lane 4 s + u of a 16-lane group points at row 8 g + 4 e + s,
+      // column 4 u of a 16-column band: lane i receives column i of the
+      // band's four rows
+      const int rr = 8 * g + (i >> 2), cc = 4 * (i & 3);
+      bf16x8_t aop[2], bop[RT];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4s_t lo = lds_read_tr16(c + rr * kGradCols + 16 * h + cc);
+        const v4s_t hi = lds_read_tr16(c + (rr + 4) * kGradCols + 16 * h + cc);
+        const v8s_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        aop[h] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const v4s_t lo = lds_read_tr16(c + PE + rr * QW + 16 * t + cc);
+        const v4s_t hi = lds_read_tr16(c + PE + (rr + 4) * QW + 16 * t + cc);
+        const v8s_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        bop[t] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[h][t] = mfma_16x16x32(aop[h], bop[t], acc[h][t]);
+    }
+  };
+
+  uint4 pa[KB][2], qa[KB][RT], pb[KB][2], qb[KB][RT];
+  load(0, pa, qa);
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) load(b + 1, pb, qb);
+    consume(pa, qa);
+    if (b + 2 < nb) load(b + 2, pa, qa);
+    if (b + 1 < nb) consume(pb, qb);
+  }
+
+  // acc[h][t][v] = O[c0 + 16 h + 4 g + v][16 t + i]
+  if (wave > 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        *reinterpret_cast<f32x4_t*>(&red[wave - 1][h * RT + t][lane][0]) = acc[h][t];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      f32x4_t v = acc[h][t];
+#pragma unroll
+      for (int w = 0; w < kGradWaves - 1; ++w) {
+        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(&red[w][h * RT + t][lane][0]);
+        v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
+      }
+      const int64_t c = c0 + 16 * h + 4 * g;     // c .. c + 3 (cols is a multiple of 8)
+      const int j = 16 * t + i;
+      if (c >= cols || j >= r) continue;
+      if (trans) {
+        *reinterpret_cast<f32x4_t*>(out + (int64_t)j * cols + c) =
+            f32x4_t{s * v[0], s * v[1], s * v[2], s * v[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[(c + e) * r + j] = s * v[e];
+      }
+    }
+}
+
+bool adapter_grads_supported(int64_t M, int64_t K, int64_t N, int r) {
+  return r >= 1 && r <= 64 && r % 8 == 0 && K % 8 == 0 && N % 8 == 0 &&
+         M * K * 2 < ((int64_t)1 << 31) && M * N * 2 < ((int64_t)1 << 31) &&
+         M * r * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_adapter_grads(const uint16_t* U, const uint16_t* X, const uint16_t* dY,
+                                const uint16_t* T, int64_t M, int64_t K, int64_t N, int r,
+                                float s, float* dA, float* dB, hipStream_t st) {
+  if (!adapter_grads_supported(M, K, N, r)) return hipErrorInvalidValue;
+  GradJob ja{X, K, K, U, dA, 1, (int)((K + kGradCols - 1) / kGradCols)};
+  GradJob jb{dY, N, N, T, dB, 0, (int)((N + kGradCols - 1) / kGradCols)};
+  const dim3 grid((unsigned)(ja.slices + jb.slices));
+  const int tiles = (r + 15) / 16;
+  if (tiles <= 1)
+    hipLaunchKernelGGL((k_adapter_grads<1, 8>), grid, dim3(kGradWaves * 64), 0, st, ja, jb, (int)M, r, s);
+  else if (tiles <= 2)
+    hipLaunchKernelGGL((k_adapter_grads<2, 4>), grid, dim3(kGradWaves * 64), 0, st, ja, jb, (int)M, r, s);
+  else
+    hipLaunchKernelGGL((k_adapter_grads<4, 4>), grid, dim3(kGradWaves * 64), 0, st, ja, jb, (int)M, r, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, bool transposed,
                          int r, uint16_t* out, hipStream_t st) {
   return transposed ? rank16_dispatch<true>(S, M, C, W, r, out, st)

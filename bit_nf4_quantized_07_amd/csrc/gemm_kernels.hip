@@ -579,10 +579,19 @@ BwdPlan plan_bwd(int64_t M, int64_t K, int64_t N, int r, bool dx) {
   const int64_t rt = ceil_div(r, r_tile(r));
   p.t_splits = 1;   // T and U in one pass (no partial sums)
   p.u_splits = 1;
-  p.m_splits_a = actual_splits(M, choose_splits((int64_t)ceil_div(r, r_tile(r)) * ceil_div(K, 128), M));
-  p.m_splits_b = actual_splits(M, choose_splits((int64_t)ceil_div(N, 128) * rt, M));
-  p.off_part_b = p.off_part + align256((size_t)p.m_splits_a * r * K * 4);
-  p.bytes = p.off_part_b + align256((size_t)p.m_splits_b * N * r * 4);
+  // dA and dB: one pass without partial sums where the shape allows, else
+  // split partials over the tokens and a fixed-order reduction.
+  p.one_pass_grads = adapter_grads_supported(M, K, N, r);
+  if (p.one_pass_grads) {
+    p.m_splits_a = p.m_splits_b = 0;
+    p.off_part_b = p.off_part;
+    p.bytes = p.off_part;
+  } else {
+    p.m_splits_a = actual_splits(M, choose_splits((int64_t)ceil_div(r, r_tile(r)) * ceil_div(K, 128), M));
+    p.m_splits_b = actual_splits(M, choose_splits((int64_t)ceil_div(N, 128) * rt, M));
+    p.off_part_b = p.off_part + align256((size_t)p.m_splits_a * r * K * 4);
+    p.bytes = p.off_part_b + align256((size_t)p.m_splits_b * N * r * 4);
+  }
   // Large M: the dequantised weight (bf16, 2 N K bytes, addressed with 32-bit
   // buffer offsets) is reused by every token tile of the dX kernel.
   p.dequant_dx = dx && M >= kDequantDxMinM && dx_nf4_supported(N) && N * K * 2 < ((int64_t)1 << 31);
@@ -872,9 +881,11 @@ hipError_t launch_qlora_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, co
     if (!own) timer_end(tm, TK_DX_GEMM, st);
     QLK_TRY(e);
   }
-  // dA = s U^T X: rows j (U^T, transposed), cols k (X^T, transposed), and
-  // dB = s dY^T T: rows n (dY^T), cols j (T^T), both contracting over m: one
-  // launch for the partials of both.
+  // dA = s U^T X and dB = s dY^T T, both contracting over m.
+  if (plan.one_pass_grads) return launch_adapter_grads(U, X, dY, T, M, K, N, r, s, dA, dB, st);
+  // Otherwise the partials of both in one launch (rows j of U^T and columns
+  // k of X^T, both transposed; rows n of dY^T and columns j of T^T), then
+  // their fixed-order sums.
   QLK_TRY(skinny_pair(rt, opnd(U, r, r, M), opnd(X, K, (int)K, M), r, (int)K, plan.m_splits_a, part,
                       opnd(dY, N, (int)N, M), opnd(T, r, r, M), (int)N, r, plan.m_splits_b, part_b,
                       M, st));

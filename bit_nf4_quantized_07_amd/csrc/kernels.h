@@ -106,6 +106,7 @@ struct FwdPlan {
 };
 struct BwdPlan {
   int u_splits, t_splits, m_splits_a, m_splits_b;
+  bool one_pass_grads;   // dA and dB by launch_adapter_grads (no partials)
   size_t off_U, off_T, off_part, off_part_b, bytes;   // dA partials at off_part, dB at off_part_b
   // dX on a bf16 copy of the weight dequantised once per call (at off_wbf16)
   // instead of decoding every tile in each of the M / 256 token tiles.
@@ -210,6 +211,14 @@ hipError_t launch_fwd_wide_bf16(const uint16_t* X, int64_t M, const uint16_t* wb
 hipError_t launch_fwd_bf16(const uint16_t* X, int64_t M, const uint16_t* wb, int64_t N, int64_t K,
                            const uint16_t* T, const uint16_t* B, int r, float s, uint16_t* Y,
                            hipStream_t st);
+// dA = s U^T X ([r, K], fp32) and dB = s dY^T T ([N, r], fp32) in one launch
+// that contracts over all M tokens per output column slice (no partial sums);
+// for the shapes adapter_grads_supported accepts (r a multiple of 8, at most
+// 64; every operand under 2 GiB).
+bool adapter_grads_supported(int64_t M, int64_t K, int64_t N, int r);
+hipError_t launch_adapter_grads(const uint16_t* U, const uint16_t* X, const uint16_t* dY,
+                                const uint16_t* T, int64_t M, int64_t K, int64_t N, int r,
+                                float s, float* dA, float* dB, hipStream_t st);
 // out[M, r] (bf16) = S[M, C] W^T with W = [r, C] or, transposed, [C, r].
 hipError_t launch_rank16(const uint16_t* S, int64_t M, int64_t C, const uint16_t* W, bool transposed,
                          int r, uint16_t* out, hipStream_t st);

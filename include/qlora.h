@@ -199,7 +199,10 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N,
  *   dB = s dY^T (X A^T)        fp32 [N, r]
  * T is the X A^T saved by the forward (bf16 [M, r]); NULL = recompute it.
  * flags: 0 or QLORA_BWD_ACCUMULATE_DX.  The reductions over M run in a fixed
- * order, so repeated calls give identical bits.  Same shape rules and
+ * order, so repeated calls give identical bits: for r <= 64 one workgroup
+ * per 32 output columns of dA^T or dB contracts over all M tokens (no
+ * partial sums in the workspace); above, fp32 partials over token ranges go
+ * through the workspace and are added in index order.  Same shape rules and
  * tolerances as the forward; workspace >= qlora_workspace_bytes(..., 1).
  * For M >= 1024 (and N % 256 == 0, 2 N K < 2 GiB) the weight is dequantised
  * once per call into the workspace (2 N K bytes of it) and dX runs on that
