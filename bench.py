@@ -246,6 +246,21 @@ def dropout_step(q, d, ws, seed):
                          workspace=ws)
 
 
+def settle(torch, fn, seconds):
+    """Run fn(i) untimed until `seconds` of wall time have passed.  The GPU
+    reaches the clock it holds under a sustained load only after some tens of
+    milliseconds of work: after a warm-up of a few steps the first timed
+    steps still run up to 8 % slower than the same steps a moment later."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def run_linear(args, q, torch, wl, lib, ev):
     """Configuration 2 (default): one linear, fwd + bwd."""
     cfg = wl.workloads()["c2_linear_4096"]
@@ -254,6 +269,7 @@ def run_linear(args, q, torch, wl, lib, ev):
     sets = make_linear_sets(q, torch, wl, cfg.name, 0, M, args.sets)
     ws = q.Workspace("cuda")
     ws.get(max(q.workspace_bytes(M, lin.K, lin.N, lin.r, b) for b in (False, True)))
+    settle(torch, lambda i: linear_step(q, sets[i % len(sets)], ws), args.settle)
     for i in range(args.warmup):
         linear_step(q, sets[i % len(sets)], ws)
     torch.cuda.synchronize()
@@ -421,6 +437,7 @@ def run_gemv(args, q, torch, wl, lib, ev):
             d = sets[i % len(sets)]
             q.linear_fwd(d["X"][:M], d["qw"], d["A"], d["B"], lin.alpha, out=Ys[i % len(sets)],
                          T_out=Ts[i % len(sets)], workspace=ws, timing=timing)
+        settle(torch, call, min(args.settle, 0.2))
         for i in range(10):
             call(i)
         torch.cuda.synchronize()
@@ -1204,6 +1221,10 @@ def main():
     ap.add_argument("--no-blocks", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the bf16-base and dropout steps (counter runs)")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up steps of the layer "
+                         "(and up to 0.2 s before each small-M size), so that the timed "
+                         "steps run at the clock the GPU holds under the load")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--library-gemm", action="store_true",
@@ -1272,7 +1293,8 @@ def main():
             cpu["gemv"] = run_cpu_gemv_baseline(args.cpu_budget / 3)
         err(f"[bench] cpu {cpu}")
     line = dict(metric=METRIC, value=round(lin["value"], 2), unit="TFLOP/s", n_gpus=1,
-                steps=args.steps, warmup=args.warmup, ms_per_step=round(lin["ms"], 4),
+                steps=args.steps, warmup=args.warmup, settle_s=args.settle,
+                ms_per_step=round(lin["ms"], 4),
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
                 data="synthetic", config=lin["config"], roofline=lin["roofline"],
                 cpu_baseline=cpu, kernels=lin["kernels"], lora_bf16_base=lin["lora_bf16"],
