@@ -338,6 +338,7 @@ def run_linear(args, q, torch, wl, lib, ev):
     # comparison the pages quantify as 20-40 % slower per step.
     for d in sets:
         d["Wbf"] = q.nf4_dequant(d["qw"])
+    settle(torch, lambda i: linear_step(q, sets[i % len(sets)], ws, "Wbf"), args.settle)
     for i in range(args.warmup):
         linear_step(q, sets[i % len(sets)], ws, "Wbf")
     torch.cuda.synchronize()
@@ -353,6 +354,7 @@ def run_linear(args, q, torch, wl, lib, ev):
     for d in sets:
         d["Xd"] = torch.empty_like(d["X"])
         d["mask"] = torch.empty(M * lin.K // 32, dtype=torch.int32, device="cuda")
+    settle(torch, lambda i: dropout_step(q, sets[i % len(sets)], ws, 2000 + i), args.settle)
     for i in range(args.warmup):
         dropout_step(q, sets[i % len(sets)], ws, 1000 + i)
     torch.cuda.synchronize()
