@@ -308,25 +308,32 @@ def _full_linear(cfg, idx, M=None, rows=48):
     ow = OracleWeight(W, full=False)
     s = oracle.lora_scale(lin.alpha, lin.r)
     Xf, Af, Bf, dYf = f64(X), f64(A), f64(B), f64(dY)
-    Tref = Xf @ Af.T
-    assert_close(got["T"], Tref, "T")
-    # Y on sampled columns (weight rows) for every token
+    # The oracle's own forward on the sampled weight rows (the layer restricted
+    # to those output columns): Y[:, ncol] and the whole of T.
     ncol = sample_rows(lin.N, rows, seed=2)
     Wr = f64(ow.rows_bf16(ncol))
-    Yref = Xf @ Wr.T + s * (Tref @ Bf[ncol].T)
+    Yref, Tref = oracle.forward(Xf, Wr, Af, Bf[ncol], lin.alpha, lin.r)
+    assert_close(got["T"], Tref, "T")
     assert_close(got["Y"][:, ncol], Yref, "Y[:, sampled]")
     if not w.backward:
         return
+    # dA and dB whole, from their definitions
     U = dYf @ Bf
     assert_close(got["dA"], s * (U.T @ Xf), "dA")
     assert_close(got["dB"], s * (dYf.T @ Tref), "dB")
-    # dX on sampled 64-column blocks for every token
+    # The oracle's backward on restricted operands: with the input features
+    # cut to sampled 64-column blocks it gives dX and dA on those columns
+    # (U = dY B is unchanged); with the output features cut to the sampled
+    # weight rows it gives dB on those rows (T = X A^T is unchanged).
     kb = np.unique(np.concatenate([[0, lin.K // 64 - 1],
                                    np.random.default_rng(3).integers(0, lin.K // 64, 6)]))
     Wc = f64(ow.colblocks_bf16(kb))
     cols = (kb[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
-    dXref = dYf @ Wc + s * (U @ Af[:, cols])
-    assert_close(got["dX"][:, cols], dXref, "dX[:, sampled]")
+    dXc, dAc, _ = oracle.backward(dYf, Xf[:, cols], Wc, Af[:, cols], Bf, lin.alpha, lin.r)
+    assert_close(got["dX"][:, cols], dXc, "dX[:, sampled]")
+    assert_close(got["dA"][:, cols], dAc, "dA[:, sampled]")
+    _, _, dBr = oracle.backward(dYf[:, ncol], Xf, Wr, Af, Bf[ncol], lin.alpha, lin.r)
+    assert_close(got["dB"][ncol], dBr, "dB[sampled]")
 
 
 def test_full_config2():
